@@ -1,0 +1,22 @@
+"""Plain fp64 CPU oracle of the Mixtral-style sparse MoE layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the graft entry
+point and the CPU-baseline leg of the benchmark may import this package.  The
+product path (the HIP library and its Python binding) never calls it and shares
+no code with it.
+"""
+from .moe_oracle import (  # noqa: F401
+    brute_force_topk,
+    dispatch,
+    expert_swiglu,
+    forward,
+    forward_mask_form,
+    forward_with_selection,
+    gate_weights,
+    mixtral_param_counts,
+    route,
+    router_logits,
+    sigmoid,
+    silu,
+    topk_select,
+)

@@ -1,0 +1,264 @@
+"""fp64 CPU oracle of the Mixtral-style sparse mixture-of-experts layer.
+
+TEST INFRASTRUCTURE: only tests/, the graft smoke check and the benchmark's
+CPU-baseline leg may use it.  It shares no code with the HIP path.
+
+What it computes is the plain definition of the layer, written out in NumPy
+float64 (every input is widened losslessly from its bf16/fp32 storage):
+
+    y = sum_i Softmax(TopK(x . W_g))_i * SwiGLU_i(x)
+
+as given by the layer equation on card 2.1 "Sparse Mixture of Experts" of the
+"Mixtral of Experts" study deck (Jiang et al. 2024), with the general
+token-choice top-k form from "How Experts Are Chosen (Routing Methods)" in
+"Mixtral of Experts? Mixture of Experts? Try to explain Mixtral 8x7B", and the
+router walk-through of Part 3, "Pip's token goes to triage" (steps 1-4) in
+"Mixture of Experts: Why Mixtral Only Wakes Up Two Specialists".
+
+Readings where the pages leave a step open (each also listed in the design notes):
+  * SwiGLU_i(x) = (SiLU(x W1_i) * (x W3_i)) W2_i with SiLU(z) = z * sigmoid(z):
+    the pages only name SwiGLU and say an expert expands with d x f matrices,
+    applies a simple non-linearity and compresses back (three matrices per
+    expert, Part 2 and Part 4 of the explainer).  No biases anywhere.
+  * Top-K ties go to the lower expert index; the K kept slots are ordered by
+    descending logit (the walk-through lists the larger score first).
+  * The softmax runs over the K kept logits only (the others are -inf).
+  * Expert indices are 0-based (the equation sums i = 0..n-1); the walk-through
+    counts from 1, so its "expert 3 and expert 7" are indices 2 and 6 here.
+  * y excludes the residual add that the surrounding block performs.
+
+Pins (tests/test_oracle_pins.py) tie every function to something other than
+itself: the walk-through's printed weights, brute force over all expert
+subsets, the K = n / K = 1 / n = K = 1 special cases, the parameter arithmetic
+printed in Part 4 of the explainer, closed forms of the sigmoid, and
+metamorphic invariants.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import itertools
+from typing import Callable, Union
+
+import numpy as np
+
+ArrayOrGetter = Union[np.ndarray, Callable[[int], np.ndarray]]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _expert(W: ArrayOrGetter, e: int) -> np.ndarray:
+    """Expert e's matrix in float64; W is either an [n][..][..] array or a
+    callable returning expert e's matrix (lets full-size checks widen one
+    expert at a time)."""
+    if callable(W):
+        return _f64(W(e))
+    return _f64(W[e])
+
+
+# ---------------------------------------------------------------- router ---
+
+def router_logits(x, Wg) -> np.ndarray:
+    """Step 1 of the walk-through: a bias-free linear layer scores every expert,
+    logits[t][e] = sum_j x[t][j] * W_g[j][e]  (x . W_g in the layer equation)."""
+    return _f64(x) @ _f64(Wg)
+
+
+def topk_select(logits: np.ndarray, K: int):
+    """Step 2 of the walk-through: keep the K largest scores and their positions.
+
+    Returns (sel, margin, slot_margin):
+      sel[t]        the K kept expert indices, descending logit, ties -> lower index
+      margin[t]     gap between the K-th and (K+1)-th sorted logits (+inf if K == n)
+      slot_margin[t] smallest gap between consecutive kept logits (+inf if K == 1)
+    """
+    logits = _f64(logits)
+    T, n = logits.shape
+    if not 1 <= K <= n:
+        raise ValueError("need 1 <= K <= n")
+    # a stable sort of the negated scores keeps equal scores in index order
+    order = np.argsort(-logits, axis=1, kind="stable")
+    sel = order[:, :K].astype(np.int64)
+    srt = np.take_along_axis(logits, order, axis=1)
+    if K < n:
+        margin = srt[:, K - 1] - srt[:, K]
+    else:
+        margin = np.full(T, np.inf)
+    if K > 1:
+        slot_margin = np.min(srt[:, :K - 1] - srt[:, 1:K], axis=1)
+    else:
+        slot_margin = np.full(T, np.inf)
+    return sel, margin, slot_margin
+
+
+def gate_weights(logits: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """Step 3 of the walk-through: softmax over the kept scores only (the
+    unselected logits are -inf in the layer equation, so they get weight 0).
+    Max-subtracted form; w[t][k] is the weight of expert sel[t][k]."""
+    kept = np.take_along_axis(_f64(logits), np.asarray(sel), axis=1)
+    z = np.exp(kept - kept.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def route(x, Wg, K: int) -> dict:
+    """Steps 1-3 plus the integer dispatch, as one record."""
+    logits = router_logits(x, Wg)
+    sel, margin, slot_margin = topk_select(logits, K)
+    w = gate_weights(logits, sel)
+    counts, offsets, perm_token, slot_pos = dispatch(sel, logits.shape[1])
+    return dict(logits=logits, sel=sel, w=w, margin=margin, slot_margin=slot_margin,
+                counts=counts, offsets=offsets, perm_token=perm_token, slot_pos=slot_pos)
+
+
+def brute_force_topk(logit_row: np.ndarray, K: int) -> tuple:
+    """Top-K by exhaustive search over all C(n, K) expert subsets: the subset with
+    the largest logit sum; among equal sums the lexicographically smallest
+    sorted index tuple.  Returned as a sorted tuple (a set, not slot order)."""
+    row = _f64(logit_row)
+    best, best_sum = None, -np.inf
+    for sub in itertools.combinations(range(row.shape[0]), K):
+        s = float(sum(row[i] for i in sub))
+        if s > best_sum:  # combinations() runs in lexicographic order
+            best, best_sum = sub, s
+    return best
+
+
+# -------------------------------------------------------------- dispatch ---
+
+def dispatch(sel: np.ndarray, n: int):
+    """Group the (token, slot) assignments by expert: a counting sort in token order.
+
+    The pages only say that experts with zero gate are not evaluated (Part 3 of
+    the explainer, step 2; the sparse-gating passage of "How a mixture-of-experts
+    model activates only part of its parameters"); grouping the surviving
+    assignments per expert is the plain way to run each expert once on its rows.
+      counts[e]      number of assignments to expert e
+      offsets[e]     exclusive prefix sum of counts, offsets[n] = T*K
+      perm_token[p]  token of position p; expert-contiguous, ascending t per expert
+      slot_pos[t][k] position of assignment (t, k)
+    """
+    sel = np.asarray(sel, dtype=np.int64)
+    T, K = sel.shape
+    counts = np.zeros(n, dtype=np.int64)
+    for e in sel.reshape(-1):
+        counts[e] += 1
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm_token = np.empty(T * K, dtype=np.int64)
+    slot_pos = np.empty((T, K), dtype=np.int64)
+    for e in range(n):
+        hit = sel == e                       # [T][K]; a token holds e at most once
+        toks = np.nonzero(hit.any(axis=1))[0]  # ascending token index
+        pos = offsets[e] + np.arange(toks.size)
+        perm_token[pos] = toks
+        k_of = np.argmax(hit[toks], axis=1)
+        slot_pos[toks, k_of] = pos
+    return counts, offsets, perm_token, slot_pos
+
+
+# --------------------------------------------------------------- experts ---
+
+def sigmoid(z) -> np.ndarray:
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z) -> np.ndarray:
+    """SiLU (Swish with beta = 1): z * sigmoid(z)."""
+    z = _f64(z)
+    return z * sigmoid(z)
+
+
+def expert_swiglu(X, W1e, W3e, W2e) -> np.ndarray:
+    """One expert on a batch of rows: expand with two d x f matrices, gate one
+    with SiLU, multiply, compress with the f x d matrix (the reading of SwiGLU
+    stated in the module header)."""
+    X = _f64(X)
+    a = X @ _f64(W1e)
+    b = X @ _f64(W3e)
+    return (silu(a) * b) @ _f64(W2e)
+
+
+# --------------------------------------------------------------- forward ---
+
+def forward_with_selection(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter,
+                           sel: np.ndarray) -> np.ndarray:
+    """Steps 3-4 of the walk-through for a given selection: weights are the
+    softmax over the selected logits, each selected expert runs on the token on
+    its own, and the outputs are summed with those weights.  Experts that no
+    token selected are never evaluated (so their weights are never read)."""
+    x = _f64(x)
+    logits = router_logits(x, Wg)
+    sel = np.asarray(sel, dtype=np.int64)
+    w = gate_weights(logits, sel)
+    T = x.shape[0]
+    n = _f64(Wg).shape[1]
+    y = None
+    for e in range(n):
+        hit = sel == e
+        rows = np.nonzero(hit.any(axis=1))[0]
+        if rows.size == 0:
+            continue
+        out = expert_swiglu(x[rows], _expert(W1, e), _expert(W3, e), _expert(W2, e))
+        if y is None:
+            y = np.zeros((T, out.shape[1]))
+        y[rows] += (w[rows] * hit[rows]).sum(axis=1)[:, None] * out
+    if y is None:
+        y = np.zeros((T, x.shape[1]))
+    return y
+
+
+def forward(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter, K: int) -> np.ndarray:
+    """The layer: route every token (steps 1-3), then run and blend its K experts."""
+    sel, _, _ = topk_select(router_logits(x, Wg), K)
+    return forward_with_selection(x, Wg, W1, W3, W2, sel)
+
+
+def forward_mask_form(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter,
+                      K: int) -> np.ndarray:
+    """The layer equation read literally: logits outside the top K are set to
+    -inf, a softmax runs over all n experts, and every expert with a non-zero
+    gate contributes gate * expert(x).  Top-K membership is decided here by
+    rank counting (a logit is kept when fewer than K logits beat it, a tie
+    being beaten by the lower index), independently of topk_select."""
+    x = _f64(x)
+    logits = router_logits(x, Wg)
+    T, n = logits.shape
+    keep = np.zeros((T, n), dtype=bool)
+    for i in range(n):
+        li = logits[:, i:i + 1]
+        beats = (logits > li) | ((logits == li) & (np.arange(n)[None, :] < i))
+        keep[:, i] = beats.sum(axis=1) < K
+    masked = np.where(keep, logits, -np.inf)
+    g = np.exp(masked - masked.max(axis=1, keepdims=True))
+    g = g / g.sum(axis=1, keepdims=True)
+    y = np.zeros_like(x)
+    for i in range(n):
+        rows = np.nonzero(g[:, i] > 0)[0]
+        if rows.size == 0:
+            continue
+        out = expert_swiglu(x[rows], _expert(W1, i), _expert(W3, i), _expert(W2, i))
+        y[rows] += g[rows, i][:, None] * out
+    return y
+
+
+# ------------------------------------------------- parameter arithmetic ---
+
+def mixtral_param_counts(d: int = 4096, f: int = 14336, layers: int = 32, n: int = 8, K: int = 2,
+                         vocab: int = 32000, attn_per_layer: int = 42_000_000) -> dict:
+    """The parameter count of Part 4 ("Why 8x7B Is Not 56B") of the explainer:
+    three d x f matrices per expert, n experts per layer; attention (about 42M
+    per layer, taken as printed), two d x vocab embedding tables and a d x n
+    router per layer are shared.  Active = shared + K experts per layer."""
+    per_expert = 3 * d * f
+    experts = per_expert * n * layers
+    attention = attn_per_layer * layers
+    embeddings = 2 * vocab * d
+    routers = d * n * layers
+    shared = attention + embeddings + routers
+    return dict(per_expert=per_expert, experts=experts, attention=attention,
+                embeddings=embeddings, routers=routers, shared=shared,
+                total=experts + shared, active=shared + K * per_expert * layers,
+                two_experts_all_layers=K * per_expert * layers,
+                naive=n * 7_000_000_000)

@@ -1,0 +1,367 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix (CPU only).
+
+Each test ties an oracle function to something other than itself: a value the
+pages print, brute force over every expert subset, a special case with a known
+answer, a closed form, or a metamorphic invariant.  A plausible slip in the
+oracle (a dropped term, a wrong sign or index, a transposed operand, a softmax
+over all n experts, a top-K tie to the higher index) fails at least one test.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import bf16_bits_from_f32, bf16_bits_to_f32, make_config_inputs, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _small(T=24, d=16, f=24, n=6, K=2, seed=7):
+    inp = make_inputs(T, d, f, n, K, dtype="f32", seed=seed)
+    return inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"), inp.f64("W2")
+
+
+# ------------------------------------------------------------ worked example
+
+def test_worked_example_selection_and_weights():
+    g = _load("worked_example.json")
+    logits = np.array(g["logits"])
+    n = logits.size
+    # x = e_0 makes the router's logits equal row 0 of W_g exactly
+    x = np.zeros((1, n))
+    x[0, 0] = 1.0
+    Wg = np.zeros((n, n))
+    Wg[0] = logits
+    r = oracle.route(x, Wg, g["K"])
+    assert list(r["sel"][0]) == g["selected_zero_based"]
+    assert [i + 1 for i in r["sel"][0]] == g["selected_page_numbering"]
+    w = r["w"][0]
+    assert list(np.round(w, g["weights_printed_decimals"])) == g["weights_printed"]
+    # two-way softmax closed form: the larger weight is sigmoid of the gap 2.3 - 1.5
+    assert abs(w[0] - 1.0 / (1.0 + math.exp(-0.8))) < 1e-15
+    assert abs(w[1] - 1.0 / (1.0 + math.exp(0.8))) < 1e-15
+
+
+# ------------------------------------------------------------------- router
+
+def test_router_logits_match_triple_loop():
+    x, Wg, *_ = _small(T=5, d=7, n=3)
+    L = oracle.router_logits(x, Wg)
+    for t in range(5):
+        for e in range(3):
+            s = 0.0
+            for j in range(7):
+                s += x[t, j] * Wg[j, e]
+            assert abs(L[t, e] - s) < 1e-13
+
+
+def test_router_one_hot_reads_wg_row():
+    rng = np.random.default_rng(3)
+    Wg = rng.standard_normal((8, 8))
+    for j in range(8):
+        x = np.zeros((1, 8))
+        x[0, j] = 1.0
+        np.testing.assert_array_equal(oracle.router_logits(x, Wg)[0], Wg[j])
+
+
+# -------------------------------------------------------------------- top-K
+
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_topk_equals_brute_force_distinct(K):
+    rng = np.random.default_rng(11 + K)
+    L = rng.standard_normal((200, 8))
+    sel, margin, _ = oracle.topk_select(L, K)
+    for t in range(L.shape[0]):
+        assert tuple(sorted(sel[t])) == oracle.brute_force_topk(L[t], K)
+        # slot order: descending logit
+        assert all(L[t, sel[t][k]] >= L[t, sel[t][k + 1]] for k in range(K - 1))
+        if K < 8:
+            assert margin[t] >= 0
+
+
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_topk_ties_go_to_lower_index(K):
+    rng = np.random.default_rng(5)
+    L = rng.integers(-2, 3, size=(300, 8)).astype(np.float64)  # many ties
+    sel, _, _ = oracle.topk_select(L, K)
+    for t in range(L.shape[0]):
+        assert tuple(sorted(sel[t])) == oracle.brute_force_topk(L[t], K)
+        # slot order: descending value, equal values by ascending index
+        keys = [(-L[t, e], e) for e in sel[t]]
+        assert keys == sorted(keys)
+
+
+def test_brute_force_is_exhaustive():
+    # every subset considered: a lone large logit at the last index must be found
+    row = np.zeros(9)
+    row[8] = 1.0
+    assert oracle.brute_force_topk(row, 1) == (8,)
+    assert oracle.brute_force_topk(row, 2) == (0, 8)
+    assert len(list(itertools.combinations(range(8), 2))) == 28
+
+
+def test_wg_zero_picks_first_k_with_equal_weights():
+    inp = make_inputs(64, 32, 16, 8, 3, dtype="f32", seed=2, wg_zero=True)
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), 3)
+    assert (r["sel"] == np.array([0, 1, 2])).all()
+    assert (r["w"] == 1.0 / 3.0).all()
+    assert (r["margin"] == 0).all()
+
+
+# ------------------------------------------------------------ gate weights
+
+def test_gate_weights_sum_to_one_positive_descending():
+    x, Wg, *_ = _small(T=200, n=8)
+    r = oracle.route(x, Wg, 2)
+    w = r["w"]
+    assert (w > 0).all()
+    assert np.abs(w.sum(axis=1) - 1.0).max() <= 1e-15
+    assert (w[:, 0] >= w[:, 1]).all()
+
+
+def test_k1_weight_exactly_one_and_argmax_expert():
+    x, Wg, W1, W3, W2 = _small(T=40, n=5, K=1)
+    r = oracle.route(x, Wg, 1)
+    assert (r["w"] == 1.0).all()
+    assert (r["sel"][:, 0] == np.argmax(r["logits"], axis=1)).all()
+    y = oracle.forward(x, Wg, W1, W3, W2, 1)
+    for t in range(x.shape[0]):
+        e = int(np.argmax(r["logits"][t]))
+        ref = oracle.expert_swiglu(x[t:t + 1], W1[e], W3[e], W2[e])[0]
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-13)
+
+
+def test_softmax_over_kept_not_over_all():
+    # renormalising a full n-way softmax restricted to the top K gives the same
+    # weights; a full softmax without renormalisation does not (n > K)
+    x, Wg, *_ = _small(T=50, n=8)
+    r = oracle.route(x, Wg, 2)
+    L = r["logits"]
+    full = np.exp(L - L.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    kept = np.take_along_axis(full, r["sel"], axis=1)
+    np.testing.assert_allclose(r["w"], kept / kept.sum(axis=1, keepdims=True), atol=1e-15)
+    assert np.abs(r["w"] - kept).max() > 1e-3
+
+
+# ---------------------------------------------------------- special cases
+
+def test_k_equals_n_is_dense_softmax_mixture():
+    x, Wg, W1, W3, W2 = _small(T=12, n=4, K=4)
+    y = oracle.forward(x, Wg, W1, W3, W2, 4)
+    L = x @ Wg
+    for t in range(x.shape[0]):
+        p = np.exp(L[t] - L[t].max())
+        p /= p.sum()
+        ref = sum(p[e] * oracle.expert_swiglu(x[t:t + 1], W1[e], W3[e], W2[e])[0] for e in range(4))
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-13)
+
+
+def test_n_k_one_is_dense_swiglu_ffn():
+    # the dense 4x FFN of "A visual guide to MoE models" (Dense Layers): 512 -> 2048 -> 512
+    rng = np.random.default_rng(9)
+    d, f, T = 512, 2048, 3
+    x = rng.standard_normal((T, d))
+    Wg = rng.standard_normal((d, 1))
+    W1 = rng.standard_normal((1, d, f)) / math.sqrt(d)
+    W3 = rng.standard_normal((1, d, f)) / math.sqrt(d)
+    W2 = rng.standard_normal((1, f, d)) / math.sqrt(f)
+    y = oracle.forward(x, Wg, W1, W3, W2, 1)
+    for t in range(T):
+        hid = np.empty(f)
+        for j in range(f):
+            a = float(np.dot(x[t], W1[0][:, j]))
+            b = float(np.dot(x[t], W3[0][:, j]))
+            hid[j] = a / (1.0 + math.exp(-a)) * b
+        ref = np.array([np.dot(hid, W2[0][:, c]) for c in range(d)])
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-11)
+
+
+def test_unselected_experts_contribute_nothing():
+    # a constant input feature with a -1e3 router weight makes experts 4 and 5
+    # lose every token; their weights are then poisoned with NaN
+    x, Wg, W1, W3, W2 = _small(T=30, n=6)
+    x2 = np.concatenate([x, np.ones((x.shape[0], 1))], axis=1)
+    Wg2 = np.concatenate([Wg, np.zeros((1, 6))], axis=0)
+    Wg2[-1, 4:] = -1e3
+    W1p = np.concatenate([W1, np.zeros((6, 1, W1.shape[2]))], axis=1)
+    W3p = np.concatenate([W3, np.zeros((6, 1, W3.shape[2]))], axis=1)
+    W2p = np.concatenate([W2, np.zeros((6, W2.shape[1], 1))], axis=2)
+    sel, _, _ = oracle.topk_select(x2 @ Wg2, 2)
+    assert not np.isin(sel, [4, 5]).any()
+    y_ref = oracle.forward(x2, Wg2, W1p, W3p, W2p, 2)
+    for W in (W1p, W3p, W2p):
+        W[4:] = np.nan
+    y_nan = oracle.forward(x2, Wg2, W1p, W3p, W2p, 2)
+    assert np.isfinite(y_nan).all()
+    np.testing.assert_array_equal(y_nan, y_ref)
+
+
+def test_mask_form_matches_gather_form():
+    for (n, K) in [(8, 2), (6, 1), (5, 5), (7, 3)]:
+        x, Wg, W1, W3, W2 = _small(T=40, n=n, K=K, seed=n * 10 + K)
+        a = oracle.forward(x, Wg, W1, W3, W2, K)
+        b = oracle.forward_mask_form(x, Wg, W1, W3, W2, K)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_mask_form_matches_gather_form_with_ties():
+    inp = make_inputs(16, 8, 12, 6, 2, dtype="f32", seed=4, wg_zero=True)
+    args = (inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"), inp.f64("W2"))
+    np.testing.assert_allclose(oracle.forward(*args, 2), oracle.forward_mask_form(*args, 2),
+                               rtol=0, atol=1e-12)
+
+
+def test_forward_equals_brute_force_per_token():
+    inp = make_config_inputs("tiny_fp32")
+    x, Wg, W1, W3, W2 = (inp.f64(k) for k in ("x", "Wg", "W1", "W3", "W2"))
+    x = x[:16]
+    y = oracle.forward(x, Wg, W1, W3, W2, 2)
+    L = x @ Wg
+    for t in range(x.shape[0]):
+        sub = oracle.brute_force_topk(L[t], 2)
+        order = sorted(sub, key=lambda e: (-L[t, e], e))
+        z = np.array([math.exp(L[t, e] - L[t, order[0]]) for e in order])
+        w = z / z.sum()
+        ref = np.zeros(x.shape[1])
+        for k, e in enumerate(order):
+            a = x[t] @ W1[e]
+            b = x[t] @ W3[e]
+            h = np.array([ai / (1.0 + math.exp(-ai)) * bi for ai, bi in zip(a, b)])
+            ref += w[k] * (h @ W2[e])
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------------- metamorphic
+
+def test_relabelling_experts_leaves_y_unchanged():
+    x, Wg, W1, W3, W2 = _small(T=50, n=8)
+    perm = np.array([3, 7, 0, 5, 1, 6, 2, 4])
+    y = oracle.forward(x, Wg, W1, W3, W2, 2)
+    yp = oracle.forward(x, Wg[:, perm], W1[perm], W3[perm], W2[perm], 2)
+    _, margin, slot_margin = oracle.topk_select(x @ Wg, 2)
+    ok = (margin > 1e-9) & (slot_margin > 1e-9)
+    assert ok.mean() > 0.9
+    np.testing.assert_allclose(yp[ok], y[ok], rtol=0, atol=1e-12)
+
+
+def test_token_permutation_permutes_rows():
+    x, Wg, W1, W3, W2 = _small(T=50, n=8)
+    perm = np.random.default_rng(1).permutation(50)
+    y = oracle.forward(x, Wg, W1, W3, W2, 2)
+    yp = oracle.forward(x[perm], Wg, W1, W3, W2, 2)
+    np.testing.assert_allclose(yp, y[perm], rtol=0, atol=1e-12)
+
+
+def test_scaling_down_projection_scales_y_exactly():
+    x, Wg, W1, W3, W2 = _small(T=50, n=8)
+    y = oracle.forward(x, Wg, W1, W3, W2, 2)
+    y2 = oracle.forward(x, Wg, W1, W3, 2.0 * W2, 2)
+    np.testing.assert_array_equal(y2, 2.0 * y)
+
+
+def test_swapping_gate_and_up_changes_y():
+    # SiLU acts on the W1 side only; a transposed reading would swap W1/W3
+    x, Wg, W1, W3, W2 = _small(T=20, n=4)
+    a = oracle.forward(x, Wg, W1, W3, W2, 2)
+    b = oracle.forward(x, Wg, W3, W1, W2, 2)
+    assert np.abs(a - b).max() > 1e-3
+
+
+# ----------------------------------------------------------- SiLU / sigmoid
+
+def test_sigmoid_and_silu_closed_forms():
+    z = np.linspace(-30, 30, 2001)
+    np.testing.assert_allclose(oracle.sigmoid(z), 0.5 * (1.0 + np.tanh(z / 2.0)), rtol=0, atol=1e-15)
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.silu(0.0) == 0.0
+    # z*s(z) - (-z)*s(-z) = z (s(z) + s(-z)) = z
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=0, atol=1e-13)
+    assert abs(float(oracle.silu(1.0)) - 0.7310585786300049) < 1e-16
+    assert float(oracle.silu(-800.0)) == 0.0  # no overflow to NaN
+
+
+# ---------------------------------------------------------------- dispatch
+
+def test_dispatch_matches_sorting_by_expert_then_token():
+    rng = np.random.default_rng(21)
+    T, n, K = 300, 8, 2
+    sel = np.stack([rng.choice(n, size=K, replace=False) for _ in range(T)])
+    counts, offsets, perm_token, slot_pos = oracle.dispatch(sel, n)
+    pairs = sorted((int(sel[t, k]), t, k) for t in range(T) for k in range(K))
+    assert [t for (_, t, _) in pairs] == list(perm_token)
+    for p, (e, t, k) in enumerate(pairs):
+        assert slot_pos[t, k] == p
+    assert list(counts) == [sum(1 for q in pairs if q[0] == e) for e in range(n)]
+    assert offsets[0] == 0 and offsets[-1] == T * K
+
+
+def test_dispatch_invariants_with_empty_experts():
+    sel = np.array([[3, 1], [1, 3], [0, 3], [3, 0]])
+    counts, offsets, perm_token, slot_pos = oracle.dispatch(sel, 6)
+    assert list(counts) == [2, 2, 0, 4, 0, 0]
+    assert list(offsets) == [0, 2, 4, 4, 8, 8, 8]
+    assert list(perm_token) == [2, 3, 0, 1, 0, 1, 2, 3]
+    for t in range(4):
+        for k in range(2):
+            p = slot_pos[t, k]
+            assert perm_token[p] == t
+            e = sel[t, k]
+            assert offsets[e] <= p < offsets[e + 1]
+
+
+# ----------------------------------------------------- parameter arithmetic
+
+def test_mixtral_parameter_arithmetic():
+    g = _load("mixtral_params.json")
+    c = oracle.mixtral_param_counts(**g["config"])
+    p = g["printed"]
+    assert round(c["per_expert"] / 1e6) == p["per_expert_millions"]
+    assert round(c["experts"] / 1e9, 1) == p["experts_billions_1dp"]
+    assert round(c["attention"] / 1e9, 1) == p["attention_billions_1dp"]
+    assert round(c["embeddings"] / 1e9, 2) == p["embeddings_billions_2dp"]
+    assert round(c["routers"] / 1e6) == p["routers_millions"]
+    assert round(c["total"] / 1e9, 1) == p["total_billions_1dp"]
+    assert round(c["shared"] / 1e9, 1) == p["shared_billions_1dp"]
+    assert round(c["two_experts_all_layers"] / 1e9, 1) == p["two_experts_all_layers_billions_1dp"]
+    assert round(c["active"] / 1e9, 1) == p["active_billions_1dp"]
+    assert c["naive"] / 1e9 == p["naive_billions"]
+    assert round(c["total"] / 1e9) == p["total_rounded_billions"]
+    assert round(c["active"] / 1e9) == p["active_rounded_billions"]
+    assert round(c["total"] * 2 / 1e9) == p["memory_16bit_gb"]
+    assert round(c["total"] * 0.5 / 1e9) == p["memory_4bit_gb"]
+    # exact integers of the closed form
+    assert c["total"] == 46_704_349_184
+    assert c["active"] == 12_881_481_728
+
+
+# ---------------------------------------------------------------- generator
+
+def test_generator_is_seeded_and_rounds_to_nearest_even():
+    a = make_inputs(8, 64, 64, 4, 2, dtype="bf16", seed=5)
+    b = make_inputs(8, 64, 64, 4, 2, dtype="bf16", seed=5)
+    for k in ("x", "Wg", "W1", "W3", "W2"):
+        np.testing.assert_array_equal(getattr(a, k), getattr(b, k))
+    r = make_inputs(8, 64, 64, 4, 2, dtype="bf16", seed=5, router_only=True)
+    np.testing.assert_array_equal(r.x, a.x)
+    np.testing.assert_array_equal(r.Wg, a.Wg)
+    v = np.array([1.0, 1.00390625, 1.005859375, 1.01171875, -2.5], dtype=np.float32)
+    np.testing.assert_array_equal(bf16_bits_to_f32(bf16_bits_from_f32(v)),
+                                  np.array([1.0, 1.0, 1.0078125, 1.015625, -2.5], dtype=np.float32))
+
+
+def test_skewed_router_recipe_shares():
+    inp = make_config_inputs("mixtral_skewed", router_only=True)
+    sel, _, _ = oracle.topk_select(oracle.router_logits(inp.f64("x"), inp.f64("Wg")), 2)
+    top1 = np.bincount(sel[:, 0], minlength=8) / sel.shape[0]
+    assert 0.45 <= top1[0] <= 0.50
+    assert top1[7] < 0.02
