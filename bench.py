@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+One step = one call of moe_forward (router, top-K + softmax, dispatch, gate/up
+projection with SwiGLU, down projection, combine) on a resident batch.  The
+default workload is the Mixtral-shape prefill layer (T=8192, d=4096, f=14336,
+n=8, K=2, bf16); the decode batch (T=32) is measured in the same run and
+reported under "decode".  Inputs are seeded synthetic draws (synth/), weights
+random-init with the Mixtral layer's shapes.  Two weight copies alternate
+between steps so repeated reads cannot be served from the 256 MB last-level
+cache.
+
+Per-kernel durations come from HIP events the library records between its
+stages on the launch stream (moe_forward_traced), over the timed steps.
+The CPU baseline times the fp64 oracle on a bounded sample of the workload.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer tokens/s at Mixtral shape; % bf16 MFMA peak (T=8192), % HBM BW (T=32)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+STAGES = ["router", "dispatch", "up_proj", "down_proj", "combine"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill",
+                    choices=["mixtral_prefill", "mixtral_skewed", "many_experts", "mixtral_decode"])
+    ap.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload(inp, dev, copies):
+    import numpy as np
+    import torch
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = up(inp.x)
+    wg = up(inp.Wg)
+    w = []
+    for c in range(copies):
+        if c == 0:
+            w.append((up(inp.W1), up(inp.W3), up(inp.W2)))
+        else:
+            w.append(tuple(t.clone() for t in w[0]))
+    return x, wg, w
+
+
+def time_workload(name, steps, warmup):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_22_amd as moe
+    from synth import CONFIGS, make_config_inputs
+
+    c = CONFIGS[name]
+    T, d, f, n, K = c["T"], c["d"], c["f"], c["n"], c["K"]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = make_config_inputs(name)
+    x, wg, wsets = upload(inp, dev, copies=2)
+    del inp
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def make_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in evs:
+            e.record(stream)  # creates the underlying hipEvent_t
+        return evs
+
+    for i in range(warmup):
+        w1, w3, w2 = wsets[i % 2]
+        moe.forward(x, wg, w1, w3, w2, K, y=y)
+    torch.cuda.synchronize()
+    events = [make_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        w1, w3, w2 = wsets[i % 2]
+        moe.forward_traced(x, wg, w1, w3, w2, K, [e.cuda_event for e in events[i]], y=y)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    stage_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(5)] for ev in events])
+    rt = moe.route(x, wg, K, outputs=("counts",))
+    torch.cuda.synchronize()
+    counts = rt["counts"].cpu().numpy()
+    assert torch.isfinite(y).all().item()
+    return dict(T=T, d=d, f=f, n=n, K=K, ms_per_step=total_ms / steps, wall_s=wall,
+                stage_ms=stage_ms.mean(axis=0), stage_ms_min=stage_ms.min(axis=0), counts=counts)
+
+
+def prefill_record(r):
+    T, d, f, n, K = r["T"], r["d"], r["f"], r["n"], r["K"]
+    up_flops = 4.0 * T * K * d * f           # a = xW1 and b = xW3 on the T*K assignments
+    layer_flops = 2.0 * T * d * n + 6.0 * T * K * d * f
+    up_ms = float(r["stage_ms"][2])
+    achieved = up_flops / (up_ms * 1e-3) / 1e12
+    return {
+        "roofline": {"kernel": "grouped_gemm_kernel<1> (gate/up projection + SwiGLU)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": up_flops, "avg_launch_ms": round(up_ms, 4)},
+        "layer_tflops": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12, 1),
+        "layer_frac_of_mfma_peak": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+    }
+
+
+def decode_record(r):
+    T, d, f, n, K = r["T"], r["d"], r["f"], r["n"], r["K"]
+    touched = int((r["counts"] > 0).sum())
+    up_bytes = touched * 2.0 * d * f * 2 + T * d * 2 + T * K * f * 2
+    layer_bytes = touched * 3.0 * d * f * 2 + d * n * 2 + T * d * 2 + T * d * 4
+    up_ms = float(r["stage_ms"][2])
+    achieved = up_bytes / (up_ms * 1e-3) / 1e9
+    layer_gbs = layer_bytes / (r["ms_per_step"] * 1e-3) / 1e9
+    return {
+        "workload": "mixtral_decode", "T": T, "d": d, "f": f, "n": n, "K": K,
+        "value": round(T / (r["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "roofline": {"kernel": "skinny_kernel<1> (gate/up projection + SwiGLU)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": up_bytes, "avg_launch_ms": round(up_ms, 4)},
+        "layer_gbs": round(layer_gbs, 1), "layer_frac_of_hbm_peak": round(layer_gbs / PEAK_HBM_GBS, 4),
+        "experts_touched": touched,
+        "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, r["stage_ms"])},
+    }
+
+
+def cpu_baseline(name, sample):
+    """The fp64 oracle as it stands, on the first `sample` tokens of the workload."""
+    import numpy as np
+
+    import oracle
+    from synth import make_config_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    inp = make_config_inputs(name)
+    x = inp.f64("x")[:sample]
+    t0 = time.perf_counter()
+    y = oracle.forward(x, inp.f64("Wg"), lambda e: inp.expert_f64("W1", e),
+                       lambda e: inp.expert_f64("W3", e), lambda e: inp.expert_f64("W2", e), inp.K)
+    el = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    return {"value": round(sample / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample} of the {inp.T} tokens of {name}: fp64 routing and every "
+                      f"touched expert (weights widened per expert), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import sparse_mixture_experts_22_amd as moe
+    moe.lib()  # fails loudly if the HIP library is missing
+
+    main_r = time_workload(args.workload, args.steps, args.warmup)
+    log(f"[bench] {args.workload}: {main_r['ms_per_step']:.3f} ms/step, stages {main_r['stage_ms']}")
+    rec = {
+        "metric": METRIC,
+        "value": round(main_r["T"] / (main_r["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) activations, random-init N(0,1/fan_in) weights",
+        "config": {"workload": args.workload, "T": main_r["T"], "d": main_r["d"], "f": main_r["f"],
+                   "n": main_r["n"], "K": main_r["K"], "parallelism": "single GPU"},
+    }
+    if args.workload == "mixtral_decode":
+        dr = decode_record(main_r)
+        rec["roofline"] = dr["roofline"]
+    else:
+        pr = prefill_record(main_r)
+        rec["roofline"] = pr["roofline"]
+        rec["layer_tflops"] = pr["layer_tflops"]
+        rec["layer_frac_of_mfma_peak"] = pr["layer_frac_of_mfma_peak"]
+    rec["stages_ms"] = {s: round(float(v), 4) for s, v in zip(STAGES, main_r["stage_ms"])}
+    rec["expert_counts"] = main_r["counts"].tolist()
+    if not args.no_decode and args.workload != "mixtral_decode":
+        dr_raw = time_workload("mixtral_decode", max(args.steps, 20), args.warmup)
+        rec["decode"] = decode_record(dr_raw)
+        log(f"[bench] decode: {dr_raw['ms_per_step']:.3f} ms/step, stages {dr_raw['stage_ms']}")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a sample ...")
+        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,138 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse mixture-of-experts layer.
+ *
+ * The layer (card 2.1 "Sparse Mixture of Experts" of the "Mixtral of Experts"
+ * study deck, Jiang et al. 2024):
+ *
+ *     y = sum_{i=0}^{n-1} Softmax(TopK(x . W_g))_i * SwiGLU_i(x)
+ *
+ * A bias-free linear router scores the n experts of every token, the K largest
+ * scores are kept (ties to the lower expert index, kept slots in descending
+ * score order), a softmax over the kept scores gives the gate weights, only the
+ * chosen experts run, and their outputs are summed with those weights (Part 3,
+ * "Pip's token goes to triage", steps 1-4, of "Mixture of Experts: Why Mixtral
+ * Only Wakes Up Two Specialists").  SwiGLU_i(z) = (SiLU(z W1_i) * (z W3_i)) W2_i,
+ * SiLU(u) = u / (1 + e^-u); no biases anywhere.  Expert indices are 0-based.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are DEVICE pointers, row-major, contiguous, owned by the caller.
+ *     The library keeps no pointer after a call returns.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); the
+ *     caller keeps buffers alive until that work completes.
+ *   - Every argument is validated before anything is enqueued; on an error
+ *     nothing is enqueued and the status says why (moe_last_error() has the
+ *     detail).  T == 0 is a valid no-op.  No C++ exception crosses the ABI.
+ *   - Layouts: x[T][d], W_g[d][n] (so logits = x . W_g; a PyTorch nn.Linear
+ *     router weight [n][d] is passed transposed), W1[n][d][f], W3[n][d][f],
+ *     W2[n][f][d].  bf16 entry points take bf16 storage (uint16 bit patterns).
+ *   - Limits: 1 <= K <= n <= 256, K <= 8, T*K < 2^31.  bf16 entry points need
+ *     d % 64 == 0, f % 64 == 0 and 16-byte aligned tensors (MOE_ERR_UNSUPPORTED).
+ *   - The library owns a per-device workspace (routing arrays and the
+ *     intermediate h and o buffers, moe_workspace_bytes() bytes).  It is
+ *     allocated on the first call on a device and grown on demand (the growing
+ *     call synchronises the device); moe_release() frees it.  Calls that share
+ *     a device's workspace must not run concurrently on different streams.
+ *   - Results are deterministic: no float atomics; every output element has a
+ *     single writer and a fixed summation order.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, K < 1, K > n, n < 1, d/f < 1, T < 0 */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside this library's limits (see above) */
+  MOE_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
+  MOE_ERR_NO_MEMORY = 4    /* workspace allocation failed */
+} moe_status_t;
+
+/* Opaque HIP stream handle (hipStream_t). */
+typedef struct ihipStream_t* moe_stream_t;
+
+/*
+ * moe_forward -- the whole layer, bf16 storage, fp32 accumulation.
+ *   x[T][d], Wg[d][n], W1[n][d][f], W3[n][d][f], W2[n][f][d]: bf16.
+ *   y[T][d]: fp32, fully overwritten (the caller adds the residual).
+ * Routing is computed exactly as moe_route does (same kernels).  The SwiGLU
+ * hidden activation is rounded once to bf16 (round-to-nearest-even) before
+ * the down projection; everything else accumulates and is stored in fp32.
+ * The combine sums the K expert outputs in slot order.
+ */
+moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const void* W3,
+                         const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                         int32_t K, float* y, moe_stream_t stream);
+
+/*
+ * moe_forward_traced -- moe_forward that also records caller-created HIP events
+ * (hipEvent_t, passed as void*) on `stream` between its stages, for timing:
+ *   stage_events[0] before the router      [1] after the router
+ *   stage_events[2] after the dispatch     [3] after the gate/up projection
+ *   stage_events[4] after the down proj.   [5] after the combine
+ * Same kernels and results as moe_forward; all six events are required.
+ */
+moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, const void* W3,
+                                const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                                int32_t K, float* y, moe_stream_t stream, void* const* stage_events);
+
+/*
+ * moe_forward_f32 -- the same layer with every input in fp32 (the hidden
+ * activation stays fp32).  No alignment or divisibility requirement.
+ */
+moe_status_t moe_forward_f32(const float* x, const float* Wg, const float* W1, const float* W3,
+                             const float* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                             int32_t K, float* y, moe_stream_t stream);
+
+/*
+ * moe_route -- router, top-K, softmax over the kept K, and the integer dispatch
+ * (steps 1-3 of the walk-through plus the grouping of assignments by expert that
+ * lets each chosen expert run once on its rows; unselected experts are never
+ * evaluated, per the sparse-gating passage of "How a mixture-of-experts model
+ * activates only part of its parameters").  x[T][d], Wg[d][n]: bf16.
+ * Every output is optional (NULL = not written); at least one must be given.
+ *   topk_idx[T][K]  int32  kept experts, descending logit, ties -> lower index
+ *   topk_w[T][K]    fp32   softmax over the kept logits (sums to 1 per token)
+ *   counts[n]       int32  number of assignments per expert
+ *   offsets[n+1]    int32  exclusive prefix sum of counts; offsets[n] = T*K
+ *   perm_token[T*K] int32  token at each position, expert-contiguous, tokens
+ *                          ascending within an expert
+ *   slot_pos[T][K]  int32  position of assignment (t, k): perm_token[slot_pos] = t
+ * The integer outputs are a pure function of the logits' fp32 values.
+ */
+moe_status_t moe_route(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n,
+                       int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
+                       moe_stream_t stream);
+
+/* moe_route_f32 -- moe_route with fp32 x and Wg. */
+moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int32_t n,
+                           int32_t K, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                           int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
+                           moe_stream_t stream);
+
+/* Bytes of library workspace a call of this shape needs (0 on invalid shapes). */
+size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K);
+
+/* Frees the workspace of every device (synchronises each device first). */
+moe_status_t moe_release(void);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,25 @@
+"""MI355X (gfx950) sparse mixture-of-experts layer.
+
+A thin ctypes binding over libmoe.so (include/moe.h).  It only checks and
+marshals arguments: every step of the layer runs in the HIP kernels.  PyTorch
+supplies device memory and the current stream.  If the library has not been
+built, every call raises; there is no CPU fallback.
+"""
+from ._binding import (  # noqa: F401
+    MoEError,
+    STATUS,
+    forward,
+    forward_f32,
+    forward_traced,
+    last_error,
+    lib,
+    lib_path,
+    release,
+    route,
+    route_f32,
+    version,
+    workspace_bytes,
+)
+
+__all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "workspace_bytes", "release",
+           "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

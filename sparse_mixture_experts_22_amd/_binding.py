@@ -1,0 +1,193 @@
+"""ctypes binding of include/moe.h.  Same names as the C entry points, minus
+the ``moe_`` prefix; tensors are torch CUDA(HIP) tensors, the stream is
+torch's current stream unless one is given."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP",
+          4: "MOE_ERR_NO_MEMORY"}
+
+EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32", "moe_workspace_bytes",
+           "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by __graft_entry__.build()).  Raises if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    try:
+        # bind to the HIP runtime torch already carries, so tensors, streams and
+        # events from torch and this library share one runtime instance
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build the HIP library first "
+                           "(python -m sparse_mixture_experts_22_amd.build)")
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.moe_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    L.moe_forward.restype = ctypes.c_int
+    L.moe_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    L.moe_forward_traced.restype = ctypes.c_int
+    L.moe_forward_f32.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    L.moe_forward_f32.restype = ctypes.c_int
+    L.moe_route.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route_f32.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route_f32.restype = ctypes.c_int
+    L.moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.moe_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_release.argtypes = []
+    L.moe_release.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_version.argtypes = []
+    L.moe_version.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def version() -> str:
+    return lib().moe_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MoEError(status, last_error())
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _expect(t, dtype, name, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _forward(fn, dtype, x, Wg, W1, W3, W2, K, y, stream, extra=()):
+    import torch
+    for t, name, nd in ((x, "x", 2), (Wg, "Wg", 2), (W1, "W1", 3), (W3, "W3", 3), (W2, "W2", 3)):
+        _expect(t, dtype, name, nd)
+    T, d = x.shape
+    n = Wg.shape[1]
+    f = W1.shape[2]
+    if Wg.shape != (d, n) or W1.shape != (n, d, f) or W3.shape != (n, d, f) or W2.shape != (n, f, d):
+        raise ValueError("shapes must be x[T][d], Wg[d][n], W1/W3[n][d][f], W2[n][f][d]")
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    else:
+        _expect(y, torch.float32, "y", 2)
+        if tuple(y.shape) != (T, d):
+            raise ValueError("y must be [T][d]")
+    _check(fn(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), T, d, f, n, int(K), _ptr(y),
+              _stream(stream), *extra))
+    return y
+
+
+def forward(x, Wg, W1, W3, W2, K, y=None, stream=None):
+    """moe_forward: bf16 x[T][d], Wg[d][n], W1/W3[n][d][f], W2[n][f][d] -> fp32 y[T][d]."""
+    import torch
+    return _forward(lib().moe_forward, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream)
+
+
+def forward_traced(x, Wg, W1, W3, W2, K, stage_events, y=None, stream=None):
+    """moe_forward_traced: as forward(), recording six caller-created hipEvent_t
+    handles (integers) between the stages on the stream."""
+    import torch
+    if len(stage_events) != 6:
+        raise ValueError("need 6 events")
+    arr = (ctypes.c_void_p * 6)(*stage_events)
+    return _forward(lib().moe_forward_traced, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream,
+                    extra=(ctypes.cast(arr, ctypes.c_void_p),))
+
+
+def forward_f32(x, Wg, W1, W3, W2, K, y=None, stream=None):
+    """moe_forward_f32: the same layer with fp32 inputs."""
+    import torch
+    return _forward(lib().moe_forward_f32, torch.float32, x, Wg, W1, W3, W2, K, y, stream)
+
+
+def _route(fn, dtype, x, Wg, K, outputs, stream):
+    import torch
+    _expect(x, dtype, "x", 2)
+    _expect(Wg, dtype, "Wg", 2)
+    T, d = x.shape
+    n = Wg.shape[1]
+    if Wg.shape[0] != d:
+        raise ValueError("Wg must be [d][n]")
+    dev = x.device
+    shapes = {"topk_idx": ((T, K), torch.int32), "topk_w": ((T, K), torch.float32),
+              "counts": ((n,), torch.int32), "offsets": ((n + 1,), torch.int32),
+              "perm_token": ((T * K,), torch.int32), "slot_pos": ((T, K), torch.int32)}
+    out = {}
+    for name in outputs:
+        shp, dt = shapes[name]
+        out[name] = torch.empty(shp, dtype=dt, device=dev)
+    _check(fn(_ptr(x), _ptr(Wg), T, d, n, int(K), _ptr(out.get("topk_idx")),
+              _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("offsets")),
+              _ptr(out.get("perm_token")), _ptr(out.get("slot_pos")), _stream(stream)))
+    return out
+
+
+ROUTE_OUTPUTS = ("topk_idx", "topk_w", "counts", "offsets", "perm_token", "slot_pos")
+
+
+def route(x, Wg, K, outputs=ROUTE_OUTPUTS, stream=None):
+    """moe_route on bf16 x, Wg; returns a dict of the requested int32/fp32 tensors."""
+    import torch
+    return _route(lib().moe_route, torch.bfloat16, x, Wg, K, outputs, stream)
+
+
+def route_f32(x, Wg, K, outputs=ROUTE_OUTPUTS, stream=None):
+    """moe_route_f32 on fp32 x, Wg."""
+    import torch
+    return _route(lib().moe_route_f32, torch.float32, x, Wg, K, outputs, stream)
+
+
+def workspace_bytes(T, d, f, n, K) -> int:
+    return int(lib().moe_workspace_bytes(T, d, f, n, K))
+
+
+def release() -> None:
+    _check(lib().moe_release())

@@ -1,0 +1,385 @@
+// C ABI of the sparse MoE layer: argument validation, the per-device
+// workspace, and the launch sequence on the caller's stream.
+//
+//   route:   router (+top-K, softmax, block histograms) -> scatter
+//   forward: route -> expert up projection (SwiGLU) -> down projection -> combine
+//
+// The host never reads device data back: all scheduling decisions that depend
+// on the routing (which tiles exist, which rows they hold) are taken on the
+// device from `offsets`.  The only host-side choice is between the tiled
+// grouped GEMM and the weight-streaming kernels, made from the shape alone.
+#include <mutex>
+#include <string>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr int kMaxDevices = 64;
+struct DeviceWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+DeviceWorkspace g_ws[kMaxDevices];
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+enum class Path { kRouteOnly, kBf16, kF32 };
+
+struct Plan {
+  size_t topk_idx = 0, topk_w = 0, hist = 0, counts = 0, offsets = 0, perm_token = 0, slot_pos = 0;
+  size_t h = 0, o = 0, total = 0;
+  bool skinny = false;
+  int splits = 1;
+};
+
+Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path) {
+  Plan p;
+  const int64_t TK = T * K;
+  const int BT = moe::route_block_tokens(n);
+  const int64_t nb = (T + BT - 1) / BT;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.topk_idx = take((size_t)TK * 4);
+  p.topk_w = take((size_t)TK * 4);
+  p.hist = take((size_t)nb * n * 4);
+  p.counts = take((size_t)n * 4);
+  p.offsets = take((size_t)(n + 1) * 4);
+  p.perm_token = take((size_t)TK * 4);
+  p.slot_pos = take((size_t)TK * 4);
+  if (path == Path::kBf16) {
+    p.skinny = TK <= (int64_t)moe::kSkinnyMaxAvgRows * n;
+    p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
+    p.h = take((size_t)TK * f * 2);
+    p.o = take((size_t)p.splits * TK * d * 4);
+  } else if (path == Path::kF32) {
+    p.h = take((size_t)TK * f * 4);
+    p.o = take((size_t)TK * d * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+// Validation shared by every entry point; nothing here touches the GPU.
+moe_status_t check_shape(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, bool need_f) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0");
+  if (d < 1) return fail(MOE_ERR_INVALID_ARG, "d must be >= 1");
+  if (need_f && f < 1) return fail(MOE_ERR_INVALID_ARG, "f must be >= 1");
+  if (n < 1) return fail(MOE_ERR_INVALID_ARG, "n must be >= 1");
+  if (K < 1 || K > n) return fail(MOE_ERR_INVALID_ARG, "K must satisfy 1 <= K <= n");
+  if (n > moe::kMaxN) return fail(MOE_ERR_UNSUPPORTED, "n > 256 experts is not supported");
+  if (K > moe::kMaxK) return fail(MOE_ERR_UNSUPPORTED, "K > 8 is not supported");
+  if (T * (int64_t)K > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (d > INT32_MAX || f > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "d and f must be < 2^31");
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+moe_status_t check_bf16(int64_t d, int64_t f, bool need_f, std::initializer_list<const void*> ptrs) {
+  if (d % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs d % 64 == 0");
+  if (need_f && f % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs f % 64 == 0");
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(MOE_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensors");
+  return MOE_OK;
+}
+
+moe_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Returns the current device's workspace, grown to at least `bytes`.
+moe_status_t get_workspace(size_t bytes, char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace& ws = g_ws[dev];
+  if (ws.bytes < bytes) {
+    if (ws.ptr != nullptr) {
+      e = hipDeviceSynchronize();  // earlier work may still use the old buffer
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      e = hipFree(ws.ptr);
+      ws.ptr = nullptr;
+      ws.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+    }
+    void* p = nullptr;
+    e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MOE_ERR_NO_MEMORY, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
+    }
+    ws.ptr = p;
+    ws.bytes = bytes;
+  }
+  *out = static_cast<char*>(ws.ptr);
+  return MOE_OK;
+}
+
+#define MOE_LAUNCH(call, what)                  \
+  do {                                          \
+    hipError_t err_ = (call);                   \
+    if (err_ != hipSuccess) return hip_fail(err_, what); \
+  } while (0)
+
+template <typename T>
+T* at(char* base, size_t off) {
+  return reinterpret_cast<T*>(base + off);
+}
+
+struct RouteOut {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_token;
+  int32_t* slot_pos;
+};
+
+RouteOut route_buffers(char* ws, const Plan& p, const RouteOut& user) {
+  RouteOut r;
+  r.topk_idx = user.topk_idx ? user.topk_idx : at<int32_t>(ws, p.topk_idx);
+  r.topk_w = user.topk_w ? user.topk_w : at<float>(ws, p.topk_w);
+  r.counts = user.counts ? user.counts : at<int32_t>(ws, p.counts);
+  r.offsets = user.offsets ? user.offsets : at<int32_t>(ws, p.offsets);
+  r.perm_token = user.perm_token ? user.perm_token : at<int32_t>(ws, p.perm_token);
+  r.slot_pos = user.slot_pos ? user.slot_pos : at<int32_t>(ws, p.slot_pos);
+  return r;
+}
+
+template <bool BF16>
+moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                        const RouteOut& user, hipStream_t stream) {
+  moe_status_t st = check_shape(T, d, 1, n, K, false);
+  if (st != MOE_OK) return st;
+  if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
+  if (!user.topk_idx && !user.topk_w && !user.counts && !user.offsets && !user.perm_token &&
+      !user.slot_pos)
+    return fail(MOE_ERR_INVALID_ARG, "at least one routing output must be non-null");
+  if (BF16) {
+    st = check_bf16(d, 0, false, {x, Wg});
+    if (st != MOE_OK) return st;
+  }
+  if (T == 0) return MOE_OK;  // nothing is written
+  const Plan p = make_plan(T, d, 0, n, K, Path::kRouteOnly);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const RouteOut r = route_buffers(ws, p, user);
+  int* hist = at<int>(ws, p.hist);
+  if (BF16)
+    MOE_LAUNCH(moe::launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
+                                       T, d, n, K, r.topk_idx, r.topk_w, hist, stream),
+               "router kernel launch");
+  else
+    MOE_LAUNCH(moe::launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d,
+                                      n, K, r.topk_idx, r.topk_w, hist, stream),
+               "router kernel launch");
+  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
+                                 r.slot_pos, stream),
+             "scatter kernel launch");
+  return MOE_OK;
+}
+
+moe_status_t check_forward_ptrs(const void* x, const void* Wg, const void* W1, const void* W3,
+                                const void* W2, const void* y) {
+  if (!x || !Wg || !W1 || !W3 || !W2 || !y)
+    return fail(MOE_ERR_INVALID_ARG, "x, Wg, W1, W3, W2 and y must be non-null");
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace {
+
+moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,
+                          int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
+                          hipStream_t stream, void* const* ev) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, d, f, n, K, true);
+  if (st != MOE_OK) return st;
+  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  if (st != MOE_OK) return st;
+  st = check_bf16(d, f, true, {x, Wg, W1, W3, W2, y});
+  if (st != MOE_OK) return st;
+  if (ev != nullptr)
+    for (int i = 0; i < 6; ++i)
+      if (ev[i] == nullptr) return fail(MOE_ERR_INVALID_ARG, "stage_events must hold 6 events");
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(T, d, f, n, K, Path::kBf16);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream) : hipSuccess;
+  };
+  const RouteOut r = route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  int* hist = at<int>(ws, p.hist);
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* o = at<float>(ws, p.o);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const int64_t TK = T * K;
+  MOE_LAUNCH(mark(0), "hipEventRecord");
+  MOE_LAUNCH(moe::launch_router_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r.topk_idx,
+                                     r.topk_w, hist, stream),
+             "router kernel launch");
+  MOE_LAUNCH(mark(1), "hipEventRecord");
+  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
+                                 r.slot_pos, stream),
+             "scatter kernel launch");
+  MOE_LAUNCH(mark(2), "hipEventRecord");
+  const auto* w1 = static_cast<const uint16_t*>(W1);
+  const auto* w3 = static_cast<const uint16_t*>(W3);
+  const auto* w2 = static_cast<const uint16_t*>(W2);
+  if (p.skinny) {
+    MOE_LAUNCH(moe::launch_skinny_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, h, stream),
+               "up-projection kernel launch");
+    MOE_LAUNCH(mark(3), "hipEventRecord");
+    MOE_LAUNCH(moe::launch_skinny_down(h, w2, r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
+               "down-projection kernel launch");
+  } else {
+    MOE_LAUNCH(moe::launch_prefill_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, h,
+                                      stream),
+               "up-projection kernel launch");
+    MOE_LAUNCH(mark(3), "hipEventRecord");
+    MOE_LAUNCH(moe::launch_prefill_down(h, w2, r.offsets, TK, n, (int)f, (int)d, o, stream),
+               "down-projection kernel launch");
+  }
+  MOE_LAUNCH(mark(4), "hipEventRecord");
+  MOE_LAUNCH(moe::launch_combine(o, p.splits, TK, r.topk_w, r.slot_pos, T, d, K, y, stream),
+             "combine kernel launch");
+  MOE_LAUNCH(mark(5), "hipEventRecord");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,
+                         int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
+                         moe_stream_t stream) {
+  return forward_bf16(x, Wg, W1, W3, W2, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream),
+                      nullptr);
+}
+
+moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, const void* W3,
+                                const void* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
+                                float* y, moe_stream_t stream, void* const* stage_events) {
+  if (stage_events == nullptr) return fail(MOE_ERR_INVALID_ARG, "stage_events must be non-null");
+  return forward_bf16(x, Wg, W1, W3, W2, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream),
+                      stage_events);
+}
+
+moe_status_t moe_forward_f32(const float* x, const float* Wg, const float* W1, const float* W3,
+                             const float* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
+                             float* y, moe_stream_t stream_) {
+  g_last_error.clear();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  moe_status_t st = check_shape(T, d, f, n, K, true);
+  if (st != MOE_OK) return st;
+  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(T, d, f, n, K, Path::kF32);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const RouteOut r = route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  int* hist = at<int>(ws, p.hist);
+  float* h = at<float>(ws, p.h);
+  float* o = at<float>(ws, p.o);
+  const int64_t TK = T * K;
+  MOE_LAUNCH(moe::launch_router_f32(x, Wg, T, d, n, K, r.topk_idx, r.topk_w, hist, stream),
+             "router kernel launch");
+  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
+                                 r.slot_pos, stream),
+             "scatter kernel launch");
+  MOE_LAUNCH(moe::launch_f32_up(x, T, r.perm_token, W1, W3, r.offsets, TK, n, (int)d, (int)f, h, stream),
+             "up-projection kernel launch");
+  MOE_LAUNCH(moe::launch_f32_down(h, W2, r.offsets, TK, n, (int)f, (int)d, o, stream),
+             "down-projection kernel launch");
+  MOE_LAUNCH(moe::launch_combine(o, 1, TK, r.topk_w, r.slot_pos, T, d, K, y, stream),
+             "combine kernel launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                       int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                       int32_t* perm_token, int32_t* slot_pos, moe_stream_t stream) {
+  g_last_error.clear();
+  return route_impl<true>(x, Wg, T, d, n, K,
+                          RouteOut{topk_idx, topk_w, counts, offsets, perm_token, slot_pos},
+                          reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                           int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                           int32_t* perm_token, int32_t* slot_pos, moe_stream_t stream) {
+  g_last_error.clear();
+  return route_impl<false>(x, Wg, T, d, n, K,
+                           RouteOut{topk_idx, topk_w, counts, offsets, perm_token, slot_pos},
+                           reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K) {
+  if (check_shape(T, d, f, n, K, true) != MOE_OK) return 0;
+  const Plan a = make_plan(T, d, f, n, K, Path::kBf16);
+  const Plan b = make_plan(T, d, f, n, K, Path::kF32);
+  return a.total > b.total ? a.total : b.total;
+}
+
+moe_status_t moe_release(void) {
+  g_last_error.clear();
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) cur = 0;
+  for (int dev = 0; dev < kMaxDevices; ++dev) {
+    DeviceWorkspace& ws = g_ws[dev];
+    if (ws.ptr == nullptr) continue;
+    hipError_t e = hipSetDevice(dev);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipFree(ws.ptr);
+    ws.ptr = nullptr;
+    ws.bytes = 0;
+    if (e != hipSuccess) {
+      (void)hipSetDevice(cur);
+      return hip_fail(e, "moe_release");
+    }
+  }
+  (void)hipSetDevice(cur);
+  return MOE_OK;
+}
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_NO_MEMORY: return "MOE_ERR_NO_MEMORY";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_version(void) { return "moe-mi355x 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Expert projections for decode-sized batches: few rows per expert, so the
+// cost is streaming every touched expert's weights from HBM once.
+//
+// The pages note that a sparse MoE holds all experts' parameters in memory
+// while a token uses only its two ("Why total and active both matter", Part 4
+// of "Mixture of Experts: Why Mixtral Only Wakes Up Two Specialists"); with a
+// small batch every expert is still touched, and the layer is bound by reading
+// 3*d*f bf16 weights per touched expert.
+//
+// Work unit: one workgroup (4 waves) per (expert, 128-column block[, K split]).
+// The 4 waves split the reduction dimension; each lane loads 8 rows x 16 bytes
+// of the weight block (one 8x8 bf16 block), transposes it in registers and
+// feeds eight v_mfma_f32_16x16x32_bf16 directly as B operands - the weights
+// never pass through LDS.  The MFMA column index c of fragment j stands for
+// weight column col0 + c*8 + j.  A fragments (16 token rows) come straight
+// from global memory (x or h is tiny and stays in L2).  Loads of the next K
+// step are issued before the MFMAs of the current one.  The 4 partial tiles
+// are summed in LDS in wave order (fixed order, deterministic), then the
+// SwiGLU epilogue (up) or the fp32 store of a partial sum (down) follows.
+// Rows beyond 16 per expert are handled by further passes over the weights.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], bf16x8_t (&out)[8]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r0 = (&in[2 * q].x)[p];
+      const uint32_t r1 = (&in[2 * q + 1].x)[p];
+      lo[q] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
+      hi[q] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+    }
+    uint4 l = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    uint4 h = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    out[2 * p] = *reinterpret_cast<bf16x8_t*>(&l);
+    out[2 * p + 1] = *reinterpret_cast<bf16x8_t*>(&h);
+  }
+}
+
+__device__ __forceinline__ void load_block(uint4 (&q)[8], const uint16_t* src, int64_t row_stride,
+                                           bool ok) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+    q[r] = ok ? *reinterpret_cast<const uint4*>(src + (int64_t)r * row_stride)
+              : make_uint4(0u, 0u, 0u, 0u);
+}
+
+__device__ __forceinline__ void mma_block(const uint4 (&q)[8], const bf16x8_t& a, f32x4_t (&acc)[8]) {
+  bf16x8_t fr[8];
+  transpose8x8(q, fr);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fr[c], acc[c], 0, 0, 0);
+}
+
+// MODE 1: up.  Waves 0-1 stream W1, waves 2-3 stream W3, each over half of K;
+//         A rows are gathered from x via perm_token; h = SiLU(a) * b in bf16.
+// MODE 2: down.  The 4 waves stream W2 over quarters of this split's K range;
+//         A rows are h; o[split] receives the fp32 partial sum.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void skinny_kernel(
+    const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
+    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
+    const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
+    uint16_t* __restrict__ hout, float* __restrict__ oout) {
+  __shared__ float red[4][32][64];  // per-wave partial accumulators
+
+  const int NB = (N + 127) / 128;
+  int bid = blockIdx.x;
+  const int sp = bid % splits;
+  bid /= splits;
+  const int nb = bid % NB;
+  const int e = bid / NB;
+  if (e >= n) return;
+  const int row_beg = offsets[e];
+  const int cnt = offsets[e + 1] - row_beg;
+  if (cnt <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+
+  // reduction range of this wave, in steps of 32
+  constexpr int KPARTS = (MODE == 1) ? 2 : 4;
+  const int part = (MODE == 1) ? (wave & 1) : wave;
+  const int nkc = Kdim / 32;
+  const int kc0 = (int)((int64_t)sp * nkc / splits);
+  const int kc1 = (int)((int64_t)(sp + 1) * nkc / splits);
+  const int wk0 = kc0 + (int)((int64_t)part * (kc1 - kc0) / KPARTS);
+  const int wk1 = kc0 + (int)((int64_t)(part + 1) * (kc1 - kc0) / KPARTS);
+
+  const int col0 = nb * 128 + r16 * 8;
+  const bool b_ok = col0 < N;
+  const uint16_t* bmat = (MODE == 1 && wave >= 2) ? B3 : B1;
+  const uint16_t* bsrc = bmat + (int64_t)e * Kdim * N + (b_ok ? col0 : 0) + (int64_t)(g * 8) * N;
+  const int64_t kstep = (int64_t)32 * N;
+
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
+    const int rr = (m0 + r16) < cnt ? (m0 + r16) : (cnt - 1);
+    const int p = (int)min<int64_t>(max(row_beg + rr, 0), TK - 1);
+    const int64_t arow = (MODE == 1) ? (int64_t)min(max(perm_token[p], 0), a_rows - 1) : (int64_t)p;
+    const uint16_t* asrc = A + arow * Kdim + g * 8;
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ping-pong: step kc in (qa, aa), step kc+1 in (qb, ab)
+    uint4 qa[8], qb[8];
+    bf16x8_t aa, ab;
+    int kc = wk0;
+    if (kc < wk1) {
+      load_block(qa, bsrc + kc * kstep, N, b_ok);
+      aa = *reinterpret_cast<const bf16x8_t*>(asrc + kc * 32);
+    }
+    while (kc < wk1) {
+      if (kc + 1 < wk1) {
+        load_block(qb, bsrc + (kc + 1) * kstep, N, b_ok);
+        ab = *reinterpret_cast<const bf16x8_t*>(asrc + (kc + 1) * 32);
+      }
+      mma_block(qa, aa, acc);
+      if (kc + 2 < wk1) {
+        load_block(qa, bsrc + (kc + 2) * kstep, N, b_ok);
+        aa = *reinterpret_cast<const bf16x8_t*>(asrc + (kc + 2) * 32);
+      }
+      if (kc + 1 < wk1) mma_block(qb, ab, acc);
+      kc += 2;
+    }
+    // partial tiles -> LDS; register slot q = c*4 + j
+    __syncthreads();  // previous pass finished reading red
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][c * 4 + j][lane] = acc[c][j];
+    __syncthreads();
+    // thread (qg = tid/64, lane) finishes slots q = qg*8 .. qg*8+7
+    const int qg = tid >> 6;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = qg * 8 + i;
+      const int c = q >> 2;
+      const int j = q & 3;
+      const int row = m0 + 4 * (lane >> 4) + j;  // D row of the 16x16 MFMA
+      const int colo = nb * 128 + (lane & 15) * 8 + c;
+      if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
+      if (MODE == 1) {
+        const float va = red[0][q][lane] + red[1][q][lane];
+        const float vb = red[2][q][lane] + red[3][q][lane];
+        hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
+      } else {
+        const float v = ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
+        oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
+                            const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
+                            uint16_t* h, hipStream_t s) {
+  const int NB = (f + 127) / 128;
+  hipLaunchKernelGGL((skinny_kernel<1>), dim3((unsigned)(n * NB)), dim3(256), 0, s, x, perm_token,
+                     W1, W3, offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
+                              int n, int f, int d, int splits, float* o, hipStream_t s) {
+  const int NB = (d + 127) / 128;
+  hipLaunchKernelGGL((skinny_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(256), 0, s, h,
+                     (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, splits,
+                     (int)TK, TK, (uint16_t*)nullptr, o);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,70 @@
+// Internal interface between the C-ABI host layer (api.hip) and the kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxN = 256;  // experts per layer
+constexpr int kMaxK = 8;    // experts kept per token
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Tokens per routing block: the router and the scatter agree on it.
+inline int route_block_tokens(int n) { return n <= 128 ? 128 : 64; }
+
+// Rows of an expert handled by one prefill tile.
+constexpr int kPrefillBM = 256;
+
+// Average assignments per expert at or below which the weight-streaming
+// ("skinny") expert kernels are used instead of the tiled grouped GEMM.
+constexpr int kSkinnyMaxAvgRows = 24;
+// Split of the down projection's reduction in the skinny path.
+constexpr int kSkinnyDownSplits = 4;
+
+// ---------------------------------------------------------------- routing
+hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                              int K, int* topk_idx, float* topk_w, int* hist, hipStream_t s);
+hipError_t launch_router_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
+                             int* topk_idx, float* topk_w, int* hist, hipStream_t s);
+hipError_t launch_scatter(const int* topk_idx, const int* hist, int64_t T, int n, int K,
+                          int* counts, int* offsets, int* perm_token, int* slot_pos, hipStream_t s);
+
+// ------------------------------------------------------ expert projections
+// Gate/up: h[p][:] = SiLU(x[perm_token[p]] W1_e) * (x[perm_token[p]] W3_e), bf16 out.
+hipError_t launch_prefill_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
+                             const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
+                             uint16_t* h, hipStream_t s);
+// Down: o[p][:] = h[p] W2_e, fp32 out.
+hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
+                               int n, int f, int d, float* o, hipStream_t s);
+hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
+                            const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
+                            uint16_t* h, hipStream_t s);
+// Down with the reduction over f split in `splits` parts: o[s][p][:] partial sums.
+hipError_t launch_skinny_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
+                              int n, int f, int d, int splits, float* o, hipStream_t s);
+hipError_t launch_f32_up(const float* x, int64_t T, const int* perm_token, const float* W1, const float* W3,
+                         const int* offsets, int64_t TK, int n, int d, int f, float* h, hipStream_t s);
+hipError_t launch_f32_down(const float* h, const float* W2, const int* offsets, int64_t TK, int n,
+                           int f, int d, float* o, hipStream_t s);
+
+// ----------------------------------------------------------------- combine
+// y[t][:] = sum_k topk_w[t][k] * (sum_s o[s][slot_pos[t][k]][:]), k and s ascending.
+hipError_t launch_combine(const float* o, int splits, int64_t TK, const float* topk_w,
+                          const int* slot_pos, int64_t T, int64_t d, int K, float* y, hipStream_t s);
+
+// bf16 round-to-nearest-even of a finite float.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  uint32_t b = __float_as_uint(v);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
+
+}  // namespace moe

@@ -1,13 +1,18 @@
 """Seeded synthetic MoE-layer inputs (x, W_g, W1, W3, W2).
 
 Recipe (stated once, used by tests and the benchmark alike):
-  * generator: numpy ``default_rng(seed)`` (PCG64); draw order x, W_g, W1, W3, W2;
+  * generator: numpy PCG64.  ``SeedSequence(seed).spawn(5)`` gives one child per
+    tensor, in the order x, W_g, W1, W3, W2.  Each tensor is drawn in blocks of
+    whole rows along its first axis (R = max(1, 2**22 // elements_per_row) rows
+    per block); block b uses ``default_rng(child.spawn(n_blocks)[b])``.  Blocks
+    are independent, so they are drawn in parallel threads;
   * standard normals are drawn in float32 and scaled:
       x ~ N(0, 1); W_g, W1, W3 ~ N(0, 1/d); W2 ~ N(0, 1/f)   (fan-in scaling);
   * bf16 configurations round every tensor once, float32 -> bf16 with
     round-to-nearest-even; the fp32 configuration keeps float32;
   * ``routing="skewed"`` builds the router as W_g[:, i] = s_i * u_i + b_i * v with
-    u_i, v ~ N(0, 1/d), s = (1, ..., 1, 0.1) and b = (+16, -16, ..., -16): expert 0
+    u_i, v ~ N(0, 1/d) (u from the W_g child's first spawned child, v from its
+    second), s = (1, ..., 1, 0.1) and b = (+16, -16, ..., -16): expert 0
     wins the top-1 pick for roughly half the tokens and the last expert rarely does.
 
 Shapes follow the layer equation of the Mixtral study deck (card 2.1): x is
@@ -18,6 +23,8 @@ d = 4096, f = 14336, n = 8, K = 2.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -43,9 +50,12 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     flat_in = a.reshape(-1).view(np.uint32)
     flat_out = out.reshape(-1)
     for s in range(0, flat_in.size, _CHUNK):
-        b = flat_in[s:s + _CHUNK].astype(np.uint64)
-        b += 0x7FFF + ((b >> 16) & 1)
-        flat_out[s:s + _CHUNK] = (b >> 16).astype(np.uint16)
+        b = flat_in[s:s + _CHUNK]
+        lsb = (b >> 16) & np.uint32(1)
+        lsb += np.uint32(0x7FFF)
+        lsb += b  # finite inputs: at most 0xFF7FFFFF + 0x8000, no uint32 overflow
+        lsb >>= 16
+        flat_out[s:s + _CHUNK] = lsb
     return out
 
 
@@ -86,11 +96,33 @@ class MoEInputs:
         return a.astype(np.float64)
 
 
-def _normal(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
-    a = rng.standard_normal(size=shape, dtype=np.float32)
-    if scale != 1.0:
-        a *= np.float32(scale)
-    return a
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _draw(ss: np.random.SeedSequence, shape, scale: float, to_bf16: bool) -> np.ndarray:
+    """N(0, scale^2) in float32 (or its bf16 bits), drawn block-wise along axis 0."""
+    shape = tuple(int(v) for v in shape)
+    rows = shape[0]
+    per_row = int(np.prod(shape[1:])) if len(shape) > 1 else 1
+    R = max(1, (1 << 22) // max(per_row, 1))
+    nblk = (rows + R - 1) // R
+    kids = ss.spawn(nblk)
+    out = np.empty(shape, dtype=np.uint16 if to_bf16 else np.float32)
+
+    def work(b):
+        lo, hi = b * R, min(rows, (b + 1) * R)
+        blk = np.random.default_rng(kids[b]).standard_normal(size=(hi - lo,) + shape[1:],
+                                                             dtype=np.float32)
+        if scale != 1.0:
+            blk *= np.float32(scale)
+        out[lo:hi] = bf16_bits_from_f32(blk) if to_bf16 else blk
+
+    if nblk == 1:
+        work(0)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=_THREADS) as ex:
+            list(ex.map(work, range(nblk)))
+    return out
 
 
 def make_inputs(T: int, d: int, f: int, n: int, K: int, dtype: str = "bf16",
@@ -102,29 +134,31 @@ def make_inputs(T: int, d: int, f: int, n: int, K: int, dtype: str = "bf16",
     leaves the expert weights as None."""
     if dtype not in ("bf16", "f32"):
         raise ValueError(dtype)
-    rng = np.random.default_rng(seed)
-    conv = bf16_bits_from_f32 if dtype == "bf16" else (lambda a: a)
-    x = conv(_normal(rng, (T, d), 1.0))
+    bf = dtype == "bf16"
+    s_x, s_wg, s_w1, s_w3, s_w2 = np.random.SeedSequence(seed).spawn(5)
+    x = _draw(s_x, (T, d), 1.0, bf)
     if routing == "uniform":
-        wg = _normal(rng, (d, n), 1.0 / np.sqrt(d))
+        wg = _draw(s_wg, (d, n), 1.0 / np.sqrt(d), False)
     elif routing == "skewed":
-        u = _normal(rng, (d, n), 1.0 / np.sqrt(d))
-        v = _normal(rng, (d,), 1.0 / np.sqrt(d))
-        s = np.ones(n, dtype=np.float32)
-        s[n - 1] = 0.1
+        s_u, s_v = s_wg.spawn(2)
+        u = _draw(s_u, (d, n), 1.0 / np.sqrt(d), False)
+        v = _draw(s_v, (d,), 1.0 / np.sqrt(d), False)
+        sc = np.ones(n, dtype=np.float32)
+        sc[n - 1] = 0.1
         b = np.full(n, -16.0, dtype=np.float32)
         b[0] = 16.0
-        wg = u * s[None, :] + v[:, None] * b[None, :]
+        wg = u * sc[None, :] + v[:, None] * b[None, :]
     else:
         raise ValueError(routing)
     if wg_zero:
         wg = np.zeros_like(wg)
-    Wg = conv(wg.astype(np.float32))
+    wg = wg.astype(np.float32)
+    Wg = bf16_bits_from_f32(wg) if bf else wg
     if router_only:
         return MoEInputs(x=x, Wg=Wg, W1=None, W3=None, W2=None, T=T, d=d, f=f, n=n, K=K, dtype=dtype)
-    W1 = conv(_normal(rng, (n, d, f), 1.0 / np.sqrt(d)))
-    W3 = conv(_normal(rng, (n, d, f), 1.0 / np.sqrt(d)))
-    W2 = conv(_normal(rng, (n, f, d), 1.0 / np.sqrt(f)))
+    W1 = _draw(s_w1, (n, d, f), 1.0 / np.sqrt(d), bf)
+    W3 = _draw(s_w3, (n, d, f), 1.0 / np.sqrt(d), bf)
+    W2 = _draw(s_w2, (n, f, d), 1.0 / np.sqrt(f), bf)
     return MoEInputs(x=x, Wg=Wg, W1=W1, W3=W3, W2=W2, T=T, d=d, f=f, n=n, K=K, dtype=dtype)
 
 

@@ -1,0 +1,112 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects invalid arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _lib():
+    import sparse_mixture_experts_22_amd as moe
+    if not os.path.exists(moe.lib_path()):
+        pytest.skip("libmoe.so not built")
+    return moe, moe.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("moe_forward", "moe_forward_f32", "moe_route", "moe_route_f32", "moe_workspace_bytes",
+              "moe_release", "moe_status_string", "moe_last_error", "moe_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    moe, L = _lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(moe._binding.EXPORTS)
+
+
+def test_status_strings():
+    _, L = _lib()
+    for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
+                       (3, b"MOE_ERR_HIP"), (4, b"MOE_ERR_NO_MEMORY")]:
+        assert L.moe_status_string(code) == name
+
+
+# Fake, never-dereferenced device addresses: validation rejects these calls
+# before any HIP call is made.
+A16 = 0x10000
+P = [A16 * (i + 1) for i in range(6)]
+
+
+@pytest.mark.parametrize("T,d,f,n,K,status", [
+    (-1, 64, 64, 8, 2, 1),     # T < 0
+    (4, 0, 64, 8, 2, 1),       # d < 1
+    (4, 64, 0, 8, 2, 1),       # f < 1
+    (4, 64, 64, 0, 1, 1),      # n < 1
+    (4, 64, 64, 8, 0, 1),      # K < 1
+    (4, 64, 64, 8, 9, 1),      # K > n
+    (4, 64, 64, 300, 2, 2),    # n > 256
+    (4, 64, 64, 16, 9, 2),     # K > 8
+    (4, 96, 64, 8, 2, 2),      # bf16 needs d % 64 == 0
+    (4, 64, 96, 8, 2, 2),      # bf16 needs f % 64 == 0
+    (2 ** 30, 64, 64, 8, 2, 2),  # T*K >= 2^31
+])
+def test_forward_validation(T, d, f, n, K, status):
+    moe, L = _lib()
+    assert L.moe_forward(P[0], P[1], P[2], P[3], P[4], T, d, f, n, K, P[5], None) == status
+    assert moe.last_error() != ""
+
+
+def test_forward_null_and_misaligned_pointers():
+    moe, L = _lib()
+    assert L.moe_forward(None, P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, P[5], None) == 1
+    assert L.moe_forward(P[0], P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, None, None) == 1
+    assert L.moe_forward(P[0] + 2, P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, P[5], None) == 2
+    assert "aligned" in moe.last_error()
+    # the fp32 path has no alignment rule, but still checks pointers and shapes
+    assert L.moe_forward_f32(None, P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, P[5], None) == 1
+    assert L.moe_forward_f32(P[0], P[1], P[2], P[3], P[4], 4, 64, 64, 8, 9, P[5], None) == 1
+
+
+def test_empty_batch_is_a_noop_without_gpu():
+    _, L = _lib()
+    assert L.moe_forward(P[0], P[1], P[2], P[3], P[4], 0, 64, 64, 8, 2, P[5], None) == 0
+    assert L.moe_forward_f32(P[0], P[1], P[2], P[3], P[4], 0, 64, 64, 8, 2, P[5], None) == 0
+    assert L.moe_route(P[0], P[1], 0, 64, 8, 2, P[2], None, None, None, None, None, None) == 0
+
+
+def test_route_validation():
+    moe, L = _lib()
+    # no output requested
+    assert L.moe_route(P[0], P[1], 4, 64, 8, 2, None, None, None, None, None, None, None) == 1
+    assert L.moe_route(None, P[1], 4, 64, 8, 2, P[2], None, None, None, None, None, None) == 1
+    assert L.moe_route(P[0], P[1], 4, 64, 8, 0, P[2], None, None, None, None, None, None) == 1
+    assert L.moe_route(P[0], P[1], 4, 72, 8, 2, P[2], None, None, None, None, None, None) == 2
+    assert L.moe_route_f32(P[0], P[1], 4, 64, 4, 5, P[2], None, None, None, None, None, None) == 1
+
+
+def test_workspace_bytes():
+    moe, L = _lib()
+    assert moe.workspace_bytes(8192, 4096, 14336, 8, 2) > 8192 * 2 * 14336 * 2 + 8192 * 2 * 4096 * 4
+    assert moe.workspace_bytes(8192, 4096, 14336, 8, 9) == 0
+    assert moe.workspace_bytes(32, 4096, 14336, 8, 2) > 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import sparse_mixture_experts_22_amd._binding as b
+    monkeypatch.setattr(b, "_LIB", None)
+    monkeypatch.setattr(b, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        b.lib()

@@ -1,0 +1,155 @@
+"""moe_forward / moe_forward_f32 on the GPU against the fp64 oracle.
+
+Small shapes are compared on every row; they span several row and column tiles
+with ragged tails, both expert kernels (tiled grouped GEMM and the
+weight-streaming path) and the degenerate cases.  The five named
+configurations run at full size in the same launch configuration the benchmark
+times; their routing is checked on every token and y on a seeded row sample
+(the oracle evaluates those rows one expert at a time).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import config_inputs, log, sample_rows, upload
+from parity import (BF16_MAX_REL, BF16_MEAN_REL, F32_MAX_REL, F32_MEAN_REL, assert_rows_close,
+                    check_routing)
+from synth import bf16_bits_from_f32, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import sparse_mixture_experts_22_amd as moe
+    return moe
+
+
+def _run(inp, dev=None):
+    import torch
+    moe = _moe()
+    dev = dev or upload(inp)
+    fn = moe.forward if inp.dtype == "bf16" else moe.forward_f32
+    y = fn(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], inp.K)
+    rfn = moe.route if inp.dtype == "bf16" else moe.route_f32
+    rt = rfn(dev["x"], dev["Wg"], inp.K)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), {k: v.cpu().numpy() for k, v in rt.items()}
+
+
+def _check_full(inp, tol=None):
+    log(f"forward: T={inp.T} d={inp.d} f={inp.f} n={inp.n} K={inp.K} dtype={inp.dtype}")
+    y, rt = _run(inp)
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
+    sub = check_routing(r, rt, inp.K)
+    ref = oracle.forward_with_selection(inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"),
+                                        inp.f64("W2"), sub)
+    mx, mn = tol or ((BF16_MAX_REL, BF16_MEAN_REL) if inp.dtype == "bf16" else (F32_MAX_REL, F32_MEAN_REL))
+    rel = assert_rows_close(y, ref, mx, mn)
+    log(f"  max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
+    return y
+
+
+def test_forward_tiny_fp32():
+    _check_full(config_inputs("tiny_fp32"))
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (2000, 192, 320, 4, 2),   # tiled path: 4 row tiles per expert, ragged rows and columns
+    (700, 256, 384, 8, 2),    # tiled path, one row tile per expert
+    (4096, 128, 128, 64, 2),  # tiled path, many experts
+    (40, 256, 320, 8, 2),     # weight-streaming path, column tail
+    (512, 128, 128, 64, 2),   # weight-streaming path, many experts
+    (300, 128, 192, 4, 4),    # K = n: dense softmax mixture
+    (300, 128, 192, 6, 1),    # K = 1
+    (257, 64, 128, 1, 1),     # n = K = 1: dense SwiGLU FFN
+    (1, 64, 64, 8, 2),        # single token
+    (600, 64, 128, 130, 4),   # 64-token routing blocks
+])
+def test_forward_bf16_shapes(T, d, f, n, K):
+    _check_full(make_inputs(T, d, f, n, K, dtype="bf16", seed=T + 31 * n + K))
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [(333, 48, 80, 6, 2), (64, 100, 36, 3, 3), (1, 8, 8, 2, 1)])
+def test_forward_f32_shapes(T, d, f, n, K):
+    _check_full(make_inputs(T, d, f, n, K, dtype="f32", seed=T + n))
+
+
+@pytest.mark.parametrize("T", [40, 3000])
+def test_forward_all_tokens_to_two_experts(T):
+    # a constant input feature with a large router weight sends every token to
+    # experts 0 and 1: one expert holds all T rows (several row passes / tiles)
+    inp = make_inputs(T, 128, 192, 8, 2, dtype="bf16", seed=T)
+    one = bf16_bits_from_f32(np.array([1.0], dtype=np.float32))[0]
+    inp.x[:, 0] = one
+    wg = np.zeros(8, dtype=np.float32)
+    wg[0], wg[1] = 60.0, 50.0
+    inp.Wg[0, :] = bf16_bits_from_f32(wg)
+    y = _check_full(inp)
+    assert np.isfinite(y).all()
+
+
+def test_forward_unselected_experts_are_never_read():
+    # experts 4..7 never win; their weights hold NaN bit patterns, y must stay finite
+    inp = make_inputs(500, 128, 192, 8, 2, dtype="bf16", seed=4)
+    one = bf16_bits_from_f32(np.array([1.0], dtype=np.float32))[0]
+    inp.x[:, 0] = one
+    col = np.zeros(8, dtype=np.float32)
+    col[4:] = -200.0
+    inp.Wg[0, :] = bf16_bits_from_f32(col)
+    clean = _run(inp)[0]
+    for name in ("W1", "W3", "W2"):
+        getattr(inp, name)[4:] = np.uint16(0x7FC0)  # bf16 quiet NaN
+    y, rt = _run(inp)
+    assert not np.isin(rt["topk_idx"], [4, 5, 6, 7]).any()
+    assert np.isfinite(y).all()
+    np.testing.assert_array_equal(y, clean)
+
+
+def test_forward_is_deterministic():
+    for args in [(3000, 256, 384, 8, 2), (48, 256, 384, 8, 2)]:
+        inp = make_inputs(*args, dtype="bf16", seed=5)
+        dev = upload(inp)
+        a, _ = _run(inp, dev)
+        b, _ = _run(inp, dev)
+        np.testing.assert_array_equal(a, b)
+
+
+def test_invalid_call_enqueues_nothing():
+    import torch
+    moe = _moe()
+    inp = make_inputs(64, 64, 64, 8, 2, dtype="bf16", seed=1)
+    dev = upload(inp)
+    y = torch.full((64, 64), 7.0, device=dev["x"].device)
+    with pytest.raises(moe.MoEError):
+        moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], 9, y=y)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,rows", [("mixtral_decode", 32), ("mixtral_prefill", 128),
+                                       ("mixtral_skewed", 128), ("many_experts", 256)])
+def test_forward_full_configs(name, rows):
+    import torch
+    moe = _moe()
+    inp = config_inputs(name)
+    log(f"full config {name}: T={inp.T} d={inp.d} f={inp.f} n={inp.n} K={inp.K}")
+    dev = upload(inp)
+    y = moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], inp.K)
+    rt = moe.route(dev["x"], dev["Wg"], inp.K)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    rt = {k: v.cpu().numpy() for k, v in rt.items()}
+    del dev
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
+    sub = check_routing(r, rt, inp.K)
+    rs = sample_rows(inp.T, rows)
+    ref = oracle.forward_with_selection(
+        inp.f64("x")[rs], inp.f64("Wg"),
+        lambda e: inp.expert_f64("W1", e), lambda e: inp.expert_f64("W3", e),
+        lambda e: inp.expert_f64("W2", e), sub[rs])
+    rel = assert_rows_close(y[rs], ref, BF16_MAX_REL, BF16_MEAN_REL)
+    assert np.isfinite(y).all()
+    log(f"  {name}: rows={len(rs)} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} "
+        f"near-ties={(r['margin'] <= 1e-3).sum()}")
