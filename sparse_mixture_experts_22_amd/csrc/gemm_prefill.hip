@@ -14,16 +14,24 @@
 // Tiling: a 256-thread workgroup (4 waves, one per SIMD) computes a 256-row x
 // 256-column fp32 accumulator tile (for MODE 1: 128 W1 columns + the same 128
 // W3 columns) with v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 (16 MFMA
-// tiles, 256 accumulator registers).  K advances in steps of 64 through two
-// LDS stages (2 x 64 KiB), global loads of step k+1 overlap the MFMAs of step k.
+// tiles, 256 accumulator registers).  K advances in steps of 32 through a ring
+// of 4 LDS stages (32 KiB each): global loads for step k+3 are in flight while
+// step k is multiplied.
 //
-// The weights are [K][N] row-major (N contiguous) but MFMA wants each lane to
-// hold 8 consecutive K values of one column.  Each thread therefore loads an
-// 8 (k) x 8 (n) bf16 block as eight 16-byte row segments, transposes it in
-// registers with byte permutes, and writes eight 16-byte column segments to
-// LDS stored [n][k].  A and B rows in LDS are 128 bytes; the 16-byte chunk
-// index is XOR-swizzled with (row & 7) so that the MFMA fragment reads (one
-// row per lane, same chunk) and the stores hit distinct banks.
+// Data movement is HBM/L2 -> LDS directly (global_load_lds, 16 bytes per lane,
+// lane l writing bytes 16*l.. of a 1 KiB block), with no register staging and
+// no LDS store instructions.  Which global 16-byte chunk a lane fetches is
+// permuted so the LDS image is XOR-swizzled:
+//   A (activations, [row][k], 64-byte rows): chunk c of row r sits at
+//     position c ^ ((r >> 1) & 3), so the MFMA A reads (one row per lane, 16 B)
+//     are bank-conflict free;
+//   B (weights, kept in their natural [k][n] layout, 512-byte rows): chunk c of
+//     row k sits at position c ^ (2 * (k & 3)).
+// The weights are n-contiguous while MFMA wants 8 consecutive k per lane; the
+// B fragments are read with ds_read_b64_tr_b16, which transposes 16-bit data
+// across each group of 16 lanes: when lane q + 4j of a group points at
+// B[k0 + j][n0 + 4q .. 4q + 3], lane i of the group receives B[k0 .. k0+3][n0 + i].
+// Two such reads give the 8 k values of one B fragment.
 //
 // Tile order: the hardware hands workgroup i to XCD (i mod 8).  The grid is
 // remapped so each XCD walks a contiguous range of the tile list, and the list
@@ -38,7 +46,7 @@ namespace {
 
 constexpr int BM = kPrefillBM;  // 256 rows
 constexpr int BN = 256;         // LDS B-tile columns
-constexpr int BK = 64;
+constexpr int BK = 32;
 constexpr int NGROUP = 4;       // column tiles per scheduling group
 
 struct Tile {
@@ -90,21 +98,29 @@ __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, Tile
   return false;
 }
 
-// 8x8 transpose of bf16: in[r] = row r (8 columns), out[c] = column c (8 rows).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t r0 = (&in[2 * q].x)[p];
-      const uint32_t r1 = (&in[2 * q + 1].x)[p];
-      lo[q] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);  // (r0.lo, r1.lo)
-      hi[q] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);  // (r0.hi, r1.hi)
-    }
-    out[2 * p] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    out[2 * p + 1] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  }
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+constexpr int STAGES = 4;
+constexpr int A_STAGE = BM * BK * 2;  // 16 KiB
+constexpr int B_STAGE = BK * BN * 2;  // 16 KiB
+
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Written as inline asm so the compiler does not treat the LDS write as an
+// unknown store and wait for every load in flight before each LDS read; the
+// kernel tracks completion itself with s_waitcnt vmcnt.  The instruction has
+// no destination register, so nothing can be overwritten while it is in flight.
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const i16x4_t both[2] = {lo, hi};
+  return *reinterpret_cast<const bf16x8_t*>(both);
 }
 
 template <int MODE>
@@ -113,8 +129,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (A_STAGE + B_STAGE)];
 
   constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
   const int NT = (N + NTW - 1) / NTW;
@@ -123,65 +138,54 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-  // A: thread loads chunk a_c (16 B) of rows a_r0 + 32*i, i = 0..7
-  const int a_c = tid & 7;
-  const int a_r0 = tid >> 3;
-  const uint16_t* a_src[8];
+  // ---- global -> LDS load assignment: wave w issues 4 A blocks and 4 B
+  // blocks (64 chunks of 16 B each) per stage.
+  const uint16_t* a_ptr[4];
+  const uint16_t* b_ptr[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = a_r0 + 32 * i;
+  for (int b = 0; b < 4; ++b) {
+    // A block: 16 rows x 4 chunks; this lane fills position (r, l % 4)
+    const int r = (wave * 4 + b) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 1) & 3);
     const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
     const int p = min(max(tc.row0 + rr, 0), TK - 1);
     const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
-    a_src[i] = A + (int64_t)row * Kdim + a_c * 8;
-  }
-  // B: thread loads the 8x8 block (k rows b_kc*8.., columns of chunk b_nc)
-  const int b_kc = tid & 7;
-  const int b_nc = tid >> 3;
-  const int64_t e_off = (int64_t)tc.e * Kdim * N;
-  int col;
-  const uint16_t* bbase;
-  if (MODE == 1) {
-    col = tc.nt * 128 + (b_nc & 15) * 8;
-    bbase = (b_nc >> 4) ? B3 : B1;
-  } else {
-    col = tc.nt * 256 + b_nc * 8;
-    bbase = B1;
-  }
-  const bool b_ok = col < N;
-  const uint16_t* b_src = bbase + e_off + (int64_t)(b_kc * 8) * N + (b_ok ? col : 0);
-
-  uint4 ra[8], rb[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-    if (b_ok) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        rb[r] = *reinterpret_cast<const uint4*>(b_src + (int64_t)(k0 + r) * N);
+    a_ptr[b] = A + (int64_t)row * Kdim + c * 8;
+    // B block: 2 rows x 32 chunks; this lane fills position (k, l % 32)
+    const int k = (wave * 4 + b) * 2 + (lane >> 5);
+    const int cb = (lane & 31) ^ (2 * (k & 3));
+    int col;
+    const uint16_t* mat;
+    if (MODE == 1) {
+      col = tc.nt * 128 + (cb & 15) * 8;
+      mat = (cb >> 4) ? B3 : B1;
     } else {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) rb[r] = make_uint4(0u, 0u, 0u, 0u);
+      col = tc.nt * 256 + cb * 8;
+      mat = B1;
     }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* as = As[buf];
-    uint16_t* bs = Bs[buf];
+    if (col >= N) col = 0;  // N tail: any valid column; its outputs are never stored
+    b_ptr[b] = mat + (int64_t)tc.e * Kdim * N + (int64_t)k * N + col;
+  }
+  char* a_lds = smem;
+  char* b_lds = smem + STAGES * A_STAGE;
+  const uint32_t a_lds_u = (uint32_t)(uintptr_t)(lds_void*)a_lds;
+  const uint32_t b_lds_u = (uint32_t)(uintptr_t)(lds_void*)b_lds;
+  // Loads k-step `kt_data` into ring slot `kt_slot & (STAGES - 1)`.
+  auto issue_stage = [&](int kt_slot, int kt_data) {
+    const int slot = kt_slot & (STAGES - 1);
+    const int kt = kt_data;
+    const uint32_t as = a_lds_u + slot * A_STAGE + wave * 4096;
+    const uint32_t bs = b_lds_u + slot * B_STAGE + wave * 4096;
+    const int64_t koff_a = (int64_t)kt * BK;
+    const int64_t koff_b = (int64_t)kt * BK * N;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = a_r0 + 32 * i;
-      *reinterpret_cast<uint4*>(as + r * BK + ((a_c ^ (r & 7)) * 8)) = ra[i];
-    }
-    uint4 tcol[8];
-    transpose8x8(rb, tcol);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int nrow = b_nc * 8 + c;
-      *reinterpret_cast<uint4*>(bs + nrow * BK + ((b_kc ^ c) * 8)) = tcol[c];
+    for (int b = 0; b < 4; ++b) {
+      load_lds16(a_ptr[b] + koff_a, as + b * 1024);
+      load_lds16(b_ptr[b] + koff_b, bs + b * 1024);
     }
   };
 
@@ -193,26 +197,45 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int lrow = lane & 31;
-  const int lk = lane >> 5;
-  int brow[4];
+  // ---- fragment read addresses (byte offsets inside a stage)
+  const int m = lane & 31;
+  const int kg = lane >> 5;
+  int a_off[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    brow[j] = (MODE == 1) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + m;
+      a_off[ks][i] = r * 64 + (((ks * 2 + kg) ^ ((m >> 1) & 3)) * 16);
+    }
+  const int g16 = lane >> 4;      // 16-lane group
+  const int h16 = g16 & 1;        // column half of a 32-column MFMA tile
+  const int kg16 = g16 >> 1;      // k half of the MFMA step
+  const int bj = (lane & 15) >> 2;
+  const int qq = lane & 3;
+  int b_off[2][4][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int nb = (MODE == 1) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+        const int k = ks * 16 + kg16 * 8 + 4 * t + bj;
+        const int cc = (nb >> 3) + 2 * h16 + (qq >> 1);
+        b_off[ks][j][t] = k * 512 + ((cc ^ (2 * bj)) * 16) + (qq & 1) * 8;
+      }
 
-  auto compute = [&](int buf) {
-    const uint16_t* as = As[buf];
-    const uint16_t* bs = Bs[buf];
+  auto compute = [&](int slot) {
+    const char* as = a_lds + slot * A_STAGE;
+    const char* bs = b_lds + slot * B_STAGE;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int ch = ((ks * 2 + lk) ^ (lane & 7)) * 8;
+    for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(as + (wm * 128 + i * 32 + lrow) * BK + ch);
+      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + a_off[ks][i]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(bs + (brow[j] + lrow) * BK + ch);
+      for (int j = 0; j < 4; ++j) b[j] = read_b_frag(bs + b_off[ks][j][0], bs + b_off[ks][j][1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -221,18 +244,28 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     }
   };
 
+  // ---- main loop.  Before step kt is consumed each wave waits until only
+  // the 16 loads of steps kt+1, kt+2 remain outstanding, then a barrier makes
+  // every wave's part of step kt visible.  The loads for step kt+3 reuse the
+  // slot of step kt-1, which every wave finished before that barrier.  Steps
+  // past the end reload the last k-slice into a slot nobody reads again, so
+  // the count of outstanding loads is the same on every iteration.
   const int nk = Kdim / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  issue_stage(0, 0);
+  issue_stage(1, min(1, nk - 1));
+  issue_stage(2, min(2, nk - 1));
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    compute(cur);
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16), expcnt/lgkmcnt unconstrained
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue_stage(kt + 3, min(kt + 3, nk - 1));
+    compute(kt & (STAGES - 1));
   }
-
+  // the last (redundant) loads must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  const int lrow = m;
+  const int lk = kg;
   // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (MODE == 1) {
 #pragma unroll

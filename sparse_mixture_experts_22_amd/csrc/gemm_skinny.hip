@@ -24,33 +24,33 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], bf16x8_t (&out)[8]) {
+__device__ __forceinline__ void transpose8x8(const u32x4_t (&in)[8], bf16x8_t (&out)[8]) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     uint32_t lo[4], hi[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t r0 = (&in[2 * q].x)[p];
-      const uint32_t r1 = (&in[2 * q + 1].x)[p];
+      const uint32_t r0 = in[2 * q][p];
+      const uint32_t r1 = in[2 * q + 1][p];
       lo[q] = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
       hi[q] = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
     }
-    uint4 l = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    uint4 h = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    u32x4_t l = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+    u32x4_t h = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
     out[2 * p] = *reinterpret_cast<bf16x8_t*>(&l);
     out[2 * p + 1] = *reinterpret_cast<bf16x8_t*>(&h);
   }
 }
 
-__device__ __forceinline__ void load_block(uint4 (&q)[8], const uint16_t* src, int64_t row_stride,
+__device__ __forceinline__ void load_block(u32x4_t (&q)[8], const uint16_t* src, int64_t row_stride,
                                            bool ok) {
 #pragma unroll
   for (int r = 0; r < 8; ++r)
-    q[r] = ok ? *reinterpret_cast<const uint4*>(src + (int64_t)r * row_stride)
-              : make_uint4(0u, 0u, 0u, 0u);
+    q[r] = ok ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * row_stride)
+              : u32x4_t{0u, 0u, 0u, 0u};
 }
 
-__device__ __forceinline__ void mma_block(const uint4 (&q)[8], const bf16x8_t& a, f32x4_t (&acc)[8]) {
+__device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t& a, f32x4_t (&acc)[8]) {
   bf16x8_t fr[8];
   transpose8x8(q, fr);
 #pragma unroll
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(
     for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // ping-pong: step kc in (qa, aa), step kc+1 in (qb, ab)
-    uint4 qa[8], qb[8];
+    u32x4_t qa[8], qb[8];
     bf16x8_t aa, ab;
     int kc = wk0;
     if (kc < wk1) {

@@ -10,7 +10,10 @@ namespace moe {
 constexpr int kMaxN = 256;  // experts per layer
 constexpr int kMaxK = 8;    // experts kept per token
 
+// Native clang vectors (not HIP's struct vector types): plain loads/stores,
+// so staging arrays of them stay in registers.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
