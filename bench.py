@@ -27,7 +27,7 @@ import time
 METRIC = "MoE-layer tokens/s at Mixtral shape; % bf16 MFMA peak (T=8192), % HBM BW (T=32)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-STAGES = ["router", "dispatch", "up_proj", "down_proj", "combine"]
+STAGES = ["route", "dispatch", "up_proj", "down_proj", "combine"]
 
 
 def parse():
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 1 GiB device-to-device copy (reference for traffic counters)")
     return ap.parse_args()
 
 
@@ -93,20 +95,26 @@ def time_workload(name, steps, warmup):
         w1, w3, w2 = wsets[i % 2]
         moe.forward(x, wg, w1, w3, w2, K, y=y)
     torch.cuda.synchronize()
-    events = [make_events() for _ in range(steps)]
-    torch.cuda.synchronize()
+    # timed region 1: plain calls, two events around the whole loop
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
         w1, w3, w2 = wsets[i % 2]
-        moe.forward_traced(x, wg, w1, w3, w2, K, [e.cuda_event for e in events[i]], y=y)
+        moe.forward(x, wg, w1, w3, w2, K, y=y)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
+    # timed region 2: the same calls with the library recording HIP events on
+    # its stream between stages (per-kernel durations; each event adds a few us)
+    events = [make_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        w1, w3, w2 = wsets[i % 2]
+        moe.forward_traced(x, wg, w1, w3, w2, K, [e.cuda_event for e in events[i]], y=y)
+    torch.cuda.synchronize()
     stage_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(5)] for ev in events])
     rt = moe.route(x, wg, K, outputs=("counts",))
     torch.cuda.synchronize()
@@ -192,6 +200,14 @@ def main():
     import sparse_mixture_experts_22_amd as moe
     moe.lib()  # fails loudly if the HIP library is missing
 
+    if args.calibrate_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     main_r = time_workload(args.workload, args.steps, args.warmup)
     log(f"[bench] {args.workload}: {main_r['ms_per_step']:.3f} ms/step, stages {main_r['stage_ms']}")
     rec = {

@@ -75,6 +75,8 @@ moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const vo
  *   stage_events[0] before the router      [1] after the router
  *   stage_events[2] after the dispatch     [3] after the gate/up projection
  *   stage_events[4] after the down proj.   [5] after the combine
+ * When a batch fits one routing block the router kernel also performs the
+ * dispatch, and [1] is recorded right after it.
  * Same kernels and results as moe_forward; all six events are required.
  */
 moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, const void* W3,

@@ -37,7 +37,8 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 enum class Path { kRouteOnly, kBf16, kF32 };
 
 struct Plan {
-  size_t topk_idx = 0, topk_w = 0, hist = 0, counts = 0, offsets = 0, perm_token = 0, slot_pos = 0;
+  size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
+         perm_token = 0, slot_pos = 0;
   size_t h = 0, o = 0, total = 0;
   bool skinny = false;
   int splits = 1;
@@ -57,6 +58,8 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path) {
   p.topk_idx = take((size_t)TK * 4);
   p.topk_w = take((size_t)TK * 4);
   p.hist = take((size_t)nb * n * 4);
+  p.bases = take((size_t)nb * n * 4);
+  p.wgT = take((size_t)moe::route_padded_experts(n) * d * 2);
   p.counts = take((size_t)n * 4);
   p.offsets = take((size_t)(n + 1) * 4);
   p.perm_token = take((size_t)TK * 4);
@@ -152,14 +155,17 @@ struct RouteOut {
   int32_t* slot_pos;
 };
 
-RouteOut route_buffers(char* ws, const Plan& p, const RouteOut& user) {
-  RouteOut r;
+moe::RouteBuffers route_buffers(char* ws, const Plan& p, const RouteOut& user) {
+  moe::RouteBuffers r;
   r.topk_idx = user.topk_idx ? user.topk_idx : at<int32_t>(ws, p.topk_idx);
   r.topk_w = user.topk_w ? user.topk_w : at<float>(ws, p.topk_w);
   r.counts = user.counts ? user.counts : at<int32_t>(ws, p.counts);
   r.offsets = user.offsets ? user.offsets : at<int32_t>(ws, p.offsets);
   r.perm_token = user.perm_token ? user.perm_token : at<int32_t>(ws, p.perm_token);
   r.slot_pos = user.slot_pos ? user.slot_pos : at<int32_t>(ws, p.slot_pos);
+  r.hist = at<int>(ws, p.hist);
+  r.bases = at<int>(ws, p.bases);
+  r.wgT = at<uint16_t>(ws, p.wgT);
   return r;
 }
 
@@ -181,19 +187,15 @@ moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int
   char* ws = nullptr;
   st = get_workspace(p.total, &ws);
   if (st != MOE_OK) return st;
-  const RouteOut r = route_buffers(ws, p, user);
-  int* hist = at<int>(ws, p.hist);
+  const moe::RouteBuffers r = route_buffers(ws, p, user);
   if (BF16)
-    MOE_LAUNCH(moe::launch_router_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
-                                       T, d, n, K, r.topk_idx, r.topk_w, hist, stream),
-               "router kernel launch");
+    MOE_LAUNCH(moe::launch_route_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
+                                      T, d, n, K, r, stream),
+               "routing kernel launch");
   else
-    MOE_LAUNCH(moe::launch_router_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d,
-                                      n, K, r.topk_idx, r.topk_w, hist, stream),
-               "router kernel launch");
-  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
-                                 r.slot_pos, stream),
-             "scatter kernel launch");
+    MOE_LAUNCH(moe::launch_route_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d, n,
+                                     K, r, stream),
+               "routing kernel launch");
   return MOE_OK;
 }
 
@@ -229,20 +231,16 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   auto mark = [&](int i) -> hipError_t {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream) : hipSuccess;
   };
-  const RouteOut r = route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
-  int* hist = at<int>(ws, p.hist);
+  const moe::RouteBuffers r =
+      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
   uint16_t* h = at<uint16_t>(ws, p.h);
   float* o = at<float>(ws, p.o);
   const auto* xb = static_cast<const uint16_t*>(x);
   const int64_t TK = T * K;
   MOE_LAUNCH(mark(0), "hipEventRecord");
-  MOE_LAUNCH(moe::launch_router_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r.topk_idx,
-                                     r.topk_w, hist, stream),
-             "router kernel launch");
-  MOE_LAUNCH(mark(1), "hipEventRecord");
-  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
-                                 r.slot_pos, stream),
-             "scatter kernel launch");
+  MOE_LAUNCH(moe::launch_route_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r, stream,
+                                    ev ? static_cast<hipEvent_t>(ev[1]) : nullptr),
+             "routing kernel launch");
   MOE_LAUNCH(mark(2), "hipEventRecord");
   const auto* w1 = static_cast<const uint16_t*>(W1);
   const auto* w3 = static_cast<const uint16_t*>(W3);
@@ -301,16 +299,12 @@ moe_status_t moe_forward_f32(const float* x, const float* Wg, const float* W1, c
   char* ws = nullptr;
   st = get_workspace(p.total, &ws);
   if (st != MOE_OK) return st;
-  const RouteOut r = route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
-  int* hist = at<int>(ws, p.hist);
+  const moe::RouteBuffers r =
+      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
   float* h = at<float>(ws, p.h);
   float* o = at<float>(ws, p.o);
   const int64_t TK = T * K;
-  MOE_LAUNCH(moe::launch_router_f32(x, Wg, T, d, n, K, r.topk_idx, r.topk_w, hist, stream),
-             "router kernel launch");
-  MOE_LAUNCH(moe::launch_scatter(r.topk_idx, hist, T, n, K, r.counts, r.offsets, r.perm_token,
-                                 r.slot_pos, stream),
-             "scatter kernel launch");
+  MOE_LAUNCH(moe::launch_route_f32(x, Wg, T, d, n, K, r, stream), "routing kernel launch");
   MOE_LAUNCH(moe::launch_f32_up(x, T, r.perm_token, W1, W3, r.offsets, TK, n, (int)d, (int)f, h, stream),
              "up-projection kernel launch");
   MOE_LAUNCH(moe::launch_f32_down(h, W2, r.offsets, TK, n, (int)f, (int)d, o, stream),

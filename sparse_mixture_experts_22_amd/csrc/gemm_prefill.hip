@@ -15,18 +15,20 @@
 // 256-column fp32 accumulator tile (for MODE 1: 128 W1 columns + the same 128
 // W3 columns) with v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 (16 MFMA
 // tiles, 256 accumulator registers).  K advances in steps of 32 through a ring
-// of 4 LDS stages (32 KiB each): global loads for step k+3 are in flight while
-// step k is multiplied.
+// of 5 LDS stages (32 KiB each, all 160 KiB of the CU's LDS): global loads for
+// steps k+1 .. k+4 are in flight while step k is multiplied.
 //
 // Data movement is HBM/L2 -> LDS directly (global_load_lds, 16 bytes per lane,
 // lane l writing bytes 16*l.. of a 1 KiB block), with no register staging and
 // no LDS store instructions.  Which global 16-byte chunk a lane fetches is
-// permuted so the LDS image is XOR-swizzled:
+// permuted so the LDS image is XOR-swizzled for gfx950's 64 banks (256 bytes
+// per cycle):
 //   A (activations, [row][k], 64-byte rows): chunk c of row r sits at
-//     position c ^ ((r >> 1) & 3), so the MFMA A reads (one row per lane, 16 B)
-//     are bank-conflict free;
+//     position c ^ ((r >> 2) & 3), so the 16 lanes of an MFMA A read served
+//     together (16 rows, same logical chunk) hit 16 distinct 16-byte slots;
 //   B (weights, kept in their natural [k][n] layout, 512-byte rows): chunk c of
-//     row k sits at position c ^ (2 * (k & 3)).
+//     row k sits at position c ^ (4 * (k & 3)), so the 32 lanes of a transpose
+//     read served together (4 rows x 2 column halves) hit distinct 32-byte slots.
 // The weights are n-contiguous while MFMA wants 8 consecutive k per lane; the
 // B fragments are read with ds_read_b64_tr_b16, which transposes 16-bit data
 // across each group of 16 lanes: when lane q + 4j of a group points at
@@ -50,7 +52,7 @@ constexpr int BK = 32;
 constexpr int NGROUP = 4;       // column tiles per scheduling group
 
 struct Tile {
-  int e, nt, row0, rows;
+  int e, m, nt, row0, rows;
 };
 
 // Maps this workgroup to a tile, or returns false if it has none.  All threads
@@ -87,6 +89,7 @@ __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, Tile
         nt = ng * NGROUP + rem % gt;
       }
       tc.e = e;
+      tc.m = m;
       tc.nt = nt;
       tc.row0 = offsets[e] + m * BM;
       const int left = offsets[e + 1] - tc.row0;
@@ -102,17 +105,59 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-constexpr int STAGES = 4;
+// LDS rings: SA stages of the A tile and SB stages of the B tile (16 KiB
+// each; SA + SB = 10 fills the CU's 160 KiB).  Waves 0-1 load only B, waves
+// 2-3 only A: a wave's vmcnt retires in issue order, so giving each operand
+// its own waves lets the weight stream (read once from HBM, the long-latency
+// operand) run SB-1 steps ahead while the activations run SA-1 steps ahead.
+#ifndef MOE_RING_A
+#define MOE_RING_A 4
+#endif
+#ifndef MOE_RING_B
+#define MOE_RING_B 6
+#endif
+// Weight prefetch distance in k-steps beyond the B ring (0 = off).
+#ifndef MOE_B_PREFETCH
+#define MOE_B_PREFETCH 0
+#endif
+constexpr int SA = MOE_RING_A;
+constexpr int SB = MOE_RING_B;
+constexpr int BPF = MOE_B_PREFETCH;
+static_assert(SA >= 2 && SB >= 2 && SA + SB + (BPF > 0 ? 1 : 0) <= 10,
+              "LDS budget is 10 stages of 16 KiB (one is scratch for the prefetch)");
+// loads each wave issues per stage of its operand (8 blocks of 1 KiB)
+constexpr int LOADS_PER_STAGE = 8;
+// s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
+}
+// inside the loop, step kt+1 of the wave's operand must have landed while the
+// S-2 later steps may still be in flight; LDS reads must have returned
+constexpr int WAIT_AHEAD_A = waitcnt_imm(LOADS_PER_STAGE * (SA - 2), 0);
+// B loaders follow every stage's 8 loads (prologue included) with exactly one
+// prefetch, so after the loads of a stage come its prefetch and the
+// (loads + prefetch) of each later stage.
+constexpr int B_LOADS_PER_STEP = LOADS_PER_STAGE + (BPF > 0 ? 1 : 0);
+constexpr int B_TRAIL = BPF > 0 ? 1 : 0;
+constexpr int WAIT_AHEAD_B = waitcnt_imm(B_LOADS_PER_STEP * (SB - 2) + B_TRAIL, 0);
+// before the loop all S steps are in flight and step 0 must have landed
+constexpr int WAIT_FIRST_A = waitcnt_imm(LOADS_PER_STAGE * (SA - 1), 15);
+constexpr int WAIT_FIRST_B = waitcnt_imm(B_LOADS_PER_STEP * (SB - 1) + B_TRAIL, 15);
+constexpr int WAITCNT_ALL = waitcnt_imm(0, 15);
+static_assert(B_LOADS_PER_STEP * (SB - 1) + B_TRAIL < 64 && LOADS_PER_STAGE * (SA - 1) < 64,
+              "vmcnt is a 6-bit counter");
+
 constexpr int A_STAGE = BM * BK * 2;  // 16 KiB
 constexpr int B_STAGE = BK * BN * 2;  // 16 KiB
 
-// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
-// Written as inline asm so the compiler does not treat the LDS write as an
-// unknown store and wait for every load in flight before each LDS read; the
-// kernel tracks completion itself with s_waitcnt vmcnt.  The instruction has
-// no destination register, so nothing can be overwritten while it is in flight.
 __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
+}
+
+// 4 bytes per lane into LDS: used only to pull weight lines into L2 early
+// (the LDS destination is a scratch area nobody reads).
+__device__ __forceinline__ void prefetch_lds4(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
 }
 
 __device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) {
@@ -129,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * (A_STAGE + B_STAGE)];
+  __shared__ __attribute__((aligned(1024))) char smem[SA * A_STAGE + SB * B_STAGE + (BPF > 0 ? 1024 : 0)];
 
   constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
   const int NT = (N + NTW - 1) / NTW;
@@ -142,51 +187,79 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-  // ---- global -> LDS load assignment: wave w issues 4 A blocks and 4 B
-  // blocks (64 chunks of 16 B each) per stage.
-  const uint16_t* a_ptr[4];
-  const uint16_t* b_ptr[4];
+  // ---- global -> LDS load assignment.  Waves 0-1 (B loaders) each fill 8
+  // of the 16 B blocks of a stage (2 rows x 32 chunks each); waves 2-3 (A
+  // loaders) each fill 8 of the 16 A blocks (16 rows x 4 chunks each).
+  const bool b_loader = wave < 2;
+  const int lw = wave & 1;  // index among the loaders of the operand
+  const uint16_t* ld_ptr[8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    // A block: 16 rows x 4 chunks; this lane fills position (r, l % 4)
-    const int r = (wave * 4 + b) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 1) & 3);
-    const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
-    const int p = min(max(tc.row0 + rr, 0), TK - 1);
-    const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
-    a_ptr[b] = A + (int64_t)row * Kdim + c * 8;
-    // B block: 2 rows x 32 chunks; this lane fills position (k, l % 32)
-    const int k = (wave * 4 + b) * 2 + (lane >> 5);
-    const int cb = (lane & 31) ^ (2 * (k & 3));
+  for (int b = 0; b < 8; ++b) {
+    const int blk = lw * 8 + b;
+    if (!b_loader) {
+      const int r = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
+      const int p = min(max(tc.row0 + rr, 0), TK - 1);
+      const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
+      ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
+    } else {
+      const int k = blk * 2 + (lane >> 5);
+      const int cb = (lane & 31) ^ (4 * (k & 3));
+      int col;
+      const uint16_t* mat;
+      if (MODE == 1) {
+        col = tc.nt * 128 + (cb & 15) * 8;
+        mat = (cb >> 4) ? B3 : B1;
+      } else {
+        col = tc.nt * 256 + cb * 8;
+        mat = B1;
+      }
+      if (col >= N) col = 0;  // N tail: any valid column; its outputs are never stored
+      ld_ptr[b] = mat + (int64_t)tc.e * Kdim * N + (int64_t)k * N + col;
+    }
+  }
+  char* a_lds = smem;
+  char* b_lds = smem + SA * A_STAGE;
+  const uint32_t ld_base = (uint32_t)(uintptr_t)(lds_void*)(b_loader ? b_lds : a_lds) + lw * 8192;
+  const int ld_stage_bytes = b_loader ? B_STAGE : A_STAGE;
+  const int ld_ring = b_loader ? SB : SA;
+  const int64_t ld_kstep = b_loader ? (int64_t)BK * N : (int64_t)BK;  // elements per k-step
+  // This wave's loads of k-step `kt_data` into slot `kt_slot % ring`.
+  auto issue_stage = [&](int kt_slot, int kt_data) {
+    const uint32_t dst = ld_base + (kt_slot % ld_ring) * ld_stage_bytes;
+    const int64_t koff = (int64_t)kt_data * ld_kstep;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
+  };
+  // Weight prefetch: the tiles an XCD runs together share each weight k-slice
+  // (32 rows x 512 bytes = 128 cache lines); tile m of the group touches 16
+  // of those lines (rows 4*(m%8) .. +3, all 4 lines of each row) BPF steps
+  // ahead of the B ring, so the ring's own loads of that slice hit in L2.
+  // Both B loader waves issue the instruction (lanes 16..63 repeat lanes
+  // 0..15); the second copy is an L2 hit and keeps the two waves' load
+  // counts identical.
+  const uint16_t* pf_ptr = nullptr;
+  uint32_t pf_lds = 0;
+  if (BPF > 0 && b_loader) {
+    const int q = lane & 15;
+    const int row = 4 * (tc.m & 7) + (q >> 2);
+    const int line = q & 3;
     int col;
     const uint16_t* mat;
     if (MODE == 1) {
-      col = tc.nt * 128 + (cb & 15) * 8;
-      mat = (cb >> 4) ? B3 : B1;
+      col = tc.nt * 128 + (line & 1) * 64;
+      mat = (line >> 1) ? B3 : B1;
     } else {
-      col = tc.nt * 256 + cb * 8;
+      col = tc.nt * 256 + line * 64;
       mat = B1;
     }
-    if (col >= N) col = 0;  // N tail: any valid column; its outputs are never stored
-    b_ptr[b] = mat + (int64_t)tc.e * Kdim * N + (int64_t)k * N + col;
+    if (col >= N) col = 0;
+    pf_ptr = mat + (int64_t)tc.e * Kdim * N + (int64_t)row * N + col;
+    pf_lds = (uint32_t)(uintptr_t)(lds_void*)(smem + SA * A_STAGE + SB * B_STAGE) + lw * 256;
   }
-  char* a_lds = smem;
-  char* b_lds = smem + STAGES * A_STAGE;
-  const uint32_t a_lds_u = (uint32_t)(uintptr_t)(lds_void*)a_lds;
-  const uint32_t b_lds_u = (uint32_t)(uintptr_t)(lds_void*)b_lds;
-  // Loads k-step `kt_data` into ring slot `kt_slot & (STAGES - 1)`.
-  auto issue_stage = [&](int kt_slot, int kt_data) {
-    const int slot = kt_slot & (STAGES - 1);
-    const int kt = kt_data;
-    const uint32_t as = a_lds_u + slot * A_STAGE + wave * 4096;
-    const uint32_t bs = b_lds_u + slot * B_STAGE + wave * 4096;
-    const int64_t koff_a = (int64_t)kt * BK;
-    const int64_t koff_b = (int64_t)kt * BK * N;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      load_lds16(a_ptr[b] + koff_a, as + b * 1024);
-      load_lds16(b_ptr[b] + koff_b, bs + b * 1024);
-    }
+  auto issue_prefetch = [&](int kt_data) {
+    if (BPF > 0 && b_loader) prefetch_lds4(pf_ptr + (int64_t)kt_data * BK * N, pf_lds);
   };
 
   f32x16_t acc[4][4];
@@ -206,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + m;
-      a_off[ks][i] = r * 64 + (((ks * 2 + kg) ^ ((m >> 1) & 3)) * 16);
+      a_off[ks][i] = r * 64 + (((ks * 2 + kg) ^ ((m >> 2) & 3)) * 16);
     }
   const int g16 = lane >> 4;      // 16-lane group
   const int h16 = g16 & 1;        // column half of a 32-column MFMA tile
@@ -223,47 +296,83 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
         const int nb = (MODE == 1) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
         const int k = ks * 16 + kg16 * 8 + 4 * t + bj;
         const int cc = (nb >> 3) + 2 * h16 + (qq >> 1);
-        b_off[ks][j][t] = k * 512 + ((cc ^ (2 * bj)) * 16) + (qq & 1) * 8;
+        b_off[ks][j][t] = k * 512 + ((cc ^ (4 * bj)) * 16) + (qq & 1) * 8;
       }
 
-  auto compute = [&](int slot) {
-    const char* as = a_lds + slot * A_STAGE;
-    const char* bs = b_lds + slot * B_STAGE;
+  auto read_frags = [&](int kt, int ks, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
+    const char* as = a_lds + (kt % SA) * A_STAGE;
+    const char* bs = b_lds + (kt % SB) * B_STAGE;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a[4], b[4];
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + a_off[ks][i]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + a_off[ks][i]);
+    for (int j = 0; j < 4; ++j) b[j] = read_b_frag(bs + b_off[ks][j][0], bs + b_off[ks][j][1]);
+  };
+  auto mfma_step = [&](const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = read_b_frag(bs + b_off[ks][j][0], bs + b_off[ks][j][1]);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  };
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Scheduling pattern of a half step: the 12 fragment reads (4 A + 8
+  // transposed B) each followed by one MFMA, then the remaining 4 MFMAs.
+  auto interleave = [] {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
-  // ---- main loop.  Before step kt is consumed each wave waits until only
-  // the 16 loads of steps kt+1, kt+2 remain outstanding, then a barrier makes
-  // every wave's part of step kt visible.  The loads for step kt+3 reuse the
-  // slot of step kt-1, which every wave finished before that barrier.  Steps
-  // past the end reload the last k-slice into a slot nobody reads again, so
-  // the count of outstanding loads is the same on every iteration.
+  // ---- main loop.  A k-step has two MFMA sub-steps (k = 0..15, 16..31).
+  // The barrier that publishes step kt+1 sits between them: before it, each
+  // wave has its sub-step-1 fragments of step kt in registers (lgkmcnt(0))
+  // and waits until its own loads of step kt+1 have landed (vmcnt); after it,
+  // step kt's slots are free and each loader wave refills its operand's slot
+  // with the step S ahead, while the sub-step-0 fragments of step kt+1 are
+  // read (issued first, ahead of the loads) during the sub-step-1 MFMAs of
+  // step kt.  Steps past the end reload the last k-slice into slots nobody
+  // reads again, so the count of outstanding loads never changes.
   const int nk = Kdim / BK;
-  issue_stage(0, 0);
-  issue_stage(1, min(1, nk - 1));
-  issue_stage(2, min(2, nk - 1));
+  const int ring = ld_ring;
+  for (int st = 0; st < ring; ++st) {
+    issue_stage(st, min(st, nk - 1));
+    issue_prefetch(min(st + BPF, nk - 1));
+  }
+  if (b_loader)
+    __builtin_amdgcn_s_waitcnt(WAIT_FIRST_B);  // step 0 landed
+  else
+    __builtin_amdgcn_s_waitcnt(WAIT_FIRST_A);
+  fence();
+  __builtin_amdgcn_s_barrier();
+  fence();
+  bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
+  read_frags(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16), expcnt/lgkmcnt unconstrained
-    asm volatile("" ::: "memory");
+    read_frags(kt, 1, fa1, fb1);
+    mfma_step(fa0, fb0);
+    interleave();
+    if (b_loader)
+      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_B);  // lgkmcnt(0) and step kt+1 landed
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_A);
+    fence();
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    issue_stage(kt + 3, min(kt + 3, nk - 1));
-    compute(kt & (STAGES - 1));
+    fence();
+    read_frags(kt + 1, 0, fa0, fb0);
+    issue_stage(kt + ring, min(kt + ring, nk - 1));
+    issue_prefetch(min(kt + ring + BPF, nk - 1));  // B loaders only
+    mfma_step(fa1, fb1);
+    interleave();
   }
   // the last (redundant) loads must land before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
+
   const int lrow = m;
   const int lk = kg;
   // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.

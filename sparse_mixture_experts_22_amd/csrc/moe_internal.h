@@ -17,8 +17,24 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Tokens per routing block: the router and the scatter agree on it.
-inline int route_block_tokens(int n) { return n <= 128 ? 128 : 64; }
+// Tokens per routing block (the router, scan and scatter agree on it; <= 32).
+int route_block_tokens(int n);
+// Experts rounded up to a multiple of 16 (rows of the transposed router).
+int route_padded_experts(int n);
+
+// Device buffers of the routing stage (all in the library workspace except
+// where a caller of moe_route supplies its own outputs).
+struct RouteBuffers {
+  int* topk_idx;    // [T][K]
+  float* topk_w;    // [T][K]
+  int* hist;        // [nb][n] per-block expert histograms
+  int* bases;       // [nb][n] per-block first positions
+  int* counts;      // [n]
+  int* offsets;     // [n+1]
+  int* perm_token;  // [T*K]
+  int* slot_pos;    // [T][K]
+  uint16_t* wgT;    // [n_pad][d] transposed router (bf16 path)
+};
 
 // Rows of an expert handled by one prefill tile.
 constexpr int kPrefillBM = 256;
@@ -30,12 +46,15 @@ constexpr int kSkinnyMaxAvgRows = 24;
 constexpr int kSkinnyDownSplits = 4;
 
 // ---------------------------------------------------------------- routing
-hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
-                              int K, int* topk_idx, float* topk_w, int* hist, hipStream_t s);
-hipError_t launch_router_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
-                             int* topk_idx, float* topk_w, int* hist, hipStream_t s);
-hipError_t launch_scatter(const int* topk_idx, const int* hist, int64_t T, int n, int K,
-                          int* counts, int* offsets, int* perm_token, int* slot_pos, hipStream_t s);
+// Router + top-K + softmax + dispatch; fills every RouteBuffers output.
+// `after_router` (optional) is recorded between the router and the dispatch.
+hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                             int K, const RouteBuffers& rb, hipStream_t s,
+                             hipEvent_t after_router = nullptr);
+hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
+                            const RouteBuffers& rb, hipStream_t s);
+// Scan + scatter from topk_idx and hist (used after a multi-block router).
+hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s);
 
 // ------------------------------------------------------ expert projections
 // Gate/up: h[p][:] = SiLU(x[perm_token[p]] W1_e) * (x[perm_token[p]] W3_e), bf16 out.

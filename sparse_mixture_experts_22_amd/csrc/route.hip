@@ -8,29 +8,36 @@
 // model activates only part of its parameters": experts with a zero gate are
 // never evaluated, so each expert's rows are gathered into one contiguous group.
 //
-// Kernels:
-//   router_bf16_kernel  logits on bf16 MFMA (16x16x32), fp32 accumulation,
-//                       then top-K + softmax + per-block expert histogram.
-//   router_f32_kernel   same epilogue, fp32 FMA dot products.
-//   scatter_kernel      per-block bases from the histograms, ranks within the
-//                       block, writes counts/offsets/perm_token/slot_pos.
-// Everything is integer or fixed-order fp32: results are bit-reproducible.
+// Kernels (bf16 path):
+//   wg_transpose_kernel  W_g [d][n] -> WgT [n_pad][d] (zero rows past n), so an
+//                        MFMA B fragment (8 consecutive k of one expert) is one
+//                        16-byte load.
+//   router_bf16_kernel   a workgroup owns BT tokens; its W waves split the d
+//                        reduction, each accumulating logits with
+//                        v_mfma_f32_16x16x32_bf16 from x and WgT read straight
+//                        from global memory; the W partial tiles are summed in
+//                        LDS in wave order, then top-K + softmax + the block's
+//                        expert histogram.  With a single routing block the
+//                        same kernel also performs the scan and the scatter.
+//   scan_kernel          one workgroup: per-block bases (offsets[e] plus the
+//                        assignments to e in earlier blocks), counts, offsets.
+//   scatter_kernel       per block: rank of each assignment among the block's
+//                        tokens that chose the same expert (LDS bitmask +
+//                        popcount), position = base + rank.
+// fp32 path: router_f32_kernel (fp32 FMA dot products) feeds the same scan and
+// scatter.  Everything is integer or fixed-order fp32: bit-reproducible.
 #include "moe_internal.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Top-K + softmax + histogram for the tokens of one block; logits_s[i*ld + e].
-// Thread i handles token t0 + i.  Ties keep the lower expert index first
-// (a later expert only displaces a strictly smaller score); an empty slot takes
-// any score, so every slot ends up holding a valid expert even for NaN input.
-__device__ void topk_softmax_epilogue(const float* logits_s, int ld, int BT, int64_t t0,
-                                      int64_t T, int n, int K, int* __restrict__ topk_idx,
-                                      float* __restrict__ topk_w, int* hist_s) {
-  const int i = threadIdx.x;
-  if (i >= BT || t0 + i >= T) return;
+// Top-K + softmax for token i of a block from logits_s[i*ld + e]; ties keep the
+// lower expert index first (a later expert only displaces a strictly smaller
+// score); an empty slot takes any score, so every slot ends up holding a valid
+// expert even for NaN input.  Returns the kept experts in id[].
+__device__ void topk_softmax(const float* logits_s, int ld, int i, int n, int K, int (&id)[kMaxK],
+                             float (&w)[kMaxK]) {
   float v[kMaxK];
-  int id[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     v[j] = -INFINITY;
@@ -52,48 +59,121 @@ __device__ void topk_softmax_epilogue(const float* logits_s, int ld, int BT, int
       }
     }
   }
-  float z[kMaxK];
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < K) {
-      z[j] = expf(v[j] - v[0]);
-      sum += z[j];
+      w[j] = expf(v[j] - v[0]);
+      sum += w[j];
     }
   }
-  const int64_t t = t0 + i;
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (j < K) {
-      topk_idx[t * K + j] = id[j];
-      topk_w[t * K + j] = z[j] / sum;
-      atomicAdd(&hist_s[id[j]], 1);  // integer: order-independent
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < K) w[j] = w[j] / sum;
+}
+
+// Shared epilogue of both routers: top-K for the block's tokens, then either
+// the block histogram (multi-block) or the whole dispatch (single block).
+// sel_s: [BT*K] ints, mask_s: [n] uint32 (BT <= 32), hist_s: [n] ints.
+__device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0, int64_t T, int n,
+                               int K, int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                               int* __restrict__ hist, bool fused, int* __restrict__ counts,
+                               int* __restrict__ offsets, int* __restrict__ perm_token,
+                               int* __restrict__ slot_pos, int* sel_s, uint32_t* mask_s,
+                               int* hist_s) {
+  const int tid = threadIdx.x;
+  const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
+  for (int e = tid; e < n; e += blockDim.x) {
+    hist_s[e] = 0;
+    mask_s[e] = 0u;
+  }
+  __syncthreads();
+  if (tid < cnt) {
+    int id[kMaxK];
+    float w[kMaxK];
+    topk_softmax(logits_s, ld, tid, n, K, id, w);
+    const int64_t t = t0 + tid;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < K) {
+        topk_idx[t * K + j] = id[j];
+        topk_w[t * K + j] = w[j];
+        sel_s[tid * K + j] = id[j];
+        atomicAdd(&hist_s[id[j]], 1);          // integer: order-independent
+        atomicOr(&mask_s[id[j]], 1u << tid);   // token tid chose expert id[j]
+      }
+    }
+  }
+  __syncthreads();
+  if (!fused) {
+    for (int e = tid; e < n; e += blockDim.x) hist[(int64_t)blockIdx.x * n + e] = hist_s[e];
+    return;
+  }
+  // single routing block: offsets = exclusive scan of the block histogram
+  __shared__ int base_s[kMaxN + 1];
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < n; ++e) {
+      base_s[e] = run;
+      run += hist_s[e];
+    }
+    base_s[n] = run;
+  }
+  __syncthreads();
+  for (int e = tid; e <= n; e += blockDim.x) {
+    offsets[e] = base_s[e];
+    if (e < n) counts[e] = hist_s[e];
+  }
+  if (tid < cnt) {
+    for (int j = 0; j < K; ++j) {
+      const int e = sel_s[tid * K + j];
+      const int pos = base_s[e] + __popc(mask_s[e] & ((1u << tid) - 1u));
+      perm_token[pos] = (int)(t0 + tid);
+      slot_pos[(t0 + tid) * K + j] = pos;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 router.  A workgroup (4 waves) owns BT = 64*TT tokens; wave w owns TT
-// tiles of 16 tokens.  W_g is staged through LDS transposed to [expert][k] in
-// chunks of 64 rows so MFMA B fragments are single 16-byte LDS reads.  The K
-// index inside an MFMA step is permuted (lane group g covers k = g*16 + s*8 ..
-// of the 64-chunk in step s) identically for both operands, which leaves the
-// dot products unchanged and makes each lane read 32 contiguous bytes of x.
-template <int NE, int TT>
-__global__ __launch_bounds__(256) void router_bf16_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ Wg,
-                                                          int64_t T, int d, int n, int K,
-                                                          int* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w,
-                                                          int* __restrict__ hist) {
-  constexpr int BT = 64 * TT;
-  constexpr int NP = NE * 16;
-  constexpr int DK = 64;
-  constexpr int LDW = DK + 8;  // padded row: consecutive experts shift by 16 B
+// W_g [d][n] -> WgT [NP][d], rows n..NP-1 zero.  64 (k) x 64 (e) tiles via LDS.
+__global__ __launch_bounds__(256) void wg_transpose_kernel(const uint16_t* __restrict__ Wg, int d,
+                                                           int n, int NP,
+                                                           uint16_t* __restrict__ WgT) {
+  __shared__ uint16_t tile[64][65];
+  const int k0 = blockIdx.x * 64;
+  const int e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int kk = idx / 64, ee = idx % 64;
+    const int k = k0 + kk, e = e0 + ee;
+    tile[kk][ee] = (k < d && e < n) ? Wg[(int64_t)k * n + e] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int ee = idx / 64, kk = idx % 64;
+    const int k = k0 + kk, e = e0 + ee;
+    if (k < d && e < NP) WgT[(int64_t)e * d + k] = tile[kk][ee];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 router.  NE expert tiles of 16, TT token tiles of 16 (BT = 16*TT), W
+// waves splitting the reduction over d in steps of 32.  Lane (r = l%16,
+// g = l/16) supplies A = x[token r][k + 8g ..] and B = WgT[expert r][k + 8g ..].
+template <int NE, int TT, int W>
+__global__ __launch_bounds__(W * 64) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
+    int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
+    int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm_token,
+    int* __restrict__ slot_pos) {
+  constexpr int BT = 16 * TT;
+  constexpr int NP = 16 * NE;
   constexpr int LDL = NP + 1;
-  __shared__ __attribute__((aligned(16))) uint16_t wgT[NP * LDW];
+  __shared__ float part_s[W * BT * NP];
   __shared__ float logits_s[BT * LDL];
-  __shared__ int hist_s[NP];
+  __shared__ int sel_s[32 * kMaxK];
+  __shared__ uint32_t mask_s[kMaxN];
+  __shared__ int hist_s[kMaxN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -102,76 +182,76 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(const uint16_t* __rest
   const int g = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
 
-  for (int e = tid; e < NP; e += 256) hist_s[e] = 0;
-
-  const uint16_t* xrow[TT];
+  const uint16_t* ap[TT];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) {
-    int64_t tok = t0 + wave * 16 * TT + tt * 16 + r;
+    int64_t tok = t0 + tt * 16 + r;
     if (tok >= T) tok = T - 1;  // rows past the end are computed, never stored
-    xrow[tt] = x + tok * (int64_t)d;
+    ap[tt] = x + tok * (int64_t)d + g * 8;
   }
+  const uint16_t* bp[NE];
+#pragma unroll
+  for (int et = 0; et < NE; ++et) bp[et] = WgT + (int64_t)(et * 16 + r) * d + g * 8;
+
   f32x4_t acc[TT][NE];
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int et = 0; et < NE; ++et) acc[tt][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const bool vec_ok = (n % 8) == 0;
-  for (int k0 = 0; k0 < d; k0 += DK) {
-    __syncthreads();  // previous chunk consumed
-    constexpr int NC = NP / 8;
-    for (int idx = tid; idx < DK * NC; idx += 256) {
-      const int kk = idx / NC;
-      const int e0 = (idx % NC) * 8;
-      uint16_t v[8];
-      const uint16_t* src = Wg + (int64_t)(k0 + kk) * n + e0;
-      if (vec_ok && e0 < n) {
-        const uint4 q = *reinterpret_cast<const uint4*>(src);
-        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+  const int nkc = d / 32;
+  const int kc0 = wave * nkc / W;
+  const int kc1 = (wave + 1) * nkc / W;
+  constexpr int U = 4;  // k-steps whose loads are issued together
+  int kc = kc0;
+  for (; kc + U <= kc1; kc += U) {
+    bf16x8_t a[U][TT], b[U][NE];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = (uint16_t)(w4[j] & 0xFFFFu);
-          v[2 * j + 1] = (uint16_t)(w4[j] >> 16);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = (e0 + j < n) ? src[j] : (uint16_t)0;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wgT[(e0 + j) * LDW + kk] = v[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kk = g * 16 + s * 8;
-      bf16x8_t a[TT];
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
-        a[tt] = *reinterpret_cast<const bf16x8_t*>(xrow[tt] + k0 + kk);
+        a[u][tt] = *reinterpret_cast<const bf16x8_t*>(ap[tt] + (kc + u) * 32);
 #pragma unroll
-      for (int et = 0; et < NE; ++et) {
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&wgT[(et * 16 + r) * LDW + kk]);
+      for (int et = 0; et < NE; ++et)
+        b[u][et] = *reinterpret_cast<const bf16x8_t*>(bp[et] + (kc + u) * 32);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int et = 0; et < NE; ++et)
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt)
-          acc[tt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tt], b, acc[tt][et], 0, 0, 0);
+          acc[tt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][tt], b[u][et], acc[tt][et], 0, 0, 0);
+  }
+  for (; kc < kc1; ++kc) {
+#pragma unroll
+    for (int et = 0; et < NE; ++et) {
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(bp[et] + kc * 32);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ap[tt] + kc * 32);
+        acc[tt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[tt][et], 0, 0, 0);
       }
     }
   }
-  // D layout of 16x16 MFMA: lane holds rows 4*g + j, column r.
+  // D layout of the 16x16 MFMA: lane holds rows (tokens) 4g + j, column (expert) r.
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
     for (int et = 0; et < NE; ++et)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tl = wave * 16 * TT + tt * 16 + 4 * g + j;
-        logits_s[tl * LDL + et * 16 + r] = acc[tt][et][j];
-      }
+      for (int j = 0; j < 4; ++j)
+        part_s[(wave * BT + tt * 16 + 4 * g + j) * NP + et * 16 + r] = acc[tt][et][j];
   __syncthreads();
-  topk_softmax_epilogue(logits_s, LDL, BT, t0, T, n, K, topk_idx, topk_w, hist_s);
+  for (int idx = tid; idx < BT * NP; idx += W * 64) {
+    float s = part_s[idx];
+#pragma unroll
+    for (int w2 = 1; w2 < W; ++w2) s += part_s[w2 * BT * NP + idx];  // fixed wave order
+    logits_s[(idx / NP) * LDL + (idx % NP)] = s;
+  }
   __syncthreads();
-  for (int e = tid; e < n; e += 256) hist[(int64_t)blockIdx.x * n + e] = hist_s[e];
+  route_epilogue(logits_s, LDL, BT, t0, T, n, K, topk_idx, topk_w, hist, fused != 0, counts, offsets,
+                 perm_token, slot_pos, sel_s, mask_s, hist_s);
 }
 
 // ---------------------------------------------------------------------------
@@ -182,12 +262,13 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
                                                          int* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
                                                          int* __restrict__ hist) {
-  __shared__ float logits_s[128 * 129];  // BT*(n+1) <= 128*129 for both block sizes
+  __shared__ float logits_s[32 * (kMaxN + 1)];
+  __shared__ int sel_s[32 * kMaxK];
+  __shared__ uint32_t mask_s[kMaxN];
   __shared__ int hist_s[kMaxN];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * BT;
   const int ld = n + 1;
-  for (int e = tid; e < n; e += 256) hist_s[e] = 0;
   for (int idx = tid; idx < BT * n; idx += 256) {
     const int i = idx / n;
     const int e = idx % n;
@@ -199,117 +280,163 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
     logits_s[i * ld + e] = s;
   }
   __syncthreads();
-  topk_softmax_epilogue(logits_s, ld, BT, t0, T, n, K, topk_idx, topk_w, hist_s);
-  __syncthreads();
-  for (int e = tid; e < n; e += 256) hist[(int64_t)blockIdx.x * n + e] = hist_s[e];
+  route_epilogue(logits_s, ld, BT, t0, T, n, K, topk_idx, topk_w, hist, false, nullptr, nullptr,
+                 nullptr, nullptr, sel_s, mask_s, hist_s);
 }
 
 // ---------------------------------------------------------------------------
-// Scatter: block b places its assignments.  The base of expert e for block b
-// is offsets[e] + (assignments to e in blocks before b); the rank of token i's
-// assignment to e inside the block counts earlier tokens of the block that
-// also chose e.  Positions are therefore expert-contiguous and ascending in
-// token index within an expert (a stable counting sort).
-__global__ __launch_bounds__(256) void scatter_kernel(const int* __restrict__ topk_idx,
-                                                      const int* __restrict__ hist, int64_t T,
-                                                      int n, int K, int BT, int nb,
-                                                      int* __restrict__ counts,
-                                                      int* __restrict__ offsets,
-                                                      int* __restrict__ perm_token,
-                                                      int* __restrict__ slot_pos) {
-  __shared__ int tot[kMaxN];
-  __shared__ int pre[kMaxN];
-  __shared__ int base[kMaxN + 1];
-  __shared__ int sel_s[128 * kMaxK];
+// Scan over the block histograms hist[nb][n] (one workgroup of 1024 threads).
+// Thread (e, p) owns a contiguous range of blocks for expert e.  Writes
+// bases[b][e] = offsets[e] + sum_{b' < b} hist[b'][e], counts and offsets.
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist, int nb, int n,
+                                                    int* __restrict__ bases,
+                                                    int* __restrict__ counts,
+                                                    int* __restrict__ offsets) {
+  __shared__ int psum[1024];
+  __shared__ int tot_s[kMaxN];
+  __shared__ int off_s[kMaxN + 1];
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
-  for (int e = tid; e < n; e += 256) {
-    tot[e] = 0;
-    pre[e] = 0;
-  }
+  int np2 = 1;
+  while (np2 < n) np2 <<= 1;
+  const int P = 1024 / np2;  // threads per expert
+  const int e = tid % np2;
+  const int p = tid / np2;
+  const int b0 = (int)((int64_t)p * nb / P);
+  const int b1 = (int)((int64_t)(p + 1) * nb / P);
+  int s = 0;
+  if (e < n)
+    for (int b = b0; b < b1; ++b) s += hist[(int64_t)b * n + e];
+  psum[tid] = s;
   __syncthreads();
-  const int64_t nh = (int64_t)nb * n;
-  for (int64_t idx = tid; idx < nh; idx += 256) {
-    const int bb = (int)(idx / n);
-    const int e = (int)(idx % n);
-    const int h = hist[idx];
-    atomicAdd(&tot[e], h);
-    if (bb < b) atomicAdd(&pre[e], h);
+  if (tid < n) {
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = psum[q * np2 + tid];
+      psum[q * np2 + tid] = run;  // exclusive prefix over the chunks of expert tid
+      run += v;
+    }
+    tot_s[tid] = run;
   }
-  const int64_t t0 = (int64_t)b * BT;
-  const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
-  for (int idx = tid; idx < cnt * K; idx += 256) sel_s[idx] = topk_idx[t0 * K + idx];
   __syncthreads();
   if (tid == 0) {
     int run = 0;
-    for (int e = 0; e < n; ++e) {
-      base[e] = run;
-      run += tot[e];
+    for (int i = 0; i < n; ++i) {
+      off_s[i] = run;
+      run += tot_s[i];
     }
-    base[n] = run;
+    off_s[n] = run;
   }
   __syncthreads();
-  if (b == 0) {
-    for (int e = tid; e <= n; e += 256) {
-      offsets[e] = base[e];
-      if (e < n) counts[e] = tot[e];
+  for (int i = tid; i <= n; i += 1024) {
+    offsets[i] = off_s[i];
+    if (i < n) counts[i] = tot_s[i];
+  }
+  if (e < n) {
+    int run = off_s[e] + psum[tid];
+    for (int b = b0; b < b1; ++b) {
+      bases[(int64_t)b * n + e] = run;
+      run += hist[(int64_t)b * n + e];
     }
   }
+}
+
+// Scatter of one routing block (BT <= 32 tokens): positions are
+// expert-contiguous and ascending in token index within an expert.
+__global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ topk_idx,
+                                                     const int* __restrict__ bases, int64_t T, int n,
+                                                     int K, int BT, int* __restrict__ perm_token,
+                                                     int* __restrict__ slot_pos) {
+  __shared__ uint32_t mask_s[kMaxN];
+  __shared__ int sel_s[32 * kMaxK];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * BT;
+  const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
+  for (int e = tid; e < n; e += 64) mask_s[e] = 0u;
+  __syncthreads();
   if (tid < cnt) {
-    for (int k = 0; k < K; ++k) {
-      const int e = sel_s[tid * K + k];
-      int rank = 0;
-      for (int i2 = 0; i2 < tid; ++i2)
-        for (int k2 = 0; k2 < K; ++k2) rank += (sel_s[i2 * K + k2] == e) ? 1 : 0;
-      const int pos = base[e] + pre[e] + rank;
+    for (int j = 0; j < K; ++j) {
+      const int e = min(max(topk_idx[(t0 + tid) * K + j], 0), n - 1);
+      sel_s[tid * K + j] = e;
+      atomicOr(&mask_s[e], 1u << tid);
+    }
+  }
+  __syncthreads();
+  if (tid < cnt) {
+    for (int j = 0; j < K; ++j) {
+      const int e = sel_s[tid * K + j];
+      const int pos = bases[(int64_t)blockIdx.x * n + e] + __popc(mask_s[e] & ((1u << tid) - 1u));
       perm_token[pos] = (int)(t0 + tid);
-      slot_pos[(t0 + tid) * K + k] = pos;
+      slot_pos[(t0 + tid) * K + j] = pos;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int NE, int TT>
-static void launch_router_bf16_t(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d,
-                                 int n, int K, int* topk_idx, float* topk_w, int* hist,
-                                 hipStream_t s) {
-  const int BT = 64 * TT;
+namespace {
+
+template <int NE, int TT, int W>
+void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t d, int n, int K,
+                     const RouteBuffers& rb, bool fused, hipStream_t s) {
+  constexpr int BT = 16 * TT;
   const int64_t nb = (T + BT - 1) / BT;
-  hipLaunchKernelGGL((router_bf16_kernel<NE, TT>), dim3((unsigned)nb), dim3(256), 0, s, x, Wg, T,
-                     (int)d, n, K, topk_idx, topk_w, hist);
+  hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
+                     T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
+                     rb.offsets, rb.perm_token, rb.slot_pos);
 }
 
-hipError_t launch_router_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
-                              int K, int* topk_idx, float* topk_w, int* hist, hipStream_t s) {
-  const int ne = (n + 15) / 16;
+}  // namespace
+
+int route_block_tokens(int n) { return n <= 64 ? 32 : 16; }
+
+int route_padded_experts(int n) { return (n + 15) / 16 * 16; }
+
+hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                             int K, const RouteBuffers& rb, hipStream_t s, hipEvent_t after_router) {
+  const int NP = route_padded_experts(n);
+  hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
+                     dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int BT = route_block_tokens(n);
+  const int64_t nb = (T + BT - 1) / BT;
+  const bool fused = nb == 1;
+  const int ne = NP / 16;
   if (ne <= 1)
-    launch_router_bf16_t<1, 2>(x, Wg, T, d, n, K, topk_idx, topk_w, hist, s);
+    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, s);
   else if (ne <= 2)
-    launch_router_bf16_t<2, 2>(x, Wg, T, d, n, K, topk_idx, topk_w, hist, s);
+    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
   else if (ne <= 4)
-    launch_router_bf16_t<4, 2>(x, Wg, T, d, n, K, topk_idx, topk_w, hist, s);
+    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
   else if (ne <= 8)
-    launch_router_bf16_t<8, 2>(x, Wg, T, d, n, K, topk_idx, topk_w, hist, s);
+    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
   else
-    launch_router_bf16_t<16, 1>(x, Wg, T, d, n, K, topk_idx, topk_w, hist, s);
-  return hipGetLastError();
+    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, s);
+  e = hipGetLastError();
+  if (e == hipSuccess && after_router != nullptr) e = hipEventRecord(after_router, s);
+  if (e != hipSuccess || fused) return e;
+  return launch_dispatch(T, n, K, rb, s);
 }
 
-hipError_t launch_router_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
-                             int* topk_idx, float* topk_w, int* hist, hipStream_t s) {
+hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
+                            const RouteBuffers& rb, hipStream_t s) {
   const int BT = route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)nb), dim3(256), 0, s, x, Wg, T, d, n, K, BT,
-                     topk_idx, topk_w, hist);
-  return hipGetLastError();
+                     rb.topk_idx, rb.topk_w, rb.hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_dispatch(T, n, K, rb, s);
 }
 
-hipError_t launch_scatter(const int* topk_idx, const int* hist, int64_t T, int n, int K,
-                          int* counts, int* offsets, int* perm_token, int* slot_pos, hipStream_t s) {
+hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s) {
   const int BT = route_block_tokens(n);
   const int nb = (int)((T + BT - 1) / BT);
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(256), 0, s, topk_idx, hist, T, n, K,
-                     BT, nb, counts, offsets, perm_token, slot_pos);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, rb.bases, rb.counts,
+                     rb.offsets);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, s, rb.topk_idx, rb.bases, T, n, K,
+                     BT, rb.perm_token, rb.slot_pos);
   return hipGetLastError();
 }
 
