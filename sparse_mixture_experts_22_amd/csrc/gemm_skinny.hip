@@ -62,8 +62,17 @@ __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t&
 //         A rows are gathered from x via perm_token; h = SiLU(a) * b in bf16.
 // MODE 2: down.  The 4 waves stream W2 over quarters of this split's K range;
 //         A rows are h; o[split] receives the fp32 partial sum.
+// With the ping-pong buffers a wave keeps two K steps of loads in flight
+// (2 workgroups per CU).  The variant without them fits 4 workgroups per CU
+// (a decode launch is resident in one round) but measured slower: per-wave
+// memory parallelism matters more here than occupancy.
+#ifndef MOE_SKINNY_PINGPONG
+#define MOE_SKINNY_PINGPONG 1
+#endif
+constexpr int SKINNY_OCC = MOE_SKINNY_PINGPONG ? 2 : 4;
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void skinny_kernel(
+__global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
@@ -112,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+#if MOE_SKINNY_PINGPONG
     // ping-pong: step kc in (qa, aa), step kc+1 in (qb, ab)
     u32x4_t qa[8], qb[8];
     bf16x8_t aa, ab;
@@ -133,6 +143,14 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(
       if (kc + 1 < wk1) mma_block(qb, ab, acc);
       kc += 2;
     }
+#else
+    for (int kc = wk0; kc < wk1; ++kc) {
+      u32x4_t q[8];
+      load_block(q, bsrc + kc * kstep, N, b_ok);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(asrc + kc * 32);
+      mma_block(q, a, acc);
+    }
+#endif
     // partial tiles -> LDS; register slot q = c*4 + j
     __syncthreads();  // previous pass finished reading red
 #pragma unroll
