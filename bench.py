@@ -39,9 +39,17 @@ def parse():
                     choices=["mixtral_prefill", "mixtral_skewed", "many_experts", "mixtral_decode"])
     ap.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=512, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens in the oracle's timed sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device-to-device copy (reference for traffic counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace --stats csv directory and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR", nargs="+",
+                    help="print a summary of rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE "
+                         "scaled by the 1 GiB calibration copy) and exit")
+    ap.add_argument("--traffic-json", metavar="FILE",
+                    help="with --summarize-counters: also write the per-kernel HBM traffic, keyed by "
+                         "the hash of the kernel's sources")
     return ap.parse_args()
 
 
@@ -116,12 +124,15 @@ def time_workload(name, steps, warmup):
         moe.forward_traced(x, wg, w1, w3, w2, K, [e.cuda_event for e in events[i]], y=y)
     torch.cuda.synchronize()
     stage_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(5)] for ev in events])
+    traced_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
     rt = moe.route(x, wg, K, outputs=("counts",))
     torch.cuda.synchronize()
     counts = rt["counts"].cpu().numpy()
     assert torch.isfinite(y).all().item()
-    return dict(T=T, d=d, f=f, n=n, K=K, ms_per_step=total_ms / steps, wall_s=wall,
-                stage_ms=stage_ms.mean(axis=0), stage_ms_min=stage_ms.min(axis=0), counts=counts)
+    return dict(name=name, T=T, d=d, f=f, n=n, K=K, ms_per_step=total_ms / steps, wall_s=wall,
+                stage_ms=stage_ms.mean(axis=0), stage_ms_min=stage_ms.min(axis=0), counts=counts,
+                traced_step_ms={"median": round(float(np.median(traced_ms)), 4),
+                                "min": round(float(traced_ms.min()), 4), "max": round(float(traced_ms.max()), 4)})
 
 
 def prefill_record(r):
@@ -133,7 +144,8 @@ def prefill_record(r):
     return {
         "roofline": {"kernel": "grouped_gemm_kernel<1> (gate/up projection + SwiGLU)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("grouped_gemm_kernel<1>") if r["name"] == "mixtral_prefill" else None,
                      "flops_per_launch": up_flops, "avg_launch_ms": round(up_ms, 4)},
         "layer_tflops": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12, 1),
         "layer_frac_of_mfma_peak": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -154,11 +166,13 @@ def decode_record(r):
         "ms_per_step": round(r["ms_per_step"], 4),
         "roofline": {"kernel": "skinny_kernel<1> (gate/up projection + SwiGLU)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic("skinny_kernel<1>") if r["name"] == "mixtral_decode" else None,
                      "bytes_per_launch": up_bytes, "avg_launch_ms": round(up_ms, 4)},
         "layer_gbs": round(layer_gbs, 1), "layer_frac_of_hbm_peak": round(layer_gbs / PEAK_HBM_GBS, 4),
         "experts_touched": touched,
         "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, r["stage_ms"])},
+        "traced_step_ms": r["traced_step_ms"],
     }
 
 
@@ -186,8 +200,111 @@ def cpu_baseline(name, sample):
                       f"touched expert (weights widened per expert), {el:.1f} s"}
 
 
+# ---------------------------------------------------------------- profiles
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_counters.json")
+CALIB_BYTES = 1 << 30  # the --calibrate-copy copy: 1 GiB read, 1 GiB written
+# Sources that determine each measured kernel's code (a change voids its counters).
+KERNEL_SOURCES = {
+    "grouped_gemm_kernel<1>": ["csrc/gemm_prefill.hip", "csrc/moe_internal.h", "build.py"],
+    "grouped_gemm_kernel<2>": ["csrc/gemm_prefill.hip", "csrc/moe_internal.h", "build.py"],
+    "skinny_kernel<1>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
+    "skinny_kernel<2>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
+}
+
+
+def sources_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_22_amd", rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` in the default workloads (mixtral_prefill for the grouped
+    GEMMs, mixtral_decode for the skinny kernels) from the committed counter summary, or None
+    when that summary is missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_hash(kernel):
+        return None
+    return rec["hbm_bytes"]
+
+
+def short_kernel_name(name):
+    import re
+    name = name.replace("(anonymous namespace)::", "").replace("moe::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return re.sub(r"\(.*", "", name)
+
+
+def summarize_trace(d):
+    import csv
+    import glob
+    path = glob.glob(os.path.join(d, "*kernel_stats.csv"))[0]
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':58s} {'calls':>5s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'%':>6s}")
+    for r in rows:
+        print(f"{short_kernel_name(r['Name'])[:58]:58s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:10.1f} "
+              f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
+
+
+def summarize_counters(dirs, traffic_json=None):
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    copies = collections.defaultdict(list)
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            for r in csv.DictReader(open(path)):
+                name = short_kernel_name(r["Kernel_Name"])
+                key = f"{name} grid={int(r['Grid_Size'])}"
+                v = float(r["Counter_Value"])
+                per[key][r["Counter_Name"]].append(v)
+                if name == "__amd_rocclr_copyBuffer":
+                    copies[r["Counter_Name"]].append(v)
+    # The largest copy of the run is the 1 GiB calibration copy (every other copy is smaller).
+    fetch_factor = CALIB_BYTES / (max(copies["FETCH_SIZE"]) * 1024) if copies.get("FETCH_SIZE") else None
+    write_factor = CALIB_BYTES / (max(copies["WRITE_SIZE"]) * 1024) if copies.get("WRITE_SIZE") else None
+    print(f"calibration: 1 GiB device copy -> FETCH_SIZE {max(copies.get('FETCH_SIZE', [0])):.0f} KiB, "
+          f"WRITE_SIZE {max(copies.get('WRITE_SIZE', [0])):.0f} KiB; "
+          f"scale factors fetch {fetch_factor}, write {write_factor}")
+    out = {"fetch_factor": fetch_factor, "write_factor": write_factor, "kernels": {}}
+    for key in sorted(per):
+        cs = {c: sum(v) / len(v) for c, v in per[key].items()}
+        line = f"{key}: n={len(next(iter(per[key].values())))} " + " ".join(
+            f"{c}={v:.6g}" for c, v in sorted(cs.items()))
+        kname = key.split(" grid=")[0]
+        if "FETCH_SIZE" in cs and "WRITE_SIZE" in cs and fetch_factor and write_factor:
+            rb = cs["FETCH_SIZE"] * 1024 * fetch_factor
+            wb = cs["WRITE_SIZE"] * 1024 * write_factor
+            line += f" -> read {rb / 1e9:.4f} GB, written {wb / 1e9:.4f} GB per launch"
+            if kname in KERNEL_SOURCES and int(key.split("grid=")[1]) >= out["kernels"].get(kname, {}).get("grid", 0):
+                out["kernels"][kname] = {"grid": int(key.split("grid=")[1]),"fetch_kib": cs["FETCH_SIZE"], "write_kib": cs["WRITE_SIZE"],
+                                       "read_bytes": rb, "write_bytes": wb, "hbm_bytes": rb + wb,
+                                       "sources_sha256": sources_hash(kname)}
+        print(line)
+    if traffic_json:
+        with open(traffic_json, "w") as fh:
+            json.dump(out, fh, indent=1)
+            fh.write("\n")
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.traffic_json)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
@@ -231,6 +348,7 @@ def main():
         rec["layer_tflops"] = pr["layer_tflops"]
         rec["layer_frac_of_mfma_peak"] = pr["layer_frac_of_mfma_peak"]
     rec["stages_ms"] = {s: round(float(v), 4) for s, v in zip(STAGES, main_r["stage_ms"])}
+    rec["traced_step_ms"] = main_r["traced_step_ms"]
     rec["expert_counts"] = main_r["counts"].tolist()
     if not args.no_decode and args.workload != "mixtral_decode":
         dr_raw = time_workload("mixtral_decode", max(args.steps, 20), args.warmup)
