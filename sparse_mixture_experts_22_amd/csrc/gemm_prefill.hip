@@ -11,24 +11,27 @@
 //                  -> bf16 (round-to-nearest-even), W1 and W3 share the A tile
 //   down (MODE 2): o[p] = h[p] W2_e -> fp32
 //
-// Tiling: a 256-thread workgroup (4 waves, one per SIMD) computes a 256-row x
-// 256-column fp32 accumulator tile (for MODE 1: 128 W1 columns + the same 128
-// W3 columns) with v_mfma_f32_32x32x16_bf16; each wave owns 128 x 128 (16 MFMA
-// tiles, 256 accumulator registers).  K advances in steps of 32 through a ring
-// of 5 LDS stages (32 KiB each, all 160 KiB of the CU's LDS): global loads for
-// steps k+1 .. k+4 are in flight while step k is multiplied.
+// Tiling: a 512-thread workgroup (8 waves, two per SIMD) computes a 256-row
+// x 256-column fp32 accumulator tile (for MODE 1: 128 W1 columns + the same
+// 128 W3 columns) with v_mfma_f32_32x32x16_bf16; each wave owns 128 rows x 64
+// columns (8 MFMA tiles, 128 accumulator registers).  Two waves per SIMD keep
+// the matrix cores fed while the partner wave is stalled issuing its share of
+// the global loads (a CU can only have a bounded number of L2 requests in
+// flight, and a load that cannot be accepted blocks its wave).
 //
 // Data movement is HBM/L2 -> LDS directly (global_load_lds, 16 bytes per lane,
 // lane l writing bytes 16*l.. of a 1 KiB block), with no register staging and
 // no LDS store instructions.  Which global 16-byte chunk a lane fetches is
 // permuted so the LDS image is XOR-swizzled for gfx950's 64 banks (256 bytes
 // per cycle):
-//   A (activations, [row][k], 64-byte rows): chunk c of row r sits at
-//     position c ^ ((r >> 2) & 3), so the 16 lanes of an MFMA A read served
-//     together (16 rows, same logical chunk) hit 16 distinct 16-byte slots;
-//   B (weights, kept in their natural [k][n] layout, 512-byte rows): chunk c of
-//     row k sits at position c ^ (4 * (k & 3)), so the 32 lanes of a transpose
-//     read served together (4 rows x 2 column halves) hit distinct 32-byte slots.
+//   A (activations, [row][k]): stored in super-stages of 64 k, 128-byte rows
+//     (one cache line per row and request); chunk c of row r sits at
+//     c ^ ((r >> 1) & 7), so the 16 lanes of an MFMA A read served together
+//     (16 rows, same logical chunk) hit 16 distinct 16-byte slots;
+//   B (weights, kept in their natural [k][n] layout, stages of 32 k, 512-byte
+//     rows): chunk c of row k sits at c ^ (4 * (k & 3)), so the 32 lanes of a
+//     transpose read served together (4 rows x 2 column halves) hit distinct
+//     32-byte slots.
 // The weights are n-contiguous while MFMA wants 8 consecutive k per lane; the
 // B fragments are read with ds_read_b64_tr_b16, which transposes 16-bit data
 // across each group of 16 lanes: when lane q + 4j of a group points at
@@ -40,6 +43,8 @@
 // is ordered expert-major, then groups of 4 column tiles, then row tiles: the
 // ~32 tiles an XCD runs at once share 8 row blocks and 4 column blocks of one
 // expert, so their A and B k-slices are served from that XCD's L2.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -105,59 +110,46 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-// LDS rings: SA stages of the A tile and SB stages of the B tile (16 KiB
-// each; SA + SB = 10 fills the CU's 160 KiB).  Waves 0-1 load only B, waves
-// 2-3 only A: a wave's vmcnt retires in issue order, so giving each operand
-// its own waves lets the weight stream (read once from HBM, the long-latency
-// operand) run SB-1 steps ahead while the activations run SA-1 steps ahead.
+// LDS rings.  The activation operand A moves in "super-stages" of 64 k
+// (256 rows x 128 bytes = 32 KiB): a CU keeps a bounded number of L2 requests
+// in flight, and 128-byte rows are one full cache line per request where
+// 64-byte rows (32 k) would be half a line.  The weight operand
+// B moves in stages of 32 k (32 rows x 512 bytes = 16 KiB, four full lines per
+// row).  2*SA + SB = 10 fills the CU's 160 KiB.  Waves 0-3 load only B, waves
+// 4-7 only A: a wave's vmcnt retires in issue order, so giving each operand
+// its own waves lets each stream run as far ahead as its own ring allows.
 #ifndef MOE_RING_A
-#define MOE_RING_A 4
+#define MOE_RING_A 3
 #endif
 #ifndef MOE_RING_B
-#define MOE_RING_B 6
+#define MOE_RING_B 4
 #endif
-// Weight prefetch distance in k-steps beyond the B ring (0 = off).
-#ifndef MOE_B_PREFETCH
-#define MOE_B_PREFETCH 0
-#endif
-constexpr int SA = MOE_RING_A;
-constexpr int SB = MOE_RING_B;
-constexpr int BPF = MOE_B_PREFETCH;
-static_assert(SA >= 2 && SB >= 2 && SA + SB + (BPF > 0 ? 1 : 0) <= 10,
-              "LDS budget is 10 stages of 16 KiB (one is scratch for the prefetch)");
-// loads each wave issues per stage of its operand (8 blocks of 1 KiB)
-constexpr int LOADS_PER_STAGE = 8;
+constexpr int SA = MOE_RING_A;  // A super-stages (64 k each)
+constexpr int SB = MOE_RING_B;  // B stages (32 k each)
+static_assert(SA >= 2 && SB >= 2 && 2 * SA + SB <= 10, "LDS budget is 160 KiB");
+constexpr int A_LOADS = 8;  // 1 KiB loads per A-loader wave per super-stage
+constexpr int B_LOADS = 4;  // 1 KiB loads per B-loader wave per stage
 // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
 constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
 }
-// inside the loop, step kt+1 of the wave's operand must have landed while the
-// S-2 later steps may still be in flight; LDS reads must have returned
-constexpr int WAIT_AHEAD_A = waitcnt_imm(LOADS_PER_STAGE * (SA - 2), 0);
-// B loaders follow every stage's 8 loads (prologue included) with exactly one
-// prefetch, so after the loads of a stage come its prefetch and the
-// (loads + prefetch) of each later stage.
-constexpr int B_LOADS_PER_STEP = LOADS_PER_STAGE + (BPF > 0 ? 1 : 0);
-constexpr int B_TRAIL = BPF > 0 ? 1 : 0;
-constexpr int WAIT_AHEAD_B = waitcnt_imm(B_LOADS_PER_STEP * (SB - 2) + B_TRAIL, 0);
-// before the loop all S steps are in flight and step 0 must have landed
-constexpr int WAIT_FIRST_A = waitcnt_imm(LOADS_PER_STAGE * (SA - 1), 15);
-constexpr int WAIT_FIRST_B = waitcnt_imm(B_LOADS_PER_STEP * (SB - 1) + B_TRAIL, 15);
+// Publishing k-step kt+1: the wave's own loads of the stage holding it must
+// have landed while the later stages may stay in flight, and its LDS reads of
+// step kt must have returned (the slot of step kt is refilled after the barrier).
+constexpr int WAIT_AHEAD_B = waitcnt_imm(B_LOADS * (SB - 2), 0);
+constexpr int WAIT_AHEAD_A = waitcnt_imm(A_LOADS * (SA - 2), 0);  // kt+1 opens a super-stage
+constexpr int WAIT_LDS_ONLY = waitcnt_imm(63, 0);                 // kt+1 in the same super-stage
+// before the loop every stage is in flight and the first one must have landed
+constexpr int WAIT_FIRST_B = waitcnt_imm(B_LOADS * (SB - 1), 15);
+constexpr int WAIT_FIRST_A = waitcnt_imm(A_LOADS * (SA - 1), 15);
 constexpr int WAITCNT_ALL = waitcnt_imm(0, 15);
-static_assert(B_LOADS_PER_STEP * (SB - 1) + B_TRAIL < 64 && LOADS_PER_STAGE * (SA - 1) < 64,
-              "vmcnt is a 6-bit counter");
+static_assert(B_LOADS * (SB - 1) < 64 && A_LOADS * (SA - 1) < 64, "vmcnt is a 6-bit counter");
 
-constexpr int A_STAGE = BM * BK * 2;  // 16 KiB
+constexpr int A_SUPER = BM * 64 * 2;  // 32 KiB
 constexpr int B_STAGE = BK * BN * 2;  // 16 KiB
 
 __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
-}
-
-// 4 bytes per lane into LDS: used only to pull weight lines into L2 early
-// (the LDS destination is a scratch area nobody reads).
-__device__ __forceinline__ void prefetch_lds4(const void* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dword %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
 }
 
 __device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) {
@@ -169,12 +161,12 @@ __device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) 
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
+__global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ __attribute__((aligned(1024))) char smem[SA * A_STAGE + SB * B_STAGE + (BPF > 0 ? 1024 : 0)];
+  __shared__ __attribute__((aligned(1024))) char smem[SA * A_SUPER + SB * B_STAGE];
 
   constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
   const int NT = (N + NTW - 1) / NTW;
@@ -184,27 +176,30 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave >> 2;  // 128-row half of the tile
+  const int wn = wave & 3;  // 64-column quarter of the tile
 
-  // ---- global -> LDS load assignment.  Waves 0-1 (B loaders) each fill 8
-  // of the 16 B blocks of a stage (2 rows x 32 chunks each); waves 2-3 (A
-  // loaders) each fill 8 of the 16 A blocks (16 rows x 4 chunks each).
-  const bool b_loader = wave < 2;
-  const int lw = wave & 1;  // index among the loaders of the operand
-  const uint16_t* ld_ptr[8];
+  // ---- global -> LDS load assignment.  Waves 0-3 (B loaders) each fill 4
+  // of the 16 1-KiB blocks of a B stage (2 rows x 32 chunks each); waves 4-7
+  // (A loaders) each fill 8 of the 32 blocks of an A super-stage (8 rows x 8
+  // chunks each: every row is one full 128-byte line).
+  const bool b_loader = wave < 4;
+  const int lw = wave & 3;  // index among the loaders of the operand
+  const uint16_t* ld_ptr[A_LOADS];
+  if (!b_loader) {
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int blk = lw * 8 + b;
-    if (!b_loader) {
-      const int r = blk * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+    for (int b = 0; b < A_LOADS; ++b) {
+      const int r = (lw * A_LOADS + b) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
       const int p = min(max(tc.row0 + rr, 0), TK - 1);
       const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
       ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
-    } else {
-      const int k = blk * 2 + (lane >> 5);
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < B_LOADS; ++b) {
+      const int k = (lw * B_LOADS + b) * 2 + (lane >> 5);
       const int cb = (lane & 31) ^ (4 * (k & 3));
       int col;
       const uint16_t* mat;
@@ -220,155 +215,144 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     }
   }
   char* a_lds = smem;
-  char* b_lds = smem + SA * A_STAGE;
-  const uint32_t ld_base = (uint32_t)(uintptr_t)(lds_void*)(b_loader ? b_lds : a_lds) + lw * 8192;
-  const int ld_stage_bytes = b_loader ? B_STAGE : A_STAGE;
-  const int ld_ring = b_loader ? SB : SA;
-  const int64_t ld_kstep = b_loader ? (int64_t)BK * N : (int64_t)BK;  // elements per k-step
-  // This wave's loads of k-step `kt_data` into slot `kt_slot % ring`.
-  auto issue_stage = [&](int kt_slot, int kt_data) {
-    const uint32_t dst = ld_base + (kt_slot % ld_ring) * ld_stage_bytes;
-    const int64_t koff = (int64_t)kt_data * ld_kstep;
+  char* b_lds = smem + SA * A_SUPER;
+  const uint32_t a_ld_base = (uint32_t)(uintptr_t)(lds_void*)a_lds + lw * (A_LOADS * 1024);
+  const uint32_t b_ld_base = (uint32_t)(uintptr_t)(lds_void*)b_lds + lw * (B_LOADS * 1024);
+  // A loaders: super-stage `s_data` (k = 64*s_data ..) into slot s_slot % SA.
+  auto issue_a = [&](int s_slot, int s_data) {
+    const uint32_t dst = a_ld_base + (s_slot % SA) * A_SUPER;
+    const int64_t koff = (int64_t)s_data * 64;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
+    for (int b = 0; b < A_LOADS; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
   };
-  // Weight prefetch: the tiles an XCD runs together share each weight k-slice
-  // (32 rows x 512 bytes = 128 cache lines); tile m of the group touches 16
-  // of those lines (rows 4*(m%8) .. +3, all 4 lines of each row) BPF steps
-  // ahead of the B ring, so the ring's own loads of that slice hit in L2.
-  // Both B loader waves issue the instruction (lanes 16..63 repeat lanes
-  // 0..15); the second copy is an L2 hit and keeps the two waves' load
-  // counts identical.
-  const uint16_t* pf_ptr = nullptr;
-  uint32_t pf_lds = 0;
-  if (BPF > 0 && b_loader) {
-    const int q = lane & 15;
-    const int row = 4 * (tc.m & 7) + (q >> 2);
-    const int line = q & 3;
-    int col;
-    const uint16_t* mat;
-    if (MODE == 1) {
-      col = tc.nt * 128 + (line & 1) * 64;
-      mat = (line >> 1) ? B3 : B1;
-    } else {
-      col = tc.nt * 256 + line * 64;
-      mat = B1;
-    }
-    if (col >= N) col = 0;
-    pf_ptr = mat + (int64_t)tc.e * Kdim * N + (int64_t)row * N + col;
-    pf_lds = (uint32_t)(uintptr_t)(lds_void*)(smem + SA * A_STAGE + SB * B_STAGE) + lw * 256;
-  }
-  auto issue_prefetch = [&](int kt_data) {
-    if (BPF > 0 && b_loader) prefetch_lds4(pf_ptr + (int64_t)kt_data * BK * N, pf_lds);
+  // B loaders: k-step `kt_data` into slot kt_slot % SB.
+  auto issue_b = [&](int kt_slot, int kt_data) {
+    const uint32_t dst = b_ld_base + (kt_slot % SB) * B_STAGE;
+    const int64_t koff = (int64_t)kt_data * BK * N;
+#pragma unroll
+    for (int b = 0; b < B_LOADS; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // ---- fragment read addresses (byte offsets inside a stage)
+  // ---- fragment read addresses (byte offsets inside a super-stage / stage).
+  // A: 128-byte rows; 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so
+  // the 16 lanes of a 16-byte read served together (16 rows, same chunk) hit
+  // 16 distinct 16-byte slots of the 64 banks.  Step kt uses chunks
+  // 4*(kt & 1) .. +3 of its super-stage; row block i adds i * 4 KiB.
   const int m = lane & 31;
   const int kg = lane >> 5;
-  int a_off[2][4];
+  int a_off[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int par = 0; par < 2; ++par)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + m;
-      a_off[ks][i] = r * 64 + (((ks * 2 + kg) ^ ((m >> 2) & 3)) * 16);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int r = wm * 128 + m;
+      a_off[par][ks] = r * 128 + (((par * 4 + ks * 2 + kg) ^ ((m >> 1) & 7)) * 16);
     }
   const int g16 = lane >> 4;      // 16-lane group
   const int h16 = g16 & 1;        // column half of a 32-column MFMA tile
   const int kg16 = g16 >> 1;      // k half of the MFMA step
   const int bj = (lane & 15) >> 2;
   const int qq = lane & 3;
-  int b_off[2][4][2];
+  int b_off[2][2][2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int nb = (MODE == 1) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32) : (wn * 128 + j * 32);
+        // MODE 1: fragment 0 = W1 columns, fragment 1 = the same W3 columns
+        const int nb = (MODE == 1) ? (j * 128 + wn * 32) : (wn * 64 + j * 32);
         const int k = ks * 16 + kg16 * 8 + 4 * t + bj;
         const int cc = (nb >> 3) + 2 * h16 + (qq >> 1);
         b_off[ks][j][t] = k * 512 + ((cc ^ (4 * bj)) * 16) + (qq & 1) * 8;
       }
 
-  auto read_frags = [&](int kt, int ks, bf16x8_t (&a)[4], bf16x8_t (&b)[4]) {
-    const char* as = a_lds + (kt % SA) * A_STAGE;
+  // fragments of sub-step ks (k 16*ks .. +15) of k-step kt, whose parity is `par`
+  auto read_frags = [&](int kt, int par, int ks, bf16x8_t (&a)[4], bf16x8_t (&b)[2]) {
+    const char* as = a_lds + ((kt >> 1) % SA) * A_SUPER + a_off[par][ks];
     const char* bs = b_lds + (kt % SB) * B_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + a_off[ks][i]);
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 4096);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = read_b_frag(bs + b_off[ks][j][0], bs + b_off[ks][j][1]);
+    for (int j = 0; j < 2; ++j) b[j] = read_b_frag(bs + b_off[ks][j][0], bs + b_off[ks][j][1]);
   };
-  auto mfma_step = [&](const bf16x8_t (&a)[4], const bf16x8_t (&b)[4]) {
+  auto mfma_step = [&](const bf16x8_t (&a)[4], const bf16x8_t (&b)[2]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   };
   auto fence = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Scheduling pattern of a half step: the 12 fragment reads (4 A + 8
-  // transposed B) each followed by one MFMA, then the remaining 4 MFMAs.
+  // Scheduling pattern of a half step: the 8 fragment reads (4 A + 4
+  // transposed B) each followed by one of the 8 MFMAs.
   auto interleave = [] {
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // ---- main loop.  A k-step has two MFMA sub-steps (k = 0..15, 16..31).
   // The barrier that publishes step kt+1 sits between them: before it, each
   // wave has its sub-step-1 fragments of step kt in registers (lgkmcnt(0))
-  // and waits until its own loads of step kt+1 have landed (vmcnt); after it,
-  // step kt's slots are free and each loader wave refills its operand's slot
-  // with the step S ahead, while the sub-step-0 fragments of step kt+1 are
-  // read (issued first, ahead of the loads) during the sub-step-1 MFMAs of
-  // step kt.  Steps past the end reload the last k-slice into slots nobody
-  // reads again, so the count of outstanding loads never changes.
-  const int nk = Kdim / BK;
-  const int ring = ld_ring;
-  for (int st = 0; st < ring; ++st) {
-    issue_stage(st, min(st, nk - 1));
-    issue_prefetch(min(st + BPF, nk - 1));
-  }
-  if (b_loader)
+  // and waits until its own loads holding step kt+1 have landed (vmcnt);
+  // after it, the slots that only step kt used are free and are refilled
+  // (B: every step, with the step SB ahead; A: after odd steps, when a whole
+  // super-stage has been consumed, with the super-stage SA ahead), while the
+  // sub-step-0 fragments of step kt+1 are read during the sub-step-1 MFMAs of
+  // step kt.  Loads past the end reload the last k-slice into slots nobody
+  // reads again, so the count of outstanding loads never changes.  The loop
+  // runs over pairs of steps so the parity of kt is a compile-time constant.
+  const int nk = Kdim / BK;  // even: Kdim is a multiple of 64
+  const int nks = nk / 2;
+  if (b_loader) {
+    for (int st = 0; st < SB; ++st) issue_b(st, min(st, nk - 1));
     __builtin_amdgcn_s_waitcnt(WAIT_FIRST_B);  // step 0 landed
-  else
-    __builtin_amdgcn_s_waitcnt(WAIT_FIRST_A);
+  } else {
+    for (int st = 0; st < SA; ++st) issue_a(st, min(st, nks - 1));
+    __builtin_amdgcn_s_waitcnt(WAIT_FIRST_A);  // super-stage 0 landed
+  }
   fence();
   __builtin_amdgcn_s_barrier();
   fence();
-  bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
-  read_frags(0, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    read_frags(kt, 1, fa1, fb1);
+  bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
+  read_frags(0, 0, 0, fa0, fb0);
+  auto step = [&](int kt, auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    read_frags(kt, par, 1, fa1, fb1);
     mfma_step(fa0, fb0);
     interleave();
     if (b_loader)
-      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_B);  // lgkmcnt(0) and step kt+1 landed
+      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_B);
     else
-      __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_A);
+      __builtin_amdgcn_s_waitcnt(par ? WAIT_AHEAD_A : WAIT_LDS_ONLY);
     fence();
     __builtin_amdgcn_s_barrier();
     fence();
-    read_frags(kt + 1, 0, fa0, fb0);
-    issue_stage(kt + ring, min(kt + ring, nk - 1));
-    issue_prefetch(min(kt + ring + BPF, nk - 1));  // B loaders only
+    read_frags(kt + 1, par ^ 1, 0, fa0, fb0);
+    if (b_loader)
+      issue_b(kt + SB, min(kt + SB, nk - 1));
+    else if (par)
+      issue_a((kt >> 1) + SA, min((kt >> 1) + SA, nks - 1));
     mfma_step(fa1, fb1);
     interleave();
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
   }
   // the last (redundant) loads must land before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
@@ -377,28 +361,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int lk = kg;
   // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (MODE == 1) {
+    const int c = tc.nt * 128 + wn * 32 + lrow;
+    if (c < N) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int c = tc.nt * 128 + wn * 64 + jj * 32 + lrow;
-        if (c >= N) continue;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
           if (row < tc.rows && tc.row0 + row < TK) {
-            const float a = acc[i][jj][r];
-            const float b = acc[i][jj + 2][r];
+            const float a = acc[i][0][r];
+            const float b = acc[i][1][r];
             hout[(int64_t)(tc.row0 + row) * N + c] = f32_to_bf16_rne(silu_f32(a) * b);
           }
         }
-      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = tc.nt * 256 + wn * 128 + j * 32 + lrow;
+      for (int j = 0; j < 2; ++j) {
+        const int c = tc.nt * 256 + wn * 64 + j * 32 + lrow;
         if (c >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -421,7 +403,7 @@ hipError_t launch_prefill_up(const uint16_t* x, int64_t T, const int* perm_token
                              const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
                              uint16_t* h, hipStream_t s) {
   const int NT = (f + 127) / 128;
-  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT)), dim3(256), 0, s, x,
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT)), dim3(512), 0, s, x,
                      perm_token, W1, W3, offsets, n, d, f, (int)T, (int)TK, h, (float*)nullptr);
   return hipGetLastError();
 }
@@ -429,7 +411,7 @@ hipError_t launch_prefill_up(const uint16_t* x, int64_t T, const int* perm_token
 hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
                                int n, int f, int d, float* o, hipStream_t s) {
   const int NT = (d + 255) / 256;
-  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT)), dim3(256), 0, s, h,
+  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT)), dim3(512), 0, s, h,
                      (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, (int)TK,
                      (int)TK, (uint16_t*)nullptr, o);
   return hipGetLastError();
