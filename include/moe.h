@@ -27,8 +27,9 @@
  *     W2[n][f][d].  bf16 entry points take bf16 storage (uint16 bit patterns).
  *   - Limits: 1 <= K <= n <= 256, K <= 8, T*K < 2^31.  bf16 entry points need
  *     d % 64 == 0, f % 64 == 0 and 16-byte aligned tensors (MOE_ERR_UNSUPPORTED).
- *   - The library owns a per-device workspace (routing arrays and the
- *     intermediate h and o buffers, moe_workspace_bytes() bytes).  It is
+ *   - The library owns a per-device workspace (routing arrays, the
+ *     intermediate h and o buffers and partial sums of split tiles, at most
+ *     moe_workspace_bytes() bytes).  It is
  *     allocated on the first call on a device and grown on demand (the growing
  *     call synchronises the device); moe_release() frees it.  Calls that share
  *     a device's workspace must not run concurrently on different streams.
@@ -118,7 +119,9 @@ moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d
                            int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
                            moe_stream_t stream);
 
-/* Bytes of library workspace a call of this shape needs (0 on invalid shapes). */
+/* Bytes of library workspace a call of this shape needs on any supported
+ * device (an upper bound: the prefill path's leftover-tile buffer scales with
+ * the device's compute units per XCD); 0 on invalid shapes. */
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K);
 
 /* Frees the workspace of every device (synchronises each device first). */

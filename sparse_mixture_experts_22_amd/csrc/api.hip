@@ -27,6 +27,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  int cus_per_xcd = 0;  // compute units per XCD, queried on first use
 };
 std::mutex g_ws_mutex;
 DeviceWorkspace g_ws[kMaxDevices];
@@ -39,12 +40,12 @@ enum class Path { kRouteOnly, kBf16, kF32 };
 struct Plan {
   size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
          perm_token = 0, slot_pos = 0;
-  size_t h = 0, o = 0, total = 0;
+  size_t h = 0, o = 0, tail = 0, total = 0;
   bool skinny = false;
   int splits = 1;
 };
 
-Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path) {
+Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus_per_xcd = 0) {
   Plan p;
   const int64_t TK = T * K;
   const int BT = moe::route_block_tokens(n);
@@ -69,6 +70,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path) {
     p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
     p.h = take((size_t)TK * f * 2);
     p.o = take((size_t)p.splits * TK * d * 4);
+    if (!p.skinny && cus_per_xcd >= 1 && cus_per_xcd <= 64) p.tail = take(moe::prefill_tail_bytes(cus_per_xcd));
   } else if (path == Path::kF32) {
     p.h = take((size_t)TK * f * 4);
     p.o = take((size_t)TK * d * 4);
@@ -132,6 +134,25 @@ moe_status_t get_workspace(size_t bytes, char** out) {
     ws.bytes = bytes;
   }
   *out = static_cast<char*>(ws.ptr);
+  return MOE_OK;
+}
+
+// Compute units per XCD of the current device (the tile scheduler assumes 8
+// XCDs, the layout of the CDNA4 parts), queried once per device.
+moe_status_t cus_per_xcd(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace& ws = g_ws[dev];
+  if (ws.cus_per_xcd == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    ws.cus_per_xcd = cus >= 8 ? cus / 8 : 1;
+  }
+  *out = ws.cus_per_xcd;
   return MOE_OK;
 }
 
@@ -224,7 +245,10 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
     for (int i = 0; i < 6; ++i)
       if (ev[i] == nullptr) return fail(MOE_ERR_INVALID_ARG, "stage_events must hold 6 events");
   if (T == 0) return MOE_OK;
-  const Plan p = make_plan(T, d, f, n, K, Path::kBf16);
+  int cus = 0;
+  st = cus_per_xcd(&cus);
+  if (st != MOE_OK) return st;
+  const Plan p = make_plan(T, d, f, n, K, Path::kBf16, cus);
   char* ws = nullptr;
   st = get_workspace(p.total, &ws);
   if (st != MOE_OK) return st;
@@ -252,11 +276,12 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
     MOE_LAUNCH(moe::launch_skinny_down(h, w2, r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
                "down-projection kernel launch");
   } else {
-    MOE_LAUNCH(moe::launch_prefill_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, h,
-                                      stream),
+    MOE_LAUNCH(moe::launch_prefill_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, cus,
+                                      h, stream),
                "up-projection kernel launch");
     MOE_LAUNCH(mark(3), "hipEventRecord");
-    MOE_LAUNCH(moe::launch_prefill_down(h, w2, r.offsets, TK, n, (int)f, (int)d, o, stream),
+    float* tail = p.tail ? at<float>(ws, p.tail) : nullptr;
+    MOE_LAUNCH(moe::launch_prefill_down(h, w2, r.offsets, TK, n, (int)f, (int)d, cus, tail, o, stream),
                "down-projection kernel launch");
   }
   MOE_LAUNCH(mark(4), "hipEventRecord");
@@ -334,7 +359,8 @@ moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d
 
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K) {
   if (check_shape(T, d, f, n, K, true) != MOE_OK) return 0;
-  const Plan a = make_plan(T, d, f, n, K, Path::kBf16);
+  // sized for the largest device layout the tile scheduler uses (64 CUs per XCD)
+  const Plan a = make_plan(T, d, f, n, K, Path::kBf16, 64);
   const Plan b = make_plan(T, d, f, n, K, Path::kF32);
   return a.total > b.total ? a.total : b.total;
 }

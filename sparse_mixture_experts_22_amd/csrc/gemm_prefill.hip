@@ -56,24 +56,27 @@ constexpr int BN = 256;         // LDS B-tile columns
 constexpr int BK = 32;
 constexpr int NGROUP = 4;       // column tiles per scheduling group
 
+constexpr int kXcds = 8;          // the hardware hands workgroup i to XCD (i mod 8)
+constexpr int kMaxTailSplit = 8;  // k-pieces per leftover tile
+
 struct Tile {
   int e, m, nt, row0, rows;
+  int k0, k1;  // k-steps [k0, k1) of this workgroup's share of the tile
+  int slot;    // >= 0: a k-piece of a split tile, partial sums go to this slot
 };
 
-// Maps this workgroup to a tile, or returns false if it has none.  All threads
-// compute the same answer from offsets[0..n] (uniform loads).
-__device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, Tile& tc) {
+__device__ int count_tiles(const int* __restrict__ offsets, int n, int NT) {
   int total = 0;
   for (int e = 0; e < n; ++e) {
     const int c = offsets[e + 1] - offsets[e];
     total += ((c + BM - 1) / BM) * NT;
   }
-  const int per = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int i = blockIdx.x >> 3;
-  if (i >= per) return false;
-  int L = xcd * per + i;
-  if (L >= total) return false;
+  return total;
+}
+
+// Position L of the tile list -> expert, row tile, column tile.  The list is
+// expert-major, then groups of NGROUP column tiles, then row tiles.
+__device__ bool tile_at(const int* __restrict__ offsets, int n, int NT, int L, Tile& tc) {
   for (int e = 0; e < n; ++e) {
     const int c = offsets[e + 1] - offsets[e];
     const int mt = (c + BM - 1) / BM;
@@ -104,6 +107,63 @@ __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, Tile
     L -= cnt;
   }
   return false;
+}
+
+// Work of one XCD: the contiguous tiles [beg, beg + cnt) of the list.  `q`
+// tiles fill whole waves of the XCD's `cus` compute units; when the `r`
+// leftover tiles would leave more than half of the last wave idle (and the
+// kernel may split), each is cut into `s` k-pieces of `chunk` k-steps, so
+// the last wave is r * s <= cus shorter workgroups.
+struct XcdPlan {
+  int beg, cnt, q, r, s, chunk;
+};
+
+__device__ XcdPlan xcd_plan(int total, int x, int cus, int nk, bool may_split) {
+  XcdPlan t;
+  const int per = (total + kXcds - 1) / kXcds;
+  t.beg = x * per;
+  t.cnt = max(0, min(per, total - t.beg));
+  t.q = t.cnt / cus * cus;
+  t.r = t.cnt - t.q;
+  t.s = 1;
+  t.chunk = nk;
+  if (may_split && t.r > 0 && 2 * t.r <= cus) {
+    const int s0 = min(min(cus / t.r, kMaxTailSplit), nk / 2);
+    if (s0 >= 2) {
+      t.chunk = 2 * ((nk / 2 + s0 - 1) / s0);  // whole 64-k super-stages
+      t.s = (nk + t.chunk - 1) / t.chunk;
+    }
+  }
+  return t;
+}
+
+// Maps this workgroup to its tile (or k-piece of a tile); false if it has none.
+// All threads compute the same answer from offsets[0..n] (uniform loads).
+__device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int nk, int cus,
+                            bool may_split, Tile& tc) {
+  const int total = count_tiles(offsets, n, NT);
+  const int x = blockIdx.x % kXcds;
+  const int i = blockIdx.x / kXcds;
+  const XcdPlan t = xcd_plan(total, x, cus, nk, may_split);
+  tc.k0 = 0;
+  tc.k1 = nk;
+  tc.slot = -1;
+  int L;
+  if (t.s == 1) {
+    if (i >= t.cnt) return false;
+    L = t.beg + i;
+  } else if (i < t.q) {
+    L = t.beg + i;
+  } else {
+    const int u = i - t.q;
+    if (u >= t.r * t.s) return false;
+    L = t.beg + t.q + u % t.r;
+    const int piece = u / t.r;
+    tc.k0 = piece * t.chunk;
+    tc.k1 = min(nk, tc.k0 + t.chunk);
+    tc.slot = x * cus + u;
+  }
+  return tile_at(offsets, n, NT, L, tc);
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -164,14 +224,15 @@ template <int MODE>
 __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
-    const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK,
-    uint16_t* __restrict__ hout, float* __restrict__ oout) {
+    const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK, int cus,
+    uint16_t* __restrict__ hout, float* __restrict__ oout, float* __restrict__ tail_ws) {
   __shared__ __attribute__((aligned(1024))) char smem[SA * A_SUPER + SB * B_STAGE];
 
   constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
   const int NT = (N + NTW - 1) / NTW;
   Tile tc;
-  if (!decode_tile(offsets, n, NT, tc)) return;
+  // only the down projection (plain fp32 output) splits leftover tiles over k
+  if (!decode_tile(offsets, n, NT, Kdim / BK, cus, MODE == 2 && tail_ws != nullptr, tc)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -218,17 +279,17 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   char* b_lds = smem + SA * A_SUPER;
   const uint32_t a_ld_base = (uint32_t)(uintptr_t)(lds_void*)a_lds + lw * (A_LOADS * 1024);
   const uint32_t b_ld_base = (uint32_t)(uintptr_t)(lds_void*)b_lds + lw * (B_LOADS * 1024);
-  // A loaders: super-stage `s_data` (k = 64*s_data ..) into slot s_slot % SA.
+  // A loaders: super-stage `s_data` of this workgroup's k range into slot s_slot % SA.
   auto issue_a = [&](int s_slot, int s_data) {
     const uint32_t dst = a_ld_base + (s_slot % SA) * A_SUPER;
-    const int64_t koff = (int64_t)s_data * 64;
+    const int64_t koff = (int64_t)(tc.k0 / 2 + s_data) * 64;
 #pragma unroll
     for (int b = 0; b < A_LOADS; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
   };
-  // B loaders: k-step `kt_data` into slot kt_slot % SB.
+  // B loaders: k-step `kt_data` of this workgroup's k range into slot kt_slot % SB.
   auto issue_b = [&](int kt_slot, int kt_data) {
     const uint32_t dst = b_ld_base + (kt_slot % SB) * B_STAGE;
-    const int64_t koff = (int64_t)kt_data * BK * N;
+    const int64_t koff = (int64_t)(tc.k0 + kt_data) * BK * N;
 #pragma unroll
     for (int b = 0; b < B_LOADS; ++b) load_lds16(ld_ptr[b] + koff, dst + b * 1024);
   };
@@ -316,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   // step kt.  Loads past the end reload the last k-slice into slots nobody
   // reads again, so the count of outstanding loads never changes.  The loop
   // runs over pairs of steps so the parity of kt is a compile-time constant.
-  const int nk = Kdim / BK;  // even: Kdim is a multiple of 64
+  const int nk = tc.k1 - tc.k0;  // even: Kdim and the pieces are multiples of 64 k
   const int nks = nk / 2;
   if (b_loader) {
     for (int st = 0; st < SB; ++st) issue_b(st, min(st, nk - 1));
@@ -360,6 +421,20 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   const int lrow = m;
   const int lk = kg;
   // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  if (MODE == 2 && tc.slot >= 0) {
+    // a k-piece: the whole 256 x 256 partial tile goes to its slot
+    float* dst = tail_ws + (int64_t)tc.slot * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+          dst[row * BN + wn * 64 + j * 32 + lrow] = acc[i][j][r];
+        }
+    return;
+  }
   if (MODE == 1) {
     const int c = tc.nt * 128 + wn * 32 + lrow;
     if (c < N) {
@@ -391,29 +466,67 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   }
 }
 
-// Upper bound of the tile count: sum_e ceil(c_e / BM) <= ceil(TK / BM) + n.
-inline unsigned prefill_grid(int64_t TK, int n, int NT) {
-  const int64_t ub = ((TK + BM - 1) / BM + n) * (int64_t)NT;
-  return (unsigned)(((ub + 7) / 8) * 8);
+// Sums the k-pieces of each split tile in piece order and stores the rows of
+// o it owns.  Workgroup b covers 4 rows of leftover tile (b / 64) % 32 of XCD
+// b / 2048; it recomputes the XCD's plan exactly as the GEMM did.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict__ offsets, int n, int N,
+                                                          int nk, int cus, const float* __restrict__ tail_ws,
+                                                          float* __restrict__ o) {
+  const int NT = (N + 255) / 256;
+  const int x = blockIdx.x / (32 * 64);
+  const int t = (blockIdx.x / 64) % 32;
+  const int rblk = blockIdx.x % 64;
+  const XcdPlan pl = xcd_plan(count_tiles(offsets, n, NT), x, cus, nk, true);
+  if (pl.s == 1 || t >= pl.r) return;
+  Tile tc;
+  if (!tile_at(offsets, n, NT, pl.beg + pl.q + t, tc)) return;
+  const int col = threadIdx.x;
+  const int c = tc.nt * 256 + col;
+  if (c >= N) return;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = rblk * 4 + rr;
+    if (row >= tc.rows) break;
+    float sum = 0.0f;
+    for (int p = 0; p < pl.s; ++p)
+      sum += tail_ws[(int64_t)(x * cus + p * pl.r + t) * (BM * BN) + row * BN + col];
+    o[(int64_t)(tc.row0 + row) * N + c] = sum;
+  }
+}
+
+// Grid: per XCD at most ceil(tiles / 8) tiles plus one extra wave of pieces.
+inline unsigned prefill_grid(int64_t TK, int n, int NT, int cus) {
+  const int64_t tiles_ub = ((TK + BM - 1) / BM + n) * (int64_t)NT;  // sum_e ceil(c_e/BM) bound
+  const int64_t per = (tiles_ub + kXcds - 1) / kXcds;
+  return (unsigned)((per + cus) * kXcds);
 }
 
 }  // namespace
 
+size_t prefill_tail_bytes(int cus_per_xcd) { return (size_t)kXcds * cus_per_xcd * BM * BN * sizeof(float); }
+
 hipError_t launch_prefill_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                              const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
-                             uint16_t* h, hipStream_t s) {
+                             int cus_per_xcd, uint16_t* h, hipStream_t s) {
   const int NT = (f + 127) / 128;
-  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT)), dim3(512), 0, s, x,
-                     perm_token, W1, W3, offsets, n, d, f, (int)T, (int)TK, h, (float*)nullptr);
+  hipLaunchKernelGGL((grouped_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(512), 0, s,
+                     x, perm_token, W1, W3, offsets, n, d, f, (int)T, (int)TK, cus_per_xcd, h,
+                     (float*)nullptr, (float*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
-                               int n, int f, int d, float* o, hipStream_t s) {
+                               int n, int f, int d, int cus_per_xcd, float* tail_ws, float* o,
+                               hipStream_t s) {
   const int NT = (d + 255) / 256;
-  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT)), dim3(512), 0, s, h,
-                     (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, (int)TK,
-                     (int)TK, (uint16_t*)nullptr, o);
+  hipLaunchKernelGGL((grouped_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(512), 0, s,
+                     h, (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, (int)TK,
+                     (int)TK, cus_per_xcd, (uint16_t*)nullptr, o, tail_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || tail_ws == nullptr) return e;
+  // leftover tiles per XCD are at most cus / 2 <= 32 (cus <= 64 is checked by the caller)
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds * 32 * 64), dim3(256), 0, s, offsets, n, d, f / BK,
+                     cus_per_xcd, tail_ws, o);
   return hipGetLastError();
 }
 

@@ -58,12 +58,18 @@ hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipS
 
 // ------------------------------------------------------ expert projections
 // Gate/up: h[p][:] = SiLU(x[perm_token[p]] W1_e) * (x[perm_token[p]] W3_e), bf16 out.
+// `cus_per_xcd`: compute units per XCD of the device (tile scheduling).
 hipError_t launch_prefill_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                              const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
-                             uint16_t* h, hipStream_t s);
-// Down: o[p][:] = h[p] W2_e, fp32 out.
+                             int cus_per_xcd, uint16_t* h, hipStream_t s);
+// Down: o[p][:] = h[p] W2_e, fp32 out.  With `tail_ws` (prefill_tail_bytes
+// bytes, 1 <= cus_per_xcd <= 64) the tiles left over after the last full wave
+// are split over k and their pieces summed by a second kernel; with nullptr
+// every tile runs whole.
 hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
-                               int n, int f, int d, float* o, hipStream_t s);
+                               int n, int f, int d, int cus_per_xcd, float* tail_ws, float* o,
+                               hipStream_t s);
+size_t prefill_tail_bytes(int cus_per_xcd);
 hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                             const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
                             uint16_t* h, hipStream_t s);
