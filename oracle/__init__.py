@@ -12,10 +12,12 @@ from .moe_oracle import (  # noqa: F401
     forward,
     forward_mask_form,
     forward_with_selection,
+    full_softmax,
     gate_weights,
     mixtral_param_counts,
     route,
     router_logits,
+    router_stats,
     sigmoid,
     silu,
     topk_select,

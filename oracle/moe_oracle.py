@@ -110,6 +110,39 @@ def route(x, Wg, K: int) -> dict:
                 counts=counts, offsets=offsets, perm_token=perm_token, slot_pos=slot_pos)
 
 
+def full_softmax(logits: np.ndarray) -> np.ndarray:
+    """The router's probability of every expert for every token: softmax over
+    all n logits (max-subtracted), before any expert is dropped."""
+    lg = _f64(logits)
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def router_stats(logits: np.ndarray, sel: np.ndarray, alpha: float) -> dict:
+    """Load-balancing statistics of the Switch design, as Part 5 of "Mixture of
+    Experts: Why Mixtral Only Wakes Up Two Specialists" describes them ("The
+    favourite expert problem", tool 2), for top-K routing:
+
+      f_i  share of the routed work sent to expert i: the T*K assignments
+           count once each, so f_i = counts_i / (T*K) and the shares sum to 1
+           (the page calls both shares even at 1/N each);
+      P_i  the router's average probability for expert i over the tokens
+           (full softmax over all N experts);
+      loss = alpha * N * sum_i f_i * P_i.
+    """
+    lg = _f64(logits)
+    T, n = lg.shape
+    K = sel.shape[1]
+    counts = np.zeros(n, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            counts[sel[t, k]] += 1
+    frac = counts / float(T * K)
+    prob = full_softmax(lg).mean(axis=0)
+    loss = alpha * n * float(np.sum(frac * prob))
+    return dict(frac=frac, prob=prob, aux_loss=loss, counts=counts)
+
+
 def brute_force_topk(logit_row: np.ndarray, K: int) -> tuple:
     """Top-K by exhaustive search over all C(n, K) expert subsets: the subset with
     the largest logit sum; among equal sums the lexicographically smallest

@@ -365,3 +365,65 @@ def test_skewed_router_recipe_shares():
     top1 = np.bincount(sel[:, 0], minlength=8) / sel.shape[0]
     assert 0.45 <= top1[0] <= 0.50
     assert top1[7] < 0.02
+
+
+# ------------------------------------------------------ router statistics
+# Part 5 of the explainer ("The favourite expert problem", tool 2): the loss
+# alpha * N * sum_i f_i P_i is smallest when both shares are even (1/N each).
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_stats_uniform_probabilities_give_alpha(K):
+    # W_g = 0: every logit ties, P_i = 1/N exactly; any f then gives alpha
+    n, T, alpha = 8, 40, 0.02
+    logits = np.zeros((T, n))
+    sel, _, _ = oracle.topk_select(logits, K)
+    st = oracle.router_stats(logits, sel, alpha)
+    np.testing.assert_array_equal(st["prob"], np.full(n, 1.0 / n))
+    assert abs(st["aux_loss"] - alpha) <= 1e-15
+
+
+def test_stats_balanced_assignment_gives_alpha():
+    # round-robin top-1 routing (token t prefers expert t mod N): f_i = 1/N
+    # exactly, so the loss is alpha * sum_i P_i = alpha whatever P is
+    n, T, alpha = 8, 64, 0.01
+    logits = np.zeros((T, n))
+    # token t's own expert wins by a margin that grows with the expert index,
+    # so the average probabilities are far from uniform
+    logits[np.arange(T), np.arange(T) % n] = 0.5 + (np.arange(T) % n)
+    sel, _, _ = oracle.topk_select(logits, 1)
+    st = oracle.router_stats(logits, sel, alpha)
+    np.testing.assert_array_equal(st["frac"], np.full(n, 1.0 / n))
+    assert not np.allclose(st["prob"], 1.0 / n)
+    assert abs(st["aux_loss"] - alpha) <= 1e-15
+
+
+def test_stats_collapse_to_one_expert_gives_alpha_n():
+    # the favourite-expert failure: every token sends everything to expert 0
+    n, T, alpha = 8, 16, 0.01
+    logits = np.zeros((T, n))
+    logits[:, 0] = 60.0  # exp(-60) ~ 1e-26: P_0 = 1 to double precision
+    sel, _, _ = oracle.topk_select(logits, 1)
+    st = oracle.router_stats(logits, sel, alpha)
+    assert st["frac"][0] == 1.0 and st["frac"][1:].sum() == 0.0
+    assert abs(st["aux_loss"] - alpha * n) <= 1e-15 * n
+
+
+def test_stats_shares_sum_to_one_and_two_expert_softmax_is_logistic():
+    rng = np.random.default_rng(6)
+    logits = rng.standard_normal((50, 2)) * 3
+    sel, _, _ = oracle.topk_select(logits, 1)
+    st = oracle.router_stats(logits, sel, 0.01)
+    assert abs(st["frac"].sum() - 1.0) <= 1e-15 and abs(st["prob"].sum() - 1.0) <= 1e-15
+    # P_0 for two experts is the mean of the logistic function of the logit gap
+    gap = logits[:, 0] - logits[:, 1]
+    np.testing.assert_allclose(st["prob"][0], np.mean(1.0 / (1.0 + np.exp(-gap))), rtol=0, atol=1e-15)
+
+
+def test_stats_cauchy_schwarz_bound_when_shares_match():
+    # with f = P the loss is alpha * N * sum f^2 >= alpha (equality iff uniform):
+    # K = N makes f uniform, and with W_g = 0 P is uniform too
+    n = 6
+    logits = np.zeros((10, n))
+    sel, _, _ = oracle.topk_select(logits, n)
+    st = oracle.router_stats(logits, sel, 0.5)
+    assert abs(st["aux_loss"] - 0.5) <= 1e-15
