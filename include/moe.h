@@ -119,6 +119,31 @@ moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d
                            int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
                            moe_stream_t stream);
 
+/*
+ * moe_route_stats -- router statistics and the load-balancing loss of the
+ * Switch design described in Part 5 of "Mixture of Experts: Why Mixtral Only
+ * Wakes Up Two Specialists" ("The favourite expert problem", tool 2), for the
+ * top-K routing of moe_route.  x[T][d], Wg[d][n]: bf16; T >= 1.
+ *   frac[n]     fp32  share of the T*K assignments sent to each expert,
+ *                     counts[e] / (T*K) (sums to 1)
+ *   prob[n]     fp32  mean over the tokens of the router's full n-way softmax
+ *                     probability of each expert (sums to 1)
+ *   aux_loss[1] fp32  alpha * n * sum_e frac[e] * prob[e]; equals alpha when
+ *                     either share is uniform (1/n each)
+ * Each output is optional (NULL = not written); at least one must be given.
+ * The selection is the one moe_route makes (same kernels); sums over tokens
+ * run in a fixed order, so results are reproducible.  T == 0 or a NaN alpha
+ * -> MOE_ERR_INVALID_ARG.
+ */
+moe_status_t moe_route_stats(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n,
+                             int32_t K, float alpha, float* frac, float* prob, float* aux_loss,
+                             moe_stream_t stream);
+
+/* moe_route_stats_f32 -- moe_route_stats with fp32 x and Wg. */
+moe_status_t moe_route_stats_f32(const float* x, const float* Wg, int64_t T, int64_t d, int32_t n,
+                                 int32_t K, float alpha, float* frac, float* prob, float* aux_loss,
+                                 moe_stream_t stream);
+
 /* Bytes of library workspace a call of this shape needs on any supported
  * device (an upper bound: the prefill path's leftover-tile buffer scales with
  * the device's compute units per XCD); 0 on invalid shapes. */

@@ -17,9 +17,12 @@ from ._binding import (  # noqa: F401
     release,
     route,
     route_f32,
+    route_stats,
+    route_stats_f32,
     version,
     workspace_bytes,
 )
 
-__all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "workspace_bytes", "release",
+__all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
+           "workspace_bytes", "release",
            "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

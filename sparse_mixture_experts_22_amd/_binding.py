@@ -12,7 +12,8 @@ _LIB = None
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP",
           4: "MOE_ERR_NO_MEMORY"}
 
-EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32", "moe_workspace_bytes",
+EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32",
+           "moe_route_stats", "moe_route_stats_f32", "moe_workspace_bytes",
            "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
 
 
@@ -54,6 +55,11 @@ def lib() -> ctypes.CDLL:
     L.moe_route.restype = ctypes.c_int
     L.moe_route_f32.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     L.moe_route_f32.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    L.moe_route_stats.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp]
+    L.moe_route_stats.restype = ctypes.c_int
+    L.moe_route_stats_f32.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp]
+    L.moe_route_stats_f32.restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_release.argtypes = []
@@ -183,6 +189,36 @@ def route_f32(x, Wg, K, outputs=ROUTE_OUTPUTS, stream=None):
     """moe_route_f32 on fp32 x, Wg."""
     import torch
     return _route(lib().moe_route_f32, torch.float32, x, Wg, K, outputs, stream)
+
+
+def _route_stats(fn, dtype, x, Wg, K, alpha, outputs, stream):
+    import torch
+    _expect(x, dtype, "x", 2)
+    _expect(Wg, dtype, "Wg", 2)
+    T, d = x.shape
+    n = Wg.shape[1]
+    if Wg.shape[0] != d:
+        raise ValueError("Wg must be [d][n]")
+    shapes = {"frac": (n,), "prob": (n,), "aux_loss": (1,)}
+    out = {name: torch.empty(shapes[name], dtype=torch.float32, device=x.device) for name in outputs}
+    _check(fn(_ptr(x), _ptr(Wg), T, d, n, int(K), float(alpha), _ptr(out.get("frac")),
+              _ptr(out.get("prob")), _ptr(out.get("aux_loss")), _stream(stream)))
+    return out
+
+
+STATS_OUTPUTS = ("frac", "prob", "aux_loss")
+
+
+def route_stats(x, Wg, K, alpha=0.01, outputs=STATS_OUTPUTS, stream=None):
+    """moe_route_stats on bf16 x, Wg: dict of frac[n], prob[n], aux_loss[1] (fp32)."""
+    import torch
+    return _route_stats(lib().moe_route_stats, torch.bfloat16, x, Wg, K, alpha, outputs, stream)
+
+
+def route_stats_f32(x, Wg, K, alpha=0.01, outputs=STATS_OUTPUTS, stream=None):
+    """moe_route_stats_f32 on fp32 x, Wg."""
+    import torch
+    return _route_stats(lib().moe_route_stats_f32, torch.float32, x, Wg, K, alpha, outputs, stream)
 
 
 def workspace_bytes(T, d, f, n, K) -> int:

@@ -35,12 +35,12 @@ DeviceWorkspace g_ws[kMaxDevices];
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum class Path { kRouteOnly, kBf16, kF32 };
+enum class Path { kRouteOnly, kStats, kBf16, kF32 };
 
 struct Plan {
   size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
          perm_token = 0, slot_pos = 0;
-  size_t h = 0, o = 0, tail = 0, total = 0;
+  size_t h = 0, o = 0, tail = 0, probsum = 0, total = 0;
   bool skinny = false;
   int splits = 1;
 };
@@ -65,6 +65,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
   p.offsets = take((size_t)(n + 1) * 4);
   p.perm_token = take((size_t)TK * 4);
   p.slot_pos = take((size_t)TK * 4);
+  if (path == Path::kStats) p.probsum = take((size_t)nb * n * 4);
   if (path == Path::kBf16) {
     p.skinny = TK <= (int64_t)moe::kSkinnyMaxAvgRows * n;
     p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
@@ -291,6 +292,38 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   return MOE_OK;
 }
 
+template <bool BF16>
+moe_status_t route_stats_impl(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                              float alpha, float* frac, float* prob, float* aux_loss, hipStream_t stream) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, d, 1, n, K, false);
+  if (st != MOE_OK) return st;
+  if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
+  if (!frac && !prob && !aux_loss) return fail(MOE_ERR_INVALID_ARG, "at least one statistics output must be non-null");
+  if (!(alpha == alpha)) return fail(MOE_ERR_INVALID_ARG, "alpha must not be NaN");
+  if (T == 0) return fail(MOE_ERR_INVALID_ARG, "router statistics need T >= 1");
+  if (BF16) {
+    st = check_bf16(d, 0, false, {x, Wg});
+    if (st != MOE_OK) return st;
+  }
+  const Plan p = make_plan(T, d, 0, n, K, Path::kStats);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const moe::RouteBuffers r =
+      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  float* probsum = at<float>(ws, p.probsum);
+  if (BF16)
+    MOE_LAUNCH(moe::launch_route_stats_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
+                                            T, d, n, K, alpha, r, probsum, frac, prob, aux_loss, stream),
+               "router statistics launch");
+  else
+    MOE_LAUNCH(moe::launch_route_stats_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d,
+                                           n, K, alpha, r, probsum, frac, prob, aux_loss, stream),
+               "router statistics launch");
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,5 +434,18 @@ const char* moe_status_string(moe_status_t s) {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 const char* moe_version(void) { return "moe-mi355x 0.1.0 (gfx950)"; }
+
+moe_status_t moe_route_stats(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                             float alpha, float* frac, float* prob, float* aux_loss, moe_stream_t stream) {
+  return route_stats_impl<true>(x, Wg, T, d, n, K, alpha, frac, prob, aux_loss,
+                                reinterpret_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_route_stats_f32(const float* x, const float* Wg, int64_t T, int64_t d, int32_t n,
+                                 int32_t K, float alpha, float* frac, float* prob, float* aux_loss,
+                                 moe_stream_t stream) {
+  return route_stats_impl<false>(x, Wg, T, d, n, K, alpha, frac, prob, aux_loss,
+                                 reinterpret_cast<hipStream_t>(stream));
+}
 
 }  // extern "C"

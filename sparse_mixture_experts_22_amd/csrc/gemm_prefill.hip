@@ -54,7 +54,10 @@ namespace {
 constexpr int BM = kPrefillBM;  // 256 rows
 constexpr int BN = 256;         // LDS B-tile columns
 constexpr int BK = 32;
-constexpr int NGROUP = 4;       // column tiles per scheduling group
+#ifndef MOE_NGROUP
+#define MOE_NGROUP 4
+#endif
+constexpr int NGROUP = MOE_NGROUP;  // column tiles per scheduling group
 
 constexpr int kXcds = 8;          // the hardware hands workgroup i to XCD (i mod 8)
 constexpr int kMaxTailSplit = 8;  // k-pieces per leftover tile
@@ -394,8 +397,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   auto step = [&](int kt, auto par_c) {
     constexpr int par = decltype(par_c)::value;
     read_frags(kt, par, 1, fa1, fb1);
+#if MOE_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
     mfma_step(fa0, fb0);
     interleave();
+#if MOE_SETPRIO
+    fence();
+    __builtin_amdgcn_s_setprio(0);
+#endif
     if (b_loader)
       __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_B);
     else
@@ -408,8 +418,15 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
       issue_b(kt + SB, min(kt + SB, nk - 1));
     else if (par)
       issue_a((kt >> 1) + SA, min((kt >> 1) + SA, nks - 1));
+#if MOE_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
     mfma_step(fa1, fb1);
     interleave();
+#if MOE_SETPRIO
+    fence();
+    __builtin_amdgcn_s_setprio(0);
+#endif
   };
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, std::integral_constant<int, 0>{});

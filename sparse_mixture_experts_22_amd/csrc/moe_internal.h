@@ -53,6 +53,16 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
                              hipEvent_t after_router = nullptr);
 hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
                             const RouteBuffers& rb, hipStream_t s);
+// Router statistics: frac[e] = counts[e]/(T*K), prob[e] = mean over tokens of
+// the full n-way softmax, aux_loss = alpha*n*sum_e frac[e]*prob[e] (each
+// output optional).  Fills topk_idx, topk_w and hist of rb; probsum holds
+// [blocks][n] floats.
+hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                                   int K, float alpha, const RouteBuffers& rb, float* probsum,
+                                   float* frac, float* prob, float* aux_loss, hipStream_t s);
+hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
+                                  float alpha, const RouteBuffers& rb, float* probsum, float* frac,
+                                  float* prob, float* aux_loss, hipStream_t s);
 // Scan + scatter from topk_idx and hist (used after a multi-block router).
 hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s);
 

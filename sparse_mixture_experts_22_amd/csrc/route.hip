@@ -80,9 +80,10 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
                                int* __restrict__ hist, bool fused, int* __restrict__ counts,
                                int* __restrict__ offsets, int* __restrict__ perm_token,
                                int* __restrict__ slot_pos, int* sel_s, uint32_t* mask_s,
-                               int* hist_s) {
+                               int* hist_s, float* __restrict__ probsum) {
   const int tid = threadIdx.x;
   const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
+  __shared__ float tmax_s[32], tsum_s[32];
   for (int e = tid; e < n; e += blockDim.x) {
     hist_s[e] = 0;
     mask_s[e] = 0u;
@@ -103,8 +104,26 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
         atomicOr(&mask_s[id[j]], 1u << tid);   // token tid chose expert id[j]
       }
     }
+    if (probsum != nullptr) {
+      // full n-way softmax of the token (router statistics): max, then the
+      // sum of exponentials in expert order
+      float mx = -INFINITY;
+      for (int e = 0; e < n; ++e) mx = fmaxf(mx, logits_s[tid * ld + e]);
+      float sm = 0.0f;
+      for (int e = 0; e < n; ++e) sm += expf(logits_s[tid * ld + e] - mx);
+      tmax_s[tid] = mx;
+      tsum_s[tid] = sm;
+    }
   }
   __syncthreads();
+  if (probsum != nullptr) {
+    // this block's sum over its tokens (in token order) of each expert's probability
+    for (int e = tid; e < n; e += blockDim.x) {
+      float acc = 0.0f;
+      for (int i = 0; i < cnt; ++i) acc += expf(logits_s[i * ld + e] - tmax_s[i]) / tsum_s[i];
+      probsum[(int64_t)blockIdx.x * n + e] = acc;
+    }
+  }
   if (!fused) {
     for (int e = tid; e < n; e += blockDim.x) hist[(int64_t)blockIdx.x * n + e] = hist_s[e];
     return;
@@ -165,7 +184,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
     int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm_token,
-    int* __restrict__ slot_pos) {
+    int* __restrict__ slot_pos, float* __restrict__ probsum) {
   constexpr int BT = 16 * TT;
   constexpr int NP = 16 * NE;
   constexpr int LDL = NP + 1;
@@ -251,7 +270,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
   }
   __syncthreads();
   route_epilogue(logits_s, LDL, BT, t0, T, n, K, topk_idx, topk_w, hist, fused != 0, counts, offsets,
-                 perm_token, slot_pos, sel_s, mask_s, hist_s);
+                 perm_token, slot_pos, sel_s, mask_s, hist_s, probsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -261,7 +280,8 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
                                                          int64_t d, int n, int K, int BT,
                                                          int* __restrict__ topk_idx,
                                                          float* __restrict__ topk_w,
-                                                         int* __restrict__ hist) {
+                                                         int* __restrict__ hist,
+                                                         float* __restrict__ probsum) {
   __shared__ float logits_s[32 * (kMaxN + 1)];
   __shared__ int sel_s[32 * kMaxK];
   __shared__ uint32_t mask_s[kMaxN];
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
   }
   __syncthreads();
   route_epilogue(logits_s, ld, BT, t0, T, n, K, topk_idx, topk_w, hist, false, nullptr, nullptr,
-                 nullptr, nullptr, sel_s, mask_s, hist_s);
+                 nullptr, nullptr, sel_s, mask_s, hist_s, probsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -376,12 +396,61 @@ namespace {
 
 template <int NE, int TT, int W>
 void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t d, int n, int K,
-                     const RouteBuffers& rb, bool fused, hipStream_t s) {
+                     const RouteBuffers& rb, bool fused, float* probsum, hipStream_t s) {
   constexpr int BT = 16 * TT;
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
                      T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
-                     rb.offsets, rb.perm_token, rb.slot_pos);
+                     rb.offsets, rb.perm_token, rb.slot_pos, probsum);
+}
+
+// Router statistics from the per-block histograms and probability sums (one
+// workgroup, thread e per expert; blocks summed in order in double):
+//   frac[e] = counts[e] / (T*K), prob[e] = sum_t p_t[e] / T,
+//   aux_loss = alpha * n * sum_e frac[e] * prob[e]   (summed in expert order).
+__global__ __launch_bounds__(256) void route_stats_kernel(const int* __restrict__ hist,
+                                                          const float* __restrict__ probsum, int nb,
+                                                          int64_t T, int n, int K, float alpha,
+                                                          float* __restrict__ frac,
+                                                          float* __restrict__ prob,
+                                                          float* __restrict__ aux_loss) {
+  __shared__ double fp_s[kMaxN];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n; e += blockDim.x) {
+    long long c = 0;
+    double p = 0.0;
+    for (int b = 0; b < nb; ++b) {
+      c += hist[(int64_t)b * n + e];
+      p += (double)probsum[(int64_t)b * n + e];
+    }
+    const double fe = (double)c / ((double)T * K);
+    const double pe = p / (double)T;
+    if (frac != nullptr) frac[e] = (float)fe;
+    if (prob != nullptr) prob[e] = (float)pe;
+    fp_s[e] = fe * pe;
+  }
+  __syncthreads();
+  if (tid == 0 && aux_loss != nullptr) {
+    double acc = 0.0;
+    for (int e = 0; e < n; ++e) acc += fp_s[e];
+    aux_loss[0] = (float)((double)alpha * n * acc);
+  }
+}
+
+// Picks the router configuration for the expert count (WgT rows padded to 16).
+void launch_router_bf16(const uint16_t* x, int64_t T, int64_t d, int n, int K, const RouteBuffers& rb,
+                        bool fused, float* probsum, hipStream_t s) {
+  const int ne = route_padded_experts(n) / 16;
+  if (ne <= 1)
+    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+  else if (ne <= 2)
+    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+  else if (ne <= 4)
+    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+  else if (ne <= 8)
+    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+  else
+    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
 }
 
 }  // namespace
@@ -400,21 +469,29 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
   const int BT = route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   const bool fused = nb == 1;
-  const int ne = NP / 16;
-  if (ne <= 1)
-    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, s);
-  else if (ne <= 2)
-    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
-  else if (ne <= 4)
-    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
-  else if (ne <= 8)
-    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, s);
-  else
-    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, s);
+  launch_router_bf16(x, T, d, n, K, rb, fused, nullptr, s);
   e = hipGetLastError();
   if (e == hipSuccess && after_router != nullptr) e = hipEventRecord(after_router, s);
   if (e != hipSuccess || fused) return e;
   return launch_dispatch(T, n, K, rb, s);
+}
+
+hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                                   int K, float alpha, const RouteBuffers& rb, float* probsum,
+                                   float* frac, float* prob, float* aux_loss, hipStream_t s) {
+  const int NP = route_padded_experts(n);
+  hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
+                     dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_router_bf16(x, T, d, n, K, rb, false, probsum, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int BT = route_block_tokens(n);
+  const int nb = (int)((T + BT - 1) / BT);
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(256), 0, s, rb.hist, probsum, nb, T, n, K, alpha,
+                     frac, prob, aux_loss);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
@@ -422,10 +499,24 @@ hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t 
   const int BT = route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)nb), dim3(256), 0, s, x, Wg, T, d, n, K, BT,
-                     rb.topk_idx, rb.topk_w, rb.hist);
+                     rb.topk_idx, rb.topk_w, rb.hist, (float*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_dispatch(T, n, K, rb, s);
+}
+
+hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
+                                  float alpha, const RouteBuffers& rb, float* probsum, float* frac,
+                                  float* prob, float* aux_loss, hipStream_t s) {
+  const int BT = route_block_tokens(n);
+  const int64_t nb = (T + BT - 1) / BT;
+  hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)nb), dim3(256), 0, s, x, Wg, T, d, n, K, BT,
+                     rb.topk_idx, rb.topk_w, rb.hist, probsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(256), 0, s, rb.hist, probsum, (int)nb, T, n, K,
+                     alpha, frac, prob, aux_loss);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s) {
