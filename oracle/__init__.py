@@ -7,9 +7,12 @@ no code with it.
 """
 from .moe_oracle import (  # noqa: F401
     brute_force_topk,
+    capacity_dispatch,
     dispatch,
+    expert_capacity,
     expert_swiglu,
     forward,
+    forward_capacity,
     forward_mask_form,
     forward_with_selection,
     full_softmax,

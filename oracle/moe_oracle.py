@@ -26,6 +26,12 @@ Readings where the pages leave a step open (each also listed in the design notes
   * Expert indices are 0-based (the equation sums i = 0..n-1); the walk-through
     counts from 1, so its "expert 3 and expert 7" are indices 2 and 6 here.
   * y excludes the residual add that the surrounding block performs.
+  * Router statistics (Part 5): f_i counts the T*K assignments once each,
+    f_i = counts_i / (T*K), so both shares are 1/N when balanced.
+  * Capacity (Part 5, "What happens when an expert is full"): with K
+    assignments per token C = ceil(cf * T * K / n); each expert keeps its first
+    C assignments in token order, dropped ones add nothing and the kept
+    weights are not renormalised.
 
 Pins (tests/test_oracle_pins.py) tie every function to something other than
 itself: the walk-through's printed weights, brute force over all expert
@@ -36,6 +42,7 @@ metamorphic invariants.  No function here is "parity unpinned".
 from __future__ import annotations
 
 import itertools
+import math
 from typing import Callable, Union
 
 import numpy as np
@@ -190,6 +197,71 @@ def dispatch(sel: np.ndarray, n: int):
 
 
 # --------------------------------------------------------------- experts ---
+
+def expert_capacity(T: int, n: int, K: int, capacity_factor: float) -> int:
+    """Expert capacity of the Switch design (Part 5 of the explainer, "What
+    happens when an expert is full"): the batch's tokens divided by the number
+    of experts, times a capacity factor.  With K assignments per token the
+    work to share is T*K, so C = ceil(capacity_factor * T * K / n)."""
+    return int(math.ceil(capacity_factor * T * K / n))
+
+
+def capacity_dispatch(sel: np.ndarray, n: int, cap: int):
+    """Dispatch with a capacity: walking the tokens in order, each expert
+    accepts assignments until it holds `cap`; later ones overflow and are
+    dropped (no row, no computation).
+      kept[t][k]     whether assignment (t, k) got a row
+      counts[e]      kept assignments of expert e (<= cap)
+      offsets, perm_token over the kept rows (expert-contiguous, ascending t)
+      slot_pos[t][k] row of a kept assignment, -1 for a dropped one
+    """
+    sel = np.asarray(sel, dtype=np.int64)
+    T, K = sel.shape
+    load = np.zeros(n, dtype=np.int64)
+    kept = np.zeros((T, K), dtype=bool)
+    for t in range(T):
+        for k in range(K):
+            e = sel[t, k]
+            if load[e] < cap:
+                kept[t, k] = True
+                load[e] += 1
+    counts = load
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm_token = np.empty(int(offsets[n]), dtype=np.int64)
+    slot_pos = np.full((T, K), -1, dtype=np.int64)
+    nxt = offsets[:n].copy()
+    for t in range(T):
+        for k in range(K):
+            if kept[t, k]:
+                e = sel[t, k]
+                perm_token[nxt[e]] = t
+                slot_pos[t, k] = nxt[e]
+                nxt[e] += 1
+    return dict(kept=kept, counts=counts, offsets=offsets, perm_token=perm_token, slot_pos=slot_pos)
+
+
+def forward_capacity(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter, sel: np.ndarray,
+                     cap: int) -> np.ndarray:
+    """The layer with dropped assignments: a dropped (t, k) computes nothing and
+    adds nothing (the token goes on through the residual connection); the kept
+    terms keep the softmax weights of all K selected logits (no renormalisation)."""
+    x = _f64(x)
+    logits = router_logits(x, Wg)
+    sel = np.asarray(sel, dtype=np.int64)
+    w = gate_weights(logits, sel)
+    kept = capacity_dispatch(sel, _f64(Wg).shape[1], cap)["kept"]
+    T = x.shape[0]
+    y = np.zeros((T, x.shape[1]))
+    for e in range(_f64(Wg).shape[1]):
+        hit = (sel == e) & kept
+        rows = np.nonzero(hit.any(axis=1))[0]
+        if rows.size == 0:
+            continue
+        out = expert_swiglu(x[rows], _expert(W1, e), _expert(W3, e), _expert(W2, e))
+        y[rows] += (w[rows] * hit[rows]).sum(axis=1)[:, None] * out
+    return y
+
 
 def sigmoid(z) -> np.ndarray:
     z = _f64(z)

@@ -427,3 +427,76 @@ def test_stats_cauchy_schwarz_bound_when_shares_match():
     sel, _, _ = oracle.topk_select(logits, n)
     st = oracle.router_stats(logits, sel, 0.5)
     assert abs(st["aux_loss"] - 0.5) <= 1e-15
+
+
+# -------------------------------------------------------- capacity dispatch
+# Part 5 of the explainer ("What happens when an expert is full"): capacity =
+# tokens / experts * capacity factor; overflowing work is dropped and the
+# token passes on through the residual connection.
+
+def test_capacity_formula():
+    assert oracle.expert_capacity(8192, 8, 2, 1.0) == 8192 * 2 // 8
+    assert oracle.expert_capacity(8192, 8, 2, 1.25) == 2560
+    assert oracle.expert_capacity(8192, 64, 2, 1.0) == 256
+    assert oracle.expert_capacity(100, 8, 1, 1.0) == 13      # ceil(12.5)
+    assert oracle.expert_capacity(10, 8, 2, 1e-9) == 1
+
+
+def test_capacity_hand_example():
+    # expert loads in token order: e0 <- t0, t1, (t2, t3, t4 overflow at C = 2);
+    # e1 <- t0, t2, (t3 overflows); e2 <- t1, t4
+    sel = np.array([[0, 1], [0, 2], [0, 1], [1, 0], [2, 0]])
+    d = oracle.capacity_dispatch(sel, 3, 2)
+    np.testing.assert_array_equal(d["kept"], [[1, 1], [1, 1], [0, 1], [0, 0], [1, 0]])
+    np.testing.assert_array_equal(d["counts"], [2, 2, 2])
+    np.testing.assert_array_equal(d["offsets"], [0, 2, 4, 6])
+    np.testing.assert_array_equal(d["perm_token"], [0, 1, 0, 2, 1, 4])
+    np.testing.assert_array_equal(d["slot_pos"], [[0, 2], [1, 4], [-1, 3], [-1, -1], [5, -1]])
+
+
+def test_capacity_drops_latest_tokens_of_overfull_experts_only():
+    rng = np.random.default_rng(11)
+    T, n, K = 400, 6, 2
+    sel = np.stack([rng.choice(n, size=K, replace=False, p=[0.4, 0.2, 0.1, 0.1, 0.1, 0.1]) for _ in range(T)])
+    cap = 90
+    d = oracle.capacity_dispatch(sel, n, cap)
+    full = oracle.dispatch(sel, n)
+    np.testing.assert_array_equal(d["counts"], np.minimum(full[0], cap))
+    for e in range(n):
+        toks = np.nonzero((sel == e).any(axis=1))[0]          # token order
+        kept_toks = np.nonzero(((sel == e) & d["kept"]).any(axis=1))[0]
+        np.testing.assert_array_equal(kept_toks, toks[:cap])
+    # kept rows point back to their tokens
+    for t in range(T):
+        for k in range(K):
+            if d["kept"][t, k]:
+                assert d["perm_token"][d["slot_pos"][t, k]] == t
+
+
+def test_capacity_without_overflow_is_dropless():
+    x, Wg, W1, W3, W2 = _small(T=60, n=6)
+    r = oracle.route(x, Wg, 2)
+    d = oracle.capacity_dispatch(r["sel"], 6, 60 * 2)
+    full = oracle.dispatch(r["sel"], 6)
+    for a, b in zip((d["counts"], d["offsets"], d["perm_token"], d["slot_pos"]), full):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(oracle.forward_capacity(x, Wg, W1, W3, W2, r["sel"], 120),
+                                  oracle.forward(x, Wg, W1, W3, W2, 2))
+
+
+def test_capacity_forward_keeps_only_kept_terms():
+    x, Wg, W1, W3, W2 = _small(T=40, n=4)
+    r = oracle.route(x, Wg, 2)
+    cap = 12
+    y = oracle.forward_capacity(x, Wg, W1, W3, W2, r["sel"], cap)
+    kept = oracle.capacity_dispatch(r["sel"], 4, cap)["kept"]
+    assert (~kept).any(axis=1).any() and (~kept).all(axis=1).any()  # partial and total drops occur
+    for t in range(40):
+        ref = np.zeros(x.shape[1])
+        for k in range(2):
+            if kept[t, k]:
+                e = r["sel"][t, k]
+                ref += r["w"][t, k] * oracle.expert_swiglu(x[t:t + 1], W1[e], W3[e], W2[e])[0]
+        np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-13)
+        if not kept[t].any():
+            assert (y[t] == 0).all()
