@@ -144,6 +144,38 @@ moe_status_t moe_route_stats_f32(const float* x, const float* Wg, int64_t T, int
                                  int32_t K, float alpha, float* frac, float* prob, float* aux_loss,
                                  moe_stream_t stream);
 
+/*
+ * Capacity-limited routing: the expert capacity of the Switch design described
+ * in Part 5 of "Mixture of Experts: Why Mixtral Only Wakes Up Two Specialists"
+ * ("What happens when an expert is full"): the tokens of the batch divided by
+ * the number of experts, times a capacity factor; with K assignments per token
+ * it is C = ceil(capacity_factor * T * K / n).  Each expert keeps its first C
+ * assignments in token order; the others are dropped: they get no row, no
+ * computation and contribute nothing to y (the token passes on through the
+ * caller's residual add; the kept gate weights are not renormalised, so a
+ * token whose K assignments are all dropped gets y = 0).
+ *   moe_expert_capacity  returns C (0 if capacity_factor is not positive and
+ *                        finite or C does not fit an int32).
+ *   moe_route_capacity   moe_route with the limit: counts[e] = kept
+ *                        assignments (<= C), offsets their exclusive scan,
+ *                        perm_token[0 .. offsets[n]) the kept rows, and
+ *                        slot_pos[t][k] = -1 for a dropped assignment.
+ *                        topk_idx / topk_w are those of moe_route.
+ *   moe_forward_capacity moe_forward with the limit.
+ * A capacity of at least the largest expert load gives moe_route / moe_forward
+ * exactly.  Invalid capacity_factor -> MOE_ERR_INVALID_ARG.
+ */
+int64_t moe_expert_capacity(int64_t T, int32_t n, int32_t K, double capacity_factor);
+
+moe_status_t moe_route_capacity(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n,
+                                int32_t K, double capacity_factor, int32_t* topk_idx, float* topk_w,
+                                int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                                int32_t* slot_pos, moe_stream_t stream);
+
+moe_status_t moe_forward_capacity(const void* x, const void* Wg, const void* W1, const void* W3,
+                                  const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                                  int32_t K, double capacity_factor, float* y, moe_stream_t stream);
+
 /* Bytes of library workspace a call of this shape needs on any supported
  * device (an upper bound: the prefill path's leftover-tile buffer scales with
  * the device's compute units per XCD); 0 on invalid shapes. */

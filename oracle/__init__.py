@@ -13,6 +13,7 @@ from .moe_oracle import (  # noqa: F401
     expert_swiglu,
     forward,
     forward_capacity,
+    forward_kept,
     forward_mask_form,
     forward_with_selection,
     full_softmax,

@@ -246,11 +246,18 @@ def forward_capacity(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGet
     """The layer with dropped assignments: a dropped (t, k) computes nothing and
     adds nothing (the token goes on through the residual connection); the kept
     terms keep the softmax weights of all K selected logits (no renormalisation)."""
+    kept = capacity_dispatch(sel, _f64(Wg).shape[1], cap)["kept"]
+    return forward_kept(x, Wg, W1, W3, W2, sel, kept)
+
+
+def forward_kept(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter, sel: np.ndarray,
+                 kept: np.ndarray) -> np.ndarray:
+    """forward_capacity for a given kept mask (rows of a larger batch can be
+    evaluated with the mask the whole batch's dispatch produced)."""
     x = _f64(x)
     logits = router_logits(x, Wg)
     sel = np.asarray(sel, dtype=np.int64)
     w = gate_weights(logits, sel)
-    kept = capacity_dispatch(sel, _f64(Wg).shape[1], cap)["kept"]
     T = x.shape[0]
     y = np.zeros((T, x.shape[1]))
     for e in range(_f64(Wg).shape[1]):

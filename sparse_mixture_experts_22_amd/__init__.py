@@ -8,7 +8,9 @@ built, every call raises; there is no CPU fallback.
 from ._binding import (  # noqa: F401
     MoEError,
     STATUS,
+    expert_capacity,
     forward,
+    forward_capacity,
     forward_f32,
     forward_traced,
     last_error,
@@ -16,6 +18,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     release,
     route,
+    route_capacity,
     route_f32,
     route_stats,
     route_stats_f32,
@@ -24,5 +27,5 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
-           "workspace_bytes", "release",
+           "expert_capacity", "route_capacity", "forward_capacity", "workspace_bytes", "release",
            "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

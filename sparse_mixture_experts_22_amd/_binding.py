@@ -13,7 +13,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
           4: "MOE_ERR_NO_MEMORY"}
 
 EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32",
-           "moe_route_stats", "moe_route_stats_f32", "moe_workspace_bytes",
+           "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
+           "moe_forward_capacity", "moe_workspace_bytes",
            "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
 
 
@@ -60,6 +61,13 @@ def lib() -> ctypes.CDLL:
     L.moe_route_stats.restype = ctypes.c_int
     L.moe_route_stats_f32.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp]
     L.moe_route_stats_f32.restype = ctypes.c_int
+    f64 = ctypes.c_double
+    L.moe_expert_capacity.argtypes = [i64, i32, i32, f64]
+    L.moe_expert_capacity.restype = i64
+    L.moe_route_capacity.argtypes = [vp, vp, i64, i64, i32, i32, f64, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route_capacity.restype = ctypes.c_int
+    L.moe_forward_capacity.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f64, vp, vp]
+    L.moe_forward_capacity.restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_release.argtypes = []
@@ -111,7 +119,7 @@ def _expect(t, dtype, name, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _forward(fn, dtype, x, Wg, W1, W3, W2, K, y, stream, extra=()):
+def _forward(fn, dtype, x, Wg, W1, W3, W2, K, y, stream, extra=(), mid=()):
     import torch
     for t, name, nd in ((x, "x", 2), (Wg, "Wg", 2), (W1, "W1", 3), (W3, "W3", 3), (W2, "W2", 3)):
         _expect(t, dtype, name, nd)
@@ -126,7 +134,7 @@ def _forward(fn, dtype, x, Wg, W1, W3, W2, K, y, stream, extra=()):
         _expect(y, torch.float32, "y", 2)
         if tuple(y.shape) != (T, d):
             raise ValueError("y must be [T][d]")
-    _check(fn(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), T, d, f, n, int(K), _ptr(y),
+    _check(fn(_ptr(x), _ptr(Wg), _ptr(W1), _ptr(W3), _ptr(W2), T, d, f, n, int(K), *mid, _ptr(y),
               _stream(stream), *extra))
     return y
 
@@ -154,7 +162,7 @@ def forward_f32(x, Wg, W1, W3, W2, K, y=None, stream=None):
     return _forward(lib().moe_forward_f32, torch.float32, x, Wg, W1, W3, W2, K, y, stream)
 
 
-def _route(fn, dtype, x, Wg, K, outputs, stream):
+def _route(fn, dtype, x, Wg, K, outputs, stream, mid=()):
     import torch
     _expect(x, dtype, "x", 2)
     _expect(Wg, dtype, "Wg", 2)
@@ -170,7 +178,7 @@ def _route(fn, dtype, x, Wg, K, outputs, stream):
     for name in outputs:
         shp, dt = shapes[name]
         out[name] = torch.empty(shp, dtype=dt, device=dev)
-    _check(fn(_ptr(x), _ptr(Wg), T, d, n, int(K), _ptr(out.get("topk_idx")),
+    _check(fn(_ptr(x), _ptr(Wg), T, d, n, int(K), *mid, _ptr(out.get("topk_idx")),
               _ptr(out.get("topk_w")), _ptr(out.get("counts")), _ptr(out.get("offsets")),
               _ptr(out.get("perm_token")), _ptr(out.get("slot_pos")), _stream(stream)))
     return out
@@ -219,6 +227,26 @@ def route_stats_f32(x, Wg, K, alpha=0.01, outputs=STATS_OUTPUTS, stream=None):
     """moe_route_stats_f32 on fp32 x, Wg."""
     import torch
     return _route_stats(lib().moe_route_stats_f32, torch.float32, x, Wg, K, alpha, outputs, stream)
+
+
+def expert_capacity(T, n, K, capacity_factor) -> int:
+    """moe_expert_capacity: ceil(capacity_factor * T * K / n) (0 if invalid)."""
+    return int(lib().moe_expert_capacity(int(T), int(n), int(K), float(capacity_factor)))
+
+
+def route_capacity(x, Wg, K, capacity_factor, outputs=None, stream=None):
+    """moe_route_capacity on bf16 x, Wg: routing with each expert keeping at most
+    expert_capacity(...) assignments (slot_pos -1 marks a dropped one)."""
+    import torch
+    return _route(lib().moe_route_capacity, torch.bfloat16, x, Wg, K,
+                  ROUTE_OUTPUTS if outputs is None else outputs, stream, mid=(float(capacity_factor),))
+
+
+def forward_capacity(x, Wg, W1, W3, W2, K, capacity_factor, y=None, stream=None):
+    """moe_forward_capacity: moe_forward with dropped assignments past each expert's capacity."""
+    import torch
+    return _forward(lib().moe_forward_capacity, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream,
+                    mid=(float(capacity_factor),))
 
 
 def workspace_bytes(T, d, f, n, K) -> int:

@@ -11,6 +11,8 @@
 #include <mutex>
 #include <string>
 
+#include <cmath>
+
 #include "moe.h"
 #include "moe_internal.h"
 
@@ -193,7 +195,7 @@ moe::RouteBuffers route_buffers(char* ws, const Plan& p, const RouteOut& user) {
 
 template <bool BF16>
 moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
-                        const RouteOut& user, hipStream_t stream) {
+                        const RouteOut& user, hipStream_t stream, int cap = INT32_MAX) {
   moe_status_t st = check_shape(T, d, 1, n, K, false);
   if (st != MOE_OK) return st;
   if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
@@ -212,7 +214,7 @@ moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int
   const moe::RouteBuffers r = route_buffers(ws, p, user);
   if (BF16)
     MOE_LAUNCH(moe::launch_route_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
-                                      T, d, n, K, r, stream),
+                                      T, d, n, K, r, stream, nullptr, cap),
                "routing kernel launch");
   else
     MOE_LAUNCH(moe::launch_route_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d, n,
@@ -234,7 +236,7 @@ namespace {
 
 moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,
                           int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
-                          hipStream_t stream, void* const* ev) {
+                          hipStream_t stream, void* const* ev, int cap = INT32_MAX) {
   g_last_error.clear();
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
@@ -264,7 +266,7 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   const int64_t TK = T * K;
   MOE_LAUNCH(mark(0), "hipEventRecord");
   MOE_LAUNCH(moe::launch_route_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r, stream,
-                                    ev ? static_cast<hipEvent_t>(ev[1]) : nullptr),
+                                    ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, cap),
              "routing kernel launch");
   MOE_LAUNCH(mark(2), "hipEventRecord");
   const auto* w1 = static_cast<const uint16_t*>(W1);
@@ -322,6 +324,15 @@ moe_status_t route_stats_impl(const void* x, const void* Wg, int64_t T, int64_t 
                                            n, K, alpha, r, probsum, frac, prob, aux_loss, stream),
                "router statistics launch");
   return MOE_OK;
+}
+
+// Expert capacity ceil(cf * T * K / n), or -1 if cf is not a positive finite
+// number or the capacity does not fit an int.
+int64_t capacity_of(int64_t T, int32_t n, int32_t K, double cf) {
+  if (!(cf > 0.0) || !std::isfinite(cf) || n < 1 || K < 1 || T < 0) return -1;
+  const double c = std::ceil(cf * (double)T * (double)K / (double)n);
+  if (c > (double)INT32_MAX) return -1;
+  return (int64_t)c;
 }
 
 }  // namespace
@@ -446,6 +457,37 @@ moe_status_t moe_route_stats_f32(const float* x, const float* Wg, int64_t T, int
                                  moe_stream_t stream) {
   return route_stats_impl<false>(x, Wg, T, d, n, K, alpha, frac, prob, aux_loss,
                                  reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t moe_expert_capacity(int64_t T, int32_t n, int32_t K, double capacity_factor) {
+  const int64_t c = capacity_of(T, n, K, capacity_factor);
+  return c < 0 ? 0 : c;
+}
+
+moe_status_t moe_forward_capacity(const void* x, const void* Wg, const void* W1, const void* W3,
+                                  const void* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
+                                  double capacity_factor, float* y, moe_stream_t stream) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, d, f, n, K, true);
+  if (st != MOE_OK) return st;
+  const int64_t cap = capacity_of(T, n, K, capacity_factor);
+  if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be positive and finite");
+  return forward_bf16(x, Wg, W1, W3, W2, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream), nullptr,
+                      (int)cap);
+}
+
+moe_status_t moe_route_capacity(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n, int32_t K,
+                                double capacity_factor, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* perm_token, int32_t* slot_pos,
+                                moe_stream_t stream) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, d, 1, n, K, false);
+  if (st != MOE_OK) return st;
+  const int64_t cap = capacity_of(T, n, K, capacity_factor);
+  if (cap < 0) return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be positive and finite");
+  return route_impl<true>(x, Wg, T, d, n, K,
+                          RouteOut{topk_idx, topk_w, counts, offsets, perm_token, slot_pos},
+                          reinterpret_cast<hipStream_t>(stream), (int)cap);
 }
 
 }  // extern "C"

@@ -27,8 +27,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t t = idx / dv;
   const int64_t c = (idx % dv) * VEC;
   float acc[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) acc[j] = 0.0f;
   for (int k = 0; k < K; ++k) {
-    const int64_t pos = min<int64_t>(max(slot_pos[t * K + k], 0), TK - 1);
+    const int sp = slot_pos[t * K + k];
+    if (sp < 0) continue;  // an assignment dropped by a full expert contributes nothing
+    const int64_t pos = min<int64_t>(sp, TK - 1);
     const float w = topk_w[t * K + k];
     float v[VEC];
     if (VEC == 4) {
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int j = 0; j < VEC; ++j) v[j] += os[j];
     }
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) acc[j] = (k == 0) ? w * v[j] : acc[j] + w * v[j];
+    for (int j = 0; j < VEC; ++j) acc[j] = acc[j] + w * v[j];
   }
   if (VEC == 4) {
     *reinterpret_cast<float4*>(y + t * d + c) = make_float4(acc[0], acc[1 % VEC], acc[2 % VEC], acc[3 % VEC]);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+
 namespace moe {
 
 constexpr int kMaxN = 256;  // experts per layer
@@ -48,9 +50,11 @@ constexpr int kSkinnyDownSplits = 4;
 // ---------------------------------------------------------------- routing
 // Router + top-K + softmax + dispatch; fills every RouteBuffers output.
 // `after_router` (optional) is recorded between the router and the dispatch.
+// `cap`: each expert keeps its first `cap` assignments in token order, the
+// rest get slot_pos -1 and no row (counts/offsets/perm_token cover the kept).
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
                              int K, const RouteBuffers& rb, hipStream_t s,
-                             hipEvent_t after_router = nullptr);
+                             hipEvent_t after_router = nullptr, int cap = INT32_MAX);
 hipError_t launch_route_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
                             const RouteBuffers& rb, hipStream_t s);
 // Router statistics: frac[e] = counts[e]/(T*K), prob[e] = mean over tokens of
@@ -64,7 +68,8 @@ hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, in
                                   float alpha, const RouteBuffers& rb, float* probsum, float* frac,
                                   float* prob, float* aux_loss, hipStream_t s);
 // Scan + scatter from topk_idx and hist (used after a multi-block router).
-hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s);
+hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s,
+                           int cap = INT32_MAX);
 
 // ------------------------------------------------------ expert projections
 // Gate/up: h[p][:] = SiLU(x[perm_token[p]] W1_e) * (x[perm_token[p]] W3_e), bf16 out.

@@ -80,7 +80,7 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
                                int* __restrict__ hist, bool fused, int* __restrict__ counts,
                                int* __restrict__ offsets, int* __restrict__ perm_token,
                                int* __restrict__ slot_pos, int* sel_s, uint32_t* mask_s,
-                               int* hist_s, float* __restrict__ probsum) {
+                               int* hist_s, float* __restrict__ probsum, int cap) {
   const int tid = threadIdx.x;
   const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
   __shared__ float tmax_s[32], tsum_s[32];
@@ -128,26 +128,31 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
     for (int e = tid; e < n; e += blockDim.x) hist[(int64_t)blockIdx.x * n + e] = hist_s[e];
     return;
   }
-  // single routing block: offsets = exclusive scan of the block histogram
+  // single routing block: offsets = exclusive scan of the block histogram,
+  // each expert keeping at most `cap` assignments (the earliest tokens)
   __shared__ int base_s[kMaxN + 1];
   if (tid == 0) {
     int run = 0;
     for (int e = 0; e < n; ++e) {
       base_s[e] = run;
-      run += hist_s[e];
+      run += min(hist_s[e], cap);
     }
     base_s[n] = run;
   }
   __syncthreads();
   for (int e = tid; e <= n; e += blockDim.x) {
     offsets[e] = base_s[e];
-    if (e < n) counts[e] = hist_s[e];
+    if (e < n) counts[e] = min(hist_s[e], cap);
   }
   if (tid < cnt) {
     for (int j = 0; j < K; ++j) {
       const int e = sel_s[tid * K + j];
-      const int pos = base_s[e] + __popc(mask_s[e] & ((1u << tid) - 1u));
-      perm_token[pos] = (int)(t0 + tid);
+      const int rank = __popc(mask_s[e] & ((1u << tid) - 1u));  // earlier tokens of e
+      int pos = -1;
+      if (rank < cap) {
+        pos = base_s[e] + rank;
+        perm_token[pos] = (int)(t0 + tid);
+      }
       slot_pos[(t0 + tid) * K + j] = pos;
     }
   }
@@ -184,7 +189,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
     int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm_token,
-    int* __restrict__ slot_pos, float* __restrict__ probsum) {
+    int* __restrict__ slot_pos, float* __restrict__ probsum, int cap) {
   constexpr int BT = 16 * TT;
   constexpr int NP = 16 * NE;
   constexpr int LDL = NP + 1;
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
   }
   __syncthreads();
   route_epilogue(logits_s, LDL, BT, t0, T, n, K, topk_idx, topk_w, hist, fused != 0, counts, offsets,
-                 perm_token, slot_pos, sel_s, mask_s, hist_s, probsum);
+                 perm_token, slot_pos, sel_s, mask_s, hist_s, probsum, cap);
 }
 
 // ---------------------------------------------------------------------------
@@ -301,14 +306,17 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
   }
   __syncthreads();
   route_epilogue(logits_s, ld, BT, t0, T, n, K, topk_idx, topk_w, hist, false, nullptr, nullptr,
-                 nullptr, nullptr, sel_s, mask_s, hist_s, probsum);
+                 nullptr, nullptr, sel_s, mask_s, hist_s, probsum, INT32_MAX);
 }
 
 // ---------------------------------------------------------------------------
 // Scan over the block histograms hist[nb][n] (one workgroup of 1024 threads).
-// Thread (e, p) owns a contiguous range of blocks for expert e.  Writes
-// bases[b][e] = offsets[e] + sum_{b' < b} hist[b'][e], counts and offsets.
-__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist, int nb, int n,
+// Thread (e, p) owns a contiguous range of blocks for expert e.  Each expert
+// keeps at most `cap` assignments (INT32_MAX: all).  Writes counts[e] =
+// min(total_e, cap), offsets = their exclusive scan, and bases[b][e] =
+// offsets[e] + sum_{b' < b} hist[b'][e] (an assignment whose position minus
+// offsets[e] reaches cap is dropped by the scatter).
+__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist, int nb, int n, int cap,
                                                     int* __restrict__ bases,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offsets) {
@@ -342,14 +350,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist
     int run = 0;
     for (int i = 0; i < n; ++i) {
       off_s[i] = run;
-      run += tot_s[i];
+      run += min(tot_s[i], cap);
     }
     off_s[n] = run;
   }
   __syncthreads();
   for (int i = tid; i <= n; i += 1024) {
     offsets[i] = off_s[i];
-    if (i < n) counts[i] = tot_s[i];
+    if (i < n) counts[i] = min(tot_s[i], cap);
   }
   if (e < n) {
     int run = off_s[e] + psum[tid];
@@ -363,8 +371,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist
 // Scatter of one routing block (BT <= 32 tokens): positions are
 // expert-contiguous and ascending in token index within an expert.
 __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ topk_idx,
-                                                     const int* __restrict__ bases, int64_t T, int n,
-                                                     int K, int BT, int* __restrict__ perm_token,
+                                                     const int* __restrict__ bases,
+                                                     const int* __restrict__ offsets, int cap, int64_t T,
+                                                     int n, int K, int BT, int* __restrict__ perm_token,
                                                      int* __restrict__ slot_pos) {
   __shared__ uint32_t mask_s[kMaxN];
   __shared__ int sel_s[32 * kMaxK];
@@ -384,8 +393,11 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ top
   if (tid < cnt) {
     for (int j = 0; j < K; ++j) {
       const int e = sel_s[tid * K + j];
-      const int pos = bases[(int64_t)blockIdx.x * n + e] + __popc(mask_s[e] & ((1u << tid) - 1u));
-      perm_token[pos] = (int)(t0 + tid);
+      int pos = bases[(int64_t)blockIdx.x * n + e] + __popc(mask_s[e] & ((1u << tid) - 1u));
+      if (pos - offsets[e] < cap)
+        perm_token[pos] = (int)(t0 + tid);
+      else
+        pos = -1;  // the expert is full: this assignment is dropped
       slot_pos[(t0 + tid) * K + j] = pos;
     }
   }
@@ -396,12 +408,12 @@ namespace {
 
 template <int NE, int TT, int W>
 void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t d, int n, int K,
-                     const RouteBuffers& rb, bool fused, float* probsum, hipStream_t s) {
+                     const RouteBuffers& rb, bool fused, float* probsum, int cap, hipStream_t s) {
   constexpr int BT = 16 * TT;
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
                      T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
-                     rb.offsets, rb.perm_token, rb.slot_pos, probsum);
+                     rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap);
 }
 
 // Router statistics from the per-block histograms and probability sums (one
@@ -439,18 +451,18 @@ __global__ __launch_bounds__(256) void route_stats_kernel(const int* __restrict_
 
 // Picks the router configuration for the expert count (WgT rows padded to 16).
 void launch_router_bf16(const uint16_t* x, int64_t T, int64_t d, int n, int K, const RouteBuffers& rb,
-                        bool fused, float* probsum, hipStream_t s) {
+                        bool fused, float* probsum, int cap, hipStream_t s) {
   const int ne = route_padded_experts(n) / 16;
   if (ne <= 1)
-    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
   else if (ne <= 2)
-    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
   else if (ne <= 4)
-    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
   else if (ne <= 8)
-    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
   else
-    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, probsum, s);
+    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
 }
 
 }  // namespace
@@ -460,7 +472,8 @@ int route_block_tokens(int n) { return n <= 64 ? 32 : 16; }
 int route_padded_experts(int n) { return (n + 15) / 16 * 16; }
 
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
-                             int K, const RouteBuffers& rb, hipStream_t s, hipEvent_t after_router) {
+                             int K, const RouteBuffers& rb, hipStream_t s, hipEvent_t after_router,
+                             int cap) {
   const int NP = route_padded_experts(n);
   hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
                      dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
@@ -469,11 +482,11 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
   const int BT = route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   const bool fused = nb == 1;
-  launch_router_bf16(x, T, d, n, K, rb, fused, nullptr, s);
+  launch_router_bf16(x, T, d, n, K, rb, fused, nullptr, cap, s);
   e = hipGetLastError();
   if (e == hipSuccess && after_router != nullptr) e = hipEventRecord(after_router, s);
   if (e != hipSuccess || fused) return e;
-  return launch_dispatch(T, n, K, rb, s);
+  return launch_dispatch(T, n, K, rb, s, cap);
 }
 
 hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
@@ -484,7 +497,7 @@ hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_
                      dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_router_bf16(x, T, d, n, K, rb, false, probsum, s);
+  launch_router_bf16(x, T, d, n, K, rb, false, probsum, INT32_MAX, s);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BT = route_block_tokens(n);
@@ -519,15 +532,15 @@ hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, in
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s) {
+hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s, int cap) {
   const int BT = route_block_tokens(n);
   const int nb = (int)((T + BT - 1) / BT);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, rb.bases, rb.counts,
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, cap, rb.bases, rb.counts,
                      rb.offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, s, rb.topk_idx, rb.bases, T, n, K,
-                     BT, rb.perm_token, rb.slot_pos);
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, s, rb.topk_idx, rb.bases, rb.offsets,
+                     cap, T, n, K, BT, rb.perm_token, rb.slot_pos);
   return hipGetLastError();
 }
 

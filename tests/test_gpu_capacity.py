@@ -1,0 +1,147 @@
+"""moe_route_capacity / moe_forward_capacity on the GPU against the fp64 oracle:
+the capacity-limited dispatch is bit-exact (on the validated selection), y
+within the bf16 bounds, and fully dropped tokens give exactly 0."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import config_inputs, log, sample_rows, upload
+from parity import BF16_MAX_REL, BF16_MEAN_REL, assert_rows_close, check_routing
+from synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import sparse_mixture_experts_22_amd as moe
+    return moe
+
+
+def _route_cap(dev, inp, cf):
+    import torch
+    moe = _moe()
+    rc = moe.route_capacity(dev["x"], dev["Wg"], inp.K, cf)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in rc.items()}
+
+
+def _check_dispatch(inp, rc, cf):
+    cap = oracle.expert_capacity(inp.T, inp.n, inp.K, cf)
+    assert _moe().expert_capacity(inp.T, inp.n, inp.K, cf) == cap
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
+    sub = check_routing(r, {"topk_idx": rc["topk_idx"]}, inp.K)
+    ref = oracle.capacity_dispatch(sub, inp.n, cap)
+    np.testing.assert_array_equal(rc["counts"], ref["counts"])
+    np.testing.assert_array_equal(rc["offsets"], ref["offsets"])
+    used = int(ref["offsets"][-1])
+    np.testing.assert_array_equal(rc["perm_token"][:used], ref["perm_token"])
+    np.testing.assert_array_equal(rc["slot_pos"].reshape(inp.T, inp.K), ref["slot_pos"])
+    log(f"  cap={cap} dropped={int((~ref['kept']).sum())} of {inp.T * inp.K}")
+    return sub, ref, cap
+
+
+@pytest.mark.parametrize("T,d,n,K,cf,routing", [
+    (32, 128, 8, 2, 0.5, "skewed"),     # one routing block: the fused dispatch
+    (30, 64, 8, 2, 0.1, "uniform"),     # capacity 1
+    (300, 64, 8, 2, 0.75, "skewed"),
+    (1000, 192, 8, 2, 1.0, "skewed"),
+    (257, 64, 130, 4, 0.5, "uniform"),
+    (500, 64, 8, 2, 100.0, "skewed"),   # no overflow: the dropless dispatch
+])
+def test_route_capacity_shapes(T, d, n, K, cf, routing):
+    inp = make_inputs(T, d, 64, n, K, dtype="bf16", seed=4321 + T + n, routing=routing, router_only=True)
+    log(f"route_capacity: T={T} d={d} n={n} K={K} cf={cf} routing={routing}")
+    dev = upload(inp)
+    rc = _route_cap(dev, inp, cf)
+    _check_dispatch(inp, rc, cf)
+    if cf >= 100.0:
+        import torch
+        full = _moe().route(dev["x"], dev["Wg"], K)
+        torch.cuda.synchronize()
+        for k in ("counts", "offsets", "perm_token", "slot_pos"):
+            np.testing.assert_array_equal(rc[k], full[k].cpu().numpy())
+
+
+@pytest.mark.parametrize("cf", [1.0, 1.25])
+def test_route_capacity_skewed_full_size(cf):
+    inp = config_inputs("mixtral_skewed", router_only=True)
+    log(f"route_capacity mixtral_skewed cf={cf}")
+    rc = _route_cap(upload(inp), inp, cf)
+    _, ref, cap = _check_dispatch(inp, rc, cf)
+    assert int((~ref["kept"]).sum()) > 0  # the favourite expert overflows
+
+
+@pytest.mark.parametrize("T,d,f,n,K,cf,routing", [
+    (32, 128, 192, 8, 2, 0.5, "skewed"),    # decode-size: weight-streaming kernels
+    (300, 128, 192, 8, 2, 0.75, "skewed"),
+    (2000, 192, 320, 4, 2, 0.8, "uniform"),  # tiled kernels
+    (700, 256, 384, 8, 2, 1.0, "skewed"),
+])
+def test_forward_capacity_shapes(T, d, f, n, K, cf, routing):
+    import torch
+    moe = _moe()
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=777 + T, routing=routing)
+    log(f"forward_capacity: T={T} d={d} f={f} n={n} K={K} cf={cf} routing={routing}")
+    dev = upload(inp)
+    y = moe.forward_capacity(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], K, cf)
+    rc = _route_cap(dev, inp, cf)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    sub, ref, cap = _check_dispatch(inp, rc, cf)
+    yref = oracle.forward_kept(inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"), inp.f64("W2"),
+                               sub, ref["kept"])
+    gone = ~ref["kept"].any(axis=1)
+    assert (y[gone] == 0).all(), "a token with every assignment dropped must get y = 0"
+    live = ~gone
+    rel = assert_rows_close(y[live], yref[live], BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} all-dropped tokens={int(gone.sum())}")
+
+
+def test_forward_capacity_without_overflow_equals_forward():
+    import torch
+    moe = _moe()
+    inp = make_inputs(600, 128, 192, 8, 2, dtype="bf16", seed=99)
+    dev = upload(inp)
+    y0 = moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], 2)
+    y1 = moe.forward_capacity(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], 2, 1000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_capacity_skewed_full_size():
+    import torch
+    moe = _moe()
+    inp = config_inputs("mixtral_skewed")
+    cf = 1.25
+    log(f"forward_capacity mixtral_skewed cf={cf}")
+    dev = upload(inp)
+    y = moe.forward_capacity(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], inp.K, cf)
+    rc = _route_cap(dev, inp, cf)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    del dev
+    sub, ref, cap = _check_dispatch(inp, rc, cf)
+    rs = sample_rows(inp.T, 128)
+    # include some tokens that lost an assignment
+    lost = np.nonzero(~ref["kept"].all(axis=1))[0]
+    rs = np.unique(np.concatenate([rs, lost[:: max(1, lost.size // 32)]]))
+    yref = oracle.forward_kept(inp.f64("x")[rs], inp.f64("Wg"), lambda e: inp.expert_f64("W1", e),
+                               lambda e: inp.expert_f64("W3", e), lambda e: inp.expert_f64("W2", e),
+                               sub[rs], ref["kept"][rs])
+    gone = ~ref["kept"][rs].any(axis=1)
+    assert (y[rs][gone] == 0).all()
+    rel = assert_rows_close(y[rs][~gone], yref[~gone], BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  rows={len(rs)} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
+
+
+def test_capacity_invalid_factor():
+    import torch
+    moe = _moe()
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    wg = torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda")
+    for cf in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(moe.MoEError):
+            moe.route_capacity(x, wg, 2, cf)
+    assert moe.expert_capacity(4, 8, 2, 0.0) == 0
