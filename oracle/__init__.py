@@ -6,8 +6,11 @@ product path (the HIP library and its Python binding) never calls it and shares
 no code with it.
 """
 from .moe_oracle import (  # noqa: F401
+    Q4_GROUP,
+    bf16_round,
     brute_force_topk,
     capacity_dispatch,
+    dequantize_q4,
     dispatch,
     expert_capacity,
     expert_swiglu,
@@ -19,10 +22,12 @@ from .moe_oracle import (  # noqa: F401
     full_softmax,
     gate_weights,
     mixtral_param_counts,
+    quantize_q4,
     route,
     router_logits,
     router_stats,
     sigmoid,
     silu,
     topk_select,
+    unpack_q4,
 )

@@ -28,6 +28,9 @@ Readings where the pages leave a step open (each also listed in the design notes
   * y excludes the residual add that the surrounding block performs.
   * Router statistics (Part 5): f_i counts the T*K assignments once each,
     f_i = counts_i / (T*K), so both shares are 1/N when balanced.
+  * 4-bit weights (the page sizes the model at 4 bits but gives no format):
+    the format is defined with quantize_q4 below; the layer on such weights is
+    the plain forward on the dequantised values.
   * Capacity (Part 5, "What happens when an expert is full"): with K
     assignments per token C = ceil(cf * T * K / n); each expert keeps its first
     C assignments in token order, dropped ones add nothing and the kept
@@ -268,6 +271,64 @@ def forward_kept(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter,
         out = expert_swiglu(x[rows], _expert(W1, e), _expert(W3, e), _expert(W2, e))
         y[rows] += (w[rows] * hit[rows]).sum(axis=1)[:, None] * out
     return y
+
+
+# ------------------------------------------------- 4-bit expert weights ---
+# The explainer (Part 4, "Why total and active both matter") sizes the model at
+# 16 bits and at 4 bits per parameter but gives no format.  The format here:
+#   groups of Q4_GROUP = 128 consecutive reduction indices r, per column c;
+#   scale s[e][g][c] = bf16_rne(max_r |W[e][r][c]| / 7) (fp32 division);
+#   code q = clamp(rint(W / s), -7, 7) with the division in fp32 (q = 0 where
+#   s = 0); dequantised weight q * s.
+# Storage of the codes (nibble u = q + 8), per expert e: column pair p = c // 2,
+# chunk j = r // 32, column parity c % 2, then 16 bytes = 4 little-endian
+# 32-bit words; word m holds r = 32j + 8m + i for i = 0..7, element i = 2t in
+# bits 4t..4t+3 and element i = 2t + 1 in bits 16+4t..16+4t+3.
+Q4_GROUP = 128
+
+
+def bf16_round(a) -> np.ndarray:
+    """float32 -> nearest bf16 value (ties to even), returned as float32."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+def quantize_q4(W) -> tuple:
+    """W [n][R][C] (float32 values) -> codes int8 [n][R][C], scales float32
+    [n][R/128][C] (bf16 values).  All arithmetic in float32, as specified."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    n, R, C = W.shape
+    G = R // Q4_GROUP
+    Wg = W.reshape(n, G, Q4_GROUP, C)
+    amax = np.abs(Wg).max(axis=2)
+    scale = bf16_round(amax / np.float32(7.0))
+    nz = scale > 0
+    den = np.where(nz, scale, np.float32(1.0))[:, :, None, :]
+    q = np.rint(Wg / den)
+    q = np.where(nz[:, :, None, :], q, np.float32(0.0))
+    q = np.clip(q, -7, 7).astype(np.int8)
+    return q.reshape(n, R, C), scale
+
+
+def dequantize_q4(codes, scales) -> np.ndarray:
+    """codes [n][R][C], scales [n][R/128][C] -> fp64 weights q * s."""
+    n, R, C = codes.shape
+    q = np.asarray(codes, dtype=np.float64).reshape(n, R // Q4_GROUP, Q4_GROUP, C)
+    return (q * np.asarray(scales, dtype=np.float64)[:, :, None, :]).reshape(n, R, C)
+
+
+def unpack_q4(packed, n: int, R: int, C: int) -> np.ndarray:
+    """Packed code bytes (the storage described above) -> codes int8 [n][R][C]."""
+    words = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").reshape(n, C // 2, R // 32, 2, 4)
+    codes = np.empty((n, R, C), dtype=np.int8)
+    for i in range(8):
+        shift = 4 * (i // 2) + 16 * (i % 2)
+        u = ((words >> np.uint32(shift)) & np.uint32(15)).astype(np.int16) - 8  # [e][p][j][s][m]
+        # r = 32j + 8m + i, c = 2p + s
+        v = u.transpose(0, 2, 4, 1, 3)  # [e][j][m][p][s]
+        codes.reshape(n, R // 32, 4, 8, C // 2, 2)[:, :, :, i, :, :] = v
+    return codes
 
 
 def sigmoid(z) -> np.ndarray:

@@ -500,3 +500,62 @@ def test_capacity_forward_keeps_only_kept_terms():
         np.testing.assert_allclose(y[t], ref, rtol=0, atol=1e-13)
         if not kept[t].any():
             assert (y[t] == 0).all()
+
+
+# ------------------------------------------------------------ 4-bit weights
+
+def test_q4_word_layout_hand_example():
+    # codes -7..0 for r = 0..7 of column 0: nibbles u = 1..8; even elements in
+    # the low half (1, 3, 5, 7 -> 0x7531), odd ones in the high half (0x8642)
+    n, R, C = 1, 128, 2
+    packed = np.full(n * R * C // 2, 0x88, dtype=np.uint8)  # every other code 0
+    packed[0:4] = [0x31, 0x75, 0x42, 0x86]
+    codes = oracle.unpack_q4(packed, n, R, C)
+    np.testing.assert_array_equal(codes[0, 0:8, 0], np.arange(-7, 1))
+    codes[0, 0:8, 0] = 0
+    assert (codes == 0).all()
+    # chunk order: column parity before the next chunk; the 17th..32nd bytes are column 1
+    packed2 = np.full_like(packed, 0x88)
+    packed2[16] = 0x9A  # column 1, r = 0 (low nibble 0xA -> +2) and r = 2 (0x9 -> +1)
+    codes2 = oracle.unpack_q4(packed2, n, R, C)
+    assert codes2[0, 0, 1] == 2 and codes2[0, 2, 1] == 1 and codes2[0, 1, 1] == 0
+
+
+def test_q4_exactly_representable_weights_round_trip():
+    rng = np.random.default_rng(21)
+    n, R, C = 2, 256, 6
+    q = rng.integers(-7, 8, size=(n, R, C)).astype(np.float32)
+    q[:, ::128, :] = 7.0                       # every group-column reaches |q| = 7
+    s = np.float32(2.0) ** rng.integers(-9, -2, size=(n, R // 128, C)).astype(np.float32)
+    W = (q.reshape(n, R // 128, 128, C) * s[:, :, None, :]).reshape(n, R, C)
+    codes, scales = oracle.quantize_q4(W)
+    np.testing.assert_array_equal(scales, s)
+    np.testing.assert_array_equal(codes, q.astype(np.int8))
+    np.testing.assert_array_equal(oracle.dequantize_q4(codes, scales), W.astype(np.float64))
+
+
+def test_q4_error_bound_and_extremes():
+    rng = np.random.default_rng(22)
+    n, R, C = 3, 384, 10
+    W = (rng.standard_normal((n, R, C)) * 0.02).astype(np.float32)
+    W[1, 128:256, 4] = 0.0                     # an all-zero group
+    codes, scales = oracle.quantize_q4(W)
+    assert codes.min() >= -7 and codes.max() <= 7
+    assert scales[1, 1, 4] == 0 and (codes[1, 128:256, 4] == 0).all()
+    # the bf16 scale is within 2^-9 of max/7, so |W/s| <= 7.02 and no code clips:
+    # every element is within half a step of its code
+    step = np.repeat(scales, 128, axis=1).astype(np.float64)
+    err = np.abs(W.astype(np.float64) - oracle.dequantize_q4(codes, scales))
+    assert (err <= 0.5 * step * (1 + 1e-6)).all()
+    # the largest magnitude of each group-column maps to +-7
+    Wg = np.abs(W.reshape(n, R // 128, 128, C))
+    at = Wg.argmax(axis=2)
+    cg = codes.reshape(n, R // 128, 128, C)
+    top = np.take_along_axis(cg, at[:, :, None, :], axis=2)[:, :, 0, :]
+    assert (np.abs(top)[scales > 0] == 7).all()
+
+
+def test_q4_bf16_round_ties_to_even():
+    v = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8)], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.bf16_round(v),
+                                  np.array([1.0, 1.0 + 2 ** -6, 1.0, -1.0], dtype=np.float32))
