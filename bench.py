@@ -39,6 +39,8 @@ def parse():
                     choices=["mixtral_prefill", "mixtral_skewed", "many_experts", "mixtral_decode"])
     ap.add_argument("--no-decode", action="store_true", help="skip the T=32 decode measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip timing the router statistics and the capacity-limited forward")
     ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens in the oracle's timed sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device-to-device copy (reference for traffic counters)")
@@ -75,7 +77,44 @@ def upload(inp, dev, copies):
     return x, wg, w
 
 
-def time_workload(name, steps, warmup):
+def _time_calls(fn, reps, stream):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(reps):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def time_extras(moe, x, wg, wsets, K, y, stream, reps):
+    """The optional paths on the same resident inputs: router statistics with the
+    load-balancing loss, and the capacity-limited forward (capacity factor 1.0)."""
+    T = x.shape[0]
+    n = wg.shape[1]
+    stats_ms = _time_calls(lambda i=0: moe.route_stats(x, wg, K, 0.01), reps, stream)
+    st = moe.route_stats(x, wg, K, 0.01)
+
+    def cap_step(i=0):
+        w1, w3, w2 = wsets[i % 2]
+        moe.forward_capacity(x, wg, w1, w3, w2, K, 1.0, y=y)
+
+    cap_ms = _time_calls(cap_step, reps, stream)
+    rc = moe.route_capacity(x, wg, K, 1.0, outputs=("offsets",))
+    kept = int(rc["offsets"][-1].item())
+    return {
+        "route_stats": {"ms_per_call": round(stats_ms, 4), "aux_loss_alpha_0.01": round(float(st["aux_loss"][0]), 6)},
+        "forward_capacity_cf1": {"ms_per_step": round(cap_ms, 4), "tokens_per_s": round(T / (cap_ms * 1e-3), 1),
+                                 "capacity": moe.expert_capacity(T, n, K, 1.0),
+                                 "dropped_assignments": T * K - kept},
+    }
+
+
+def time_workload(name, steps, warmup, with_extras=False):
     import numpy as np
     import torch
 
@@ -129,10 +168,12 @@ def time_workload(name, steps, warmup):
     torch.cuda.synchronize()
     counts = rt["counts"].cpu().numpy()
     assert torch.isfinite(y).all().item()
+    extras = time_extras(moe, x, wg, wsets, K, y, stream, max(3, steps // 4)) if with_extras else None
     return dict(name=name, T=T, d=d, f=f, n=n, K=K, ms_per_step=total_ms / steps, wall_s=wall,
                 stage_ms=stage_ms.mean(axis=0), stage_ms_min=stage_ms.min(axis=0), counts=counts,
                 traced_step_ms={"median": round(float(np.median(traced_ms)), 4),
-                                "min": round(float(traced_ms.min()), 4), "max": round(float(traced_ms.max()), 4)})
+                                "min": round(float(traced_ms.min()), 4), "max": round(float(traced_ms.max()), 4)},
+                extras=extras)
 
 
 def prefill_record(r):
@@ -174,6 +215,57 @@ def decode_record(r):
         "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, r["stage_ms"])},
         "traced_step_ms": r["traced_step_ms"],
     }
+
+
+def time_decode_q4(steps, warmup):
+    """The decode batch with 4-bit expert weights (quantized on the GPU from the
+    bf16 weights; two quantized copies alternate between steps)."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_22_amd as moe
+    from synth import CONFIGS, make_config_inputs
+
+    name = "mixtral_decode"
+    c = CONFIGS[name]
+    T, d, f, n, K = c["T"], c["d"], c["f"], c["n"], c["K"]
+    dev = torch.device("cuda:0")
+    inp = make_config_inputs(name)
+    x, wg, wsets = upload(inp, dev, copies=1)
+    del inp
+    qsets = []
+    for cp in range(2):
+        w1, w3, w2 = wsets[0]
+        if cp == 1:  # a second, distinct copy: perturb nothing, just separate storage
+            w1, w3, w2 = w1.clone(), w3.clone(), w2.clone()
+        qsets.append(tuple(moe.quantize_q4(w) for w in (w1, w3, w2)))
+    del wsets
+    torch.cuda.synchronize()
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        q1, q3, q2 = qsets[i % 2]
+        moe.forward_q4(x, wg, q1, q3, q2, d, f, K, y=y)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        q1, q3, q2 = qsets[i % 2]
+        moe.forward_q4(x, wg, q1, q3, q2, d, f, K, y=y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    counts = moe.route(x, wg, K, outputs=("counts",))["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    # algorithmic bytes: codes + scales of the touched experts, x, W_g, fp32 y
+    wbytes = touched * 3 * (d * f // 2 + (d // 128) * f * 2)
+    layer_bytes = wbytes + T * d * 2 + d * n * 2 + T * d * 4
+    gbs = layer_bytes / (ms * 1e-3) / 1e9
+    return {"workload": name + " (4-bit expert weights)", "T": T, "value": round(T / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 4), "weight_bytes": wbytes,
+            "layer_gbs": round(gbs, 1), "layer_frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "experts_touched": touched}
 
 
 def cpu_baseline(name, sample):
@@ -325,7 +417,7 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    main_r = time_workload(args.workload, args.steps, args.warmup)
+    main_r = time_workload(args.workload, args.steps, args.warmup, with_extras=not args.no_extras)
     log(f"[bench] {args.workload}: {main_r['ms_per_step']:.3f} ms/step, stages {main_r['stage_ms']}")
     rec = {
         "metric": METRIC,
@@ -349,11 +441,16 @@ def main():
         rec["layer_frac_of_mfma_peak"] = pr["layer_frac_of_mfma_peak"]
     rec["stages_ms"] = {s: round(float(v), 4) for s, v in zip(STAGES, main_r["stage_ms"])}
     rec["traced_step_ms"] = main_r["traced_step_ms"]
+    if main_r["extras"] is not None:
+        rec["extras"] = main_r["extras"]
     rec["expert_counts"] = main_r["counts"].tolist()
     if not args.no_decode and args.workload != "mixtral_decode":
         dr_raw = time_workload("mixtral_decode", max(args.steps, 20), args.warmup)
         rec["decode"] = decode_record(dr_raw)
         log(f"[bench] decode: {dr_raw['ms_per_step']:.3f} ms/step, stages {dr_raw['stage_ms']}")
+    if not args.no_decode and not args.no_extras:
+        rec["decode_q4"] = time_decode_q4(max(args.steps, 20), args.warmup)
+        log(f"[bench] decode (4-bit weights): {rec['decode_q4']['ms_per_step']:.3f} ms/step")
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a sample ...")
         rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample)

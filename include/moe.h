@@ -176,6 +176,37 @@ moe_status_t moe_forward_capacity(const void* x, const void* Wg, const void* W1,
                                   const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
                                   int32_t K, double capacity_factor, float* y, moe_stream_t stream);
 
+/*
+ * 4-bit expert weights.  The explainer sizes the model at 16 and at 4 bits per
+ * parameter ("Why total and active both matter", Part 4 of "Mixture of
+ * Experts: Why Mixtral Only Wakes Up Two Specialists") but gives no format;
+ * this library's format, for a weight stack W[n][R][C] (R = reduction index):
+ *   scales [n][R/128][C] bf16: s = bf16_rne(max |W| over 128 consecutive r of
+ *           a column / 7), computed in fp32;
+ *   codes   n*R*C/2 bytes: q = clamp(rint(W / s), -7, 7) (fp32 division, q = 0
+ *           where s = 0), nibble q + 8; per expert, by column pair c/2, then
+ *           chunk r/32, then column parity, 16 bytes = 4 little-endian words,
+ *           word m holding r = 32j + 8m + i with element i = 2t in bits
+ *           4t..4t+3 and element 2t+1 in bits 16+4t..16+4t+3.
+ * The dequantised weight is q * s.
+ *
+ * moe_quantize_q4 -- W bf16 [n][R][C] (R % 128 == 0, C even; W and codes
+ *   16-byte aligned) -> codes, scales.  Deterministic, bit-exact to the format.
+ * moe_forward_q4  -- the layer with 4-bit W1, W3 (R = d, C = f) and W2 (R = f,
+ *   C = d) given as (codes, scales) pairs; x, Wg bf16, y fp32.  Needs d % 128
+ *   == 0 and f % 128 == 0.  Routing, SwiGLU, bf16 rounding of h and the
+ *   combine are as in moe_forward; every projection uses the weight-streaming
+ *   kernels, which suit decode batches (a few rows per expert) - larger
+ *   batches are correct but re-stream the weights per 16 rows of an expert.
+ */
+moe_status_t moe_quantize_q4(const void* W, int32_t n, int64_t R, int64_t C, void* codes, void* scales,
+                             moe_stream_t stream);
+
+moe_status_t moe_forward_q4(const void* x, const void* Wg, const void* W1q, const void* W1s,
+                            const void* W3q, const void* W3s, const void* W2q, const void* W2s,
+                            int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
+                            moe_stream_t stream);
+
 /* Bytes of library workspace a call of this shape needs on any supported
  * device (an upper bound: the prefill path's leftover-tile buffer scales with
  * the device's compute units per XCD); 0 on invalid shapes. */

@@ -11,11 +11,13 @@ from ._binding import (  # noqa: F401
     expert_capacity,
     forward,
     forward_capacity,
+    forward_q4,
     forward_f32,
     forward_traced,
     last_error,
     lib,
     lib_path,
+    quantize_q4,
     release,
     route,
     route_capacity,
@@ -27,5 +29,6 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
-           "expert_capacity", "route_capacity", "forward_capacity", "workspace_bytes", "release",
+           "expert_capacity", "route_capacity", "forward_capacity",
+           "quantize_q4", "forward_q4", "workspace_bytes", "release",
            "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

@@ -14,7 +14,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 
 EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32",
            "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
-           "moe_forward_capacity", "moe_workspace_bytes",
+           "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4", "moe_workspace_bytes",
            "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
 
 
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.moe_route_capacity.restype = ctypes.c_int
     L.moe_forward_capacity.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, f64, vp, vp]
     L.moe_forward_capacity.restype = ctypes.c_int
+    L.moe_quantize_q4.argtypes = [vp, i32, i64, i64, vp, vp, vp]
+    L.moe_quantize_q4.restype = ctypes.c_int
+    L.moe_forward_q4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    L.moe_forward_q4.restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_release.argtypes = []
@@ -247,6 +251,39 @@ def forward_capacity(x, Wg, W1, W3, W2, K, capacity_factor, y=None, stream=None)
     import torch
     return _forward(lib().moe_forward_capacity, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream,
                     mid=(float(capacity_factor),))
+
+
+def quantize_q4(W, stream=None):
+    """moe_quantize_q4: bf16 W[n][R][C] -> (codes uint8 [n*R*C/2], scales bf16 [n][R/128][C])."""
+    import torch
+    _expect(W, torch.bfloat16, "W", 3)
+    n, R, C = W.shape
+    codes = torch.empty((n * R * C // 2,), dtype=torch.uint8, device=W.device)
+    scales = torch.empty((n, R // 128, C), dtype=torch.bfloat16, device=W.device)
+    _check(lib().moe_quantize_q4(_ptr(W), n, R, C, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def forward_q4(x, Wg, w1, w3, w2, d, f, K, y=None, stream=None):
+    """moe_forward_q4: w1, w3, w2 are (codes, scales) pairs from quantize_q4 of
+    W1/W3 [n][d][f] and W2 [n][f][d]; returns fp32 y[T][d]."""
+    import torch
+    _expect(x, torch.bfloat16, "x", 2)
+    _expect(Wg, torch.bfloat16, "Wg", 2)
+    T = x.shape[0]
+    n = Wg.shape[1]
+    if x.shape[1] != d or Wg.shape[0] != d:
+        raise ValueError("x must be [T][d] and Wg [d][n]")
+    for (q, s), (R, C) in zip((w1, w3, w2), ((d, f), (d, f), (f, d))):
+        if q.dtype != torch.uint8 or q.numel() != n * R * C // 2 or not q.is_contiguous():
+            raise ValueError("codes must be contiguous uint8 of n*R*C/2 bytes")
+        if s.dtype != torch.bfloat16 or tuple(s.shape) != (n, R // 128, C) or not s.is_contiguous():
+            raise ValueError("scales must be contiguous bf16 [n][R/128][C]")
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _check(lib().moe_forward_q4(_ptr(x), _ptr(Wg), _ptr(w1[0]), _ptr(w1[1]), _ptr(w3[0]), _ptr(w3[1]),
+                                _ptr(w2[0]), _ptr(w2[1]), T, d, f, n, int(K), _ptr(y), _stream(stream)))
+    return y
 
 
 def workspace_bytes(T, d, f, n, K) -> int:

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "gemm_prefill.hip", "gemm_skinny.hip", "misc.hip", "api.hip"]
+SOURCES = ["route.hip", "gemm_prefill.hip", "gemm_skinny.hip", "quant4.hip", "misc.hip", "api.hip"]
 ARCH = "gfx950"
 
 

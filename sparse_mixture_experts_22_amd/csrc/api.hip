@@ -47,7 +47,8 @@ struct Plan {
   int splits = 1;
 };
 
-Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus_per_xcd = 0) {
+Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus_per_xcd = 0,
+               bool force_skinny = false) {
   Plan p;
   const int64_t TK = T * K;
   const int BT = moe::route_block_tokens(n);
@@ -69,7 +70,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
   p.slot_pos = take((size_t)TK * 4);
   if (path == Path::kStats) p.probsum = take((size_t)nb * n * 4);
   if (path == Path::kBf16) {
-    p.skinny = TK <= (int64_t)moe::kSkinnyMaxAvgRows * n;
+    p.skinny = force_skinny || TK <= (int64_t)moe::kSkinnyMaxAvgRows * n;
     p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
     p.h = take((size_t)TK * f * 2);
     p.o = take((size_t)p.splits * TK * d * 4);
@@ -326,6 +327,42 @@ moe_status_t route_stats_impl(const void* x, const void* Wg, int64_t T, int64_t 
   return MOE_OK;
 }
 
+moe_status_t forward_q4(const void* x, const void* Wg, const void* W1q, const void* W1s, const void* W3q,
+                        const void* W3s, const void* W2q, const void* W2s, int64_t T, int64_t d, int64_t f,
+                        int32_t n, int32_t K, float* y, hipStream_t stream) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, d, f, n, K, true);
+  if (st != MOE_OK) return st;
+  if (!x || !Wg || !W1q || !W1s || !W3q || !W3s || !W2q || !W2s || !y)
+    return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  if (d % 128 != 0 || f % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "4-bit path needs d % 128 == 0 and f % 128 == 0");
+  st = check_bf16(d, f, true, {x, Wg, W1q, W3q, W2q, y});
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(T, d, f, n, K, Path::kBf16, 0, true);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const moe::RouteBuffers r =
+      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* o = at<float>(ws, p.o);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const int64_t TK = T * K;
+  MOE_LAUNCH(moe::launch_route_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r, stream),
+             "routing kernel launch");
+  MOE_LAUNCH(moe::launch_q4_up(xb, T, r.perm_token, static_cast<const uint8_t*>(W1q),
+                               static_cast<const uint16_t*>(W1s), static_cast<const uint8_t*>(W3q),
+                               static_cast<const uint16_t*>(W3s), r.offsets, TK, n, (int)d, (int)f, h, stream),
+             "up-projection kernel launch");
+  MOE_LAUNCH(moe::launch_q4_down(h, static_cast<const uint8_t*>(W2q), static_cast<const uint16_t*>(W2s),
+                                 r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
+             "down-projection kernel launch");
+  MOE_LAUNCH(moe::launch_combine(o, p.splits, TK, r.topk_w, r.slot_pos, T, d, K, y, stream),
+             "combine kernel launch");
+  return MOE_OK;
+}
+
 // Expert capacity ceil(cf * T * K / n), or -1 if cf is not a positive finite
 // number or the capacity does not fit an int.
 int64_t capacity_of(int64_t T, int32_t n, int32_t K, double cf) {
@@ -488,6 +525,30 @@ moe_status_t moe_route_capacity(const void* x, const void* Wg, int64_t T, int64_
   return route_impl<true>(x, Wg, T, d, n, K,
                           RouteOut{topk_idx, topk_w, counts, offsets, perm_token, slot_pos},
                           reinterpret_cast<hipStream_t>(stream), (int)cap);
+}
+
+moe_status_t moe_quantize_q4(const void* W, int32_t n, int64_t R, int64_t C, void* codes, void* scales,
+                             moe_stream_t stream) {
+  g_last_error.clear();
+  if (!W || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  if (n < 1 || R < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "n, R and C must be >= 1");
+  if (R % 128 != 0 || C % 2 != 0) return fail(MOE_ERR_UNSUPPORTED, "4-bit format needs R % 128 == 0 and C even");
+  if (R > INT32_MAX || C > INT32_MAX || (int64_t)n * R * C / 2 > ((int64_t)1 << 40))
+    return fail(MOE_ERR_UNSUPPORTED, "weight stack too large");
+  if (!aligned16(W) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "W and codes must be 16-byte aligned, scales 2-byte aligned");
+  MOE_LAUNCH(moe::launch_quantize_q4(static_cast<const uint16_t*>(W), n, (int)R, (int)C,
+                                     static_cast<uint8_t*>(codes), static_cast<uint16_t*>(scales),
+                                     reinterpret_cast<hipStream_t>(stream)),
+             "quantize kernel launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_q4(const void* x, const void* Wg, const void* W1q, const void* W1s, const void* W3q,
+                            const void* W3s, const void* W2q, const void* W2s, int64_t T, int64_t d,
+                            int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream) {
+  return forward_q4(x, Wg, W1q, W1s, W3q, W3s, W2q, W2s, T, d, f, n, K, y,
+                    reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -96,6 +96,18 @@ hipError_t launch_f32_up(const float* x, int64_t T, const int* perm_token, const
 hipError_t launch_f32_down(const float* h, const float* W2, const int* offsets, int64_t TK, int n,
                            int f, int d, float* o, hipStream_t s);
 
+// ------------------------------------------------------- 4-bit weights
+// Quantize W bf16 [n][R][C] (R % 128 == 0, C % 2 == 0) into codes
+// (n*R*C/2 bytes, 16-byte aligned) and bf16 scales [n][R/128][C].
+hipError_t launch_quantize_q4(const uint16_t* W, int n, int R, int C, uint8_t* codes, uint16_t* scales,
+                              hipStream_t s);
+// Decode-size projections on 4-bit weights (same row layout as the bf16 ones).
+hipError_t launch_q4_up(const uint16_t* x, int64_t T, const int* perm_token, const uint8_t* Q1,
+                        const uint16_t* S1, const uint8_t* Q3, const uint16_t* S3, const int* offsets,
+                        int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s);
+hipError_t launch_q4_down(const uint16_t* h, const uint8_t* Q2, const uint16_t* S2, const int* offsets,
+                          int64_t TK, int n, int f, int d, int splits, float* o, hipStream_t s);
+
 // ----------------------------------------------------------------- combine
 // y[t][:] = sum_k topk_w[t][k] * (sum_s o[s][slot_pos[t][k]][:]), k and s ascending.
 hipError_t launch_combine(const float* o, int splits, int64_t TK, const float* topk_w,

@@ -1,0 +1,245 @@
+// 4-bit expert weights: the quantizer and the decode-size expert projections
+// that stream them.
+//
+// The explainer sizes Mixtral at 16 bits and at 4 bits per parameter ("Why
+// total and active both matter", Part 4 of "Mixture of Experts: Why Mixtral
+// Only Wakes Up Two Specialists") without giving a format; decode batches are
+// bound by streaming every touched expert's weights, so 4-bit weights move a
+// quarter of the bytes.  Format (per weight stack W[n][R][C], R = reduction):
+//   scale s[e][g][c] = bf16_rne(max_{r in group g} |W[e][r][c]| / 7), groups
+//   of 128 reduction indices; code q = clamp(rint(W / s), -7, 7) (q = 0 where
+//   s = 0), both divisions in fp32; nibble u = q + 8.
+//   Codes of expert e: column pair p = c/2, chunk j = r/32, parity c%2, then
+//   16 bytes = 4 little-endian words; word m holds r = 32j + 8m + i, element
+//   i = 2t in bits 4t..4t+3 and i = 2t+1 in bits 16+4t..16+4t+3.
+// A 128-byte line thus holds 256 reduction indices of one column pair, and
+// one word ORed into 0x43004300 after masking with 0x000F000F (shifted by
+// 4t) gives two bf16 values 128 + u = 136 + q of an MFMA B operand.
+//
+// Projection kernel (one workgroup of 4 waves per (expert, 128 columns[, K
+// split])): lane (c = l%16, g = l/16) of column tile ct loads the 16 bytes of
+// column ct*16 + c, chunk 4*blk + g: reduction indices 128blk + 32g + 0..31,
+// four MFMA B operands (word j: 128blk + 32g + 8j + 0..7).  The A operand of
+// lane (row, g) uses the same reduction indices, so each 16x16x32 MFMA j sums
+// over 32 indices of one 128-group.  Per group and column tile the MFMAs give
+// sum_k x_k (136 + q_k); one extra MFMA chain against a splat of 136 gives
+// 136 sum_k x_k (shared by the 8 column tiles), and
+//   acc += s[g][col] * (tile - correction)
+// applies the scale once per group.  The rest follows the bf16 weight-
+// streaming kernels: waves split the reduction, partials are summed in LDS in
+// wave order, SwiGLU epilogue (up) or fp32 partial store (down).
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int Q4G = 128;            // reduction indices per scale group
+constexpr uint32_t kBias136 = 0x4308u;  // bf16 136.0
+
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ W, int n, int R,
+                                                          int C, uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ scales) {
+  const int G = R / Q4G;
+  const int cb = (C + 255) / 256;
+  int b = blockIdx.x;
+  const int cblk = b % cb;
+  b /= cb;
+  const int g = b % G;
+  const int e = b / G;
+  const int c = cblk * 256 + threadIdx.x;
+  if (e >= n || c >= C) return;
+  const uint16_t* col = W + ((int64_t)e * R + (int64_t)g * Q4G) * C + c;
+  float amax = 0.0f;
+  for (int r = 0; r < Q4G; ++r) amax = fmaxf(amax, fabsf(__uint_as_float((uint32_t)col[(int64_t)r * C] << 16)));
+  const uint16_t sbits = f32_to_bf16_rne(amax / 7.0f);
+  const float s = __uint_as_float((uint32_t)sbits << 16);
+  scales[((int64_t)e * G + g) * C + c] = sbits;
+  uint8_t* dst = codes + ((((int64_t)e * (C / 2) + c / 2) * (R / 32) + 4 * g) * 2 + (c & 1)) * 16;
+  for (int jj = 0; jj < 4; ++jj) {  // chunk 4g + jj
+    u32x4_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = __uint_as_float((uint32_t)col[(int64_t)(32 * jj + 8 * m + i) * C] << 16);
+        float q = 0.0f;
+        if (s > 0.0f) q = fminf(fmaxf(rintf(w / s), -7.0f), 7.0f);
+        const uint32_t u = (uint32_t)((int)q + 8);
+        word |= u << (4 * (i >> 1) + 16 * (i & 1));
+      }
+      out[m] = word;
+    }
+    *reinterpret_cast<u32x4_t*>(dst + (int64_t)jj * 32) = out;
+  }
+}
+
+__device__ __forceinline__ bf16x8_t dq4(uint32_t w) {
+  u32x4_t r;
+  r[0] = (w & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return *reinterpret_cast<bf16x8_t*>(&r);
+}
+
+// MODE 1: up.  Waves 0-1 stream W1 codes, waves 2-3 W3, each over half of
+//         the groups; A rows gathered from x; h = SiLU(a) * b in bf16.
+// MODE 2: down.  The 4 waves split this split's groups; o[split] partials.
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
+    const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
+    const uint8_t* __restrict__ Q1, const uint16_t* __restrict__ S1,
+    const uint8_t* __restrict__ Q3, const uint16_t* __restrict__ S3,
+    const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
+    uint16_t* __restrict__ hout, float* __restrict__ oout) {
+  __shared__ float red[4][32][64];
+
+  const int NB = (N + 127) / 128;
+  int bid = blockIdx.x;
+  const int sp = bid % splits;
+  bid /= splits;
+  const int nb = bid % NB;
+  const int e = bid / NB;
+  if (e >= n) return;
+  const int row_beg = offsets[e];
+  const int cnt = offsets[e + 1] - row_beg;
+  if (cnt <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int c16 = lane & 15;
+  const int g = lane >> 4;
+
+  constexpr int KPARTS = (MODE == 1) ? 2 : 4;
+  const int part = (MODE == 1) ? (wave & 1) : wave;
+  const int ngr = Kdim / Q4G;
+  const int kb0 = (int)((int64_t)sp * ngr / splits);
+  const int kb1 = (int)((int64_t)(sp + 1) * ngr / splits);
+  const int wb0 = kb0 + (int)((int64_t)part * (kb1 - kb0) / KPARTS);
+  const int wb1 = kb0 + (int)((int64_t)(part + 1) * (kb1 - kb0) / KPARTS);
+
+  const bool third = MODE == 1 && wave >= 2;
+  const uint8_t* Q = third ? Q3 : Q1;
+  const uint16_t* S = third ? S3 : S1;
+  // column tile 0's code chunk of block 0 and scale column; tile ct adds 8
+  // column pairs (8 * Kdim bytes of codes) and 16 scale columns.  N is a
+  // multiple of 128 (checked by the caller), so every column exists.
+  const int col0 = nb * 128 + c16;
+  const uint8_t* qsrc = Q + ((((int64_t)e * (N / 2) + col0 / 2) * (Kdim / 32) + g) * 2 + (col0 & 1)) * 16;
+  const int64_t qtile = (int64_t)8 * Kdim;
+  const uint16_t* ssrc = S + (int64_t)e * ngr * N + col0;
+  bf16x8_t bias;
+  {
+    const uint32_t bb = kBias136 | (kBias136 << 16);
+    u32x4_t t = u32x4_t{bb, bb, bb, bb};
+    bias = *reinterpret_cast<bf16x8_t*>(&t);
+  }
+
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
+    const int rr = (m0 + c16) < cnt ? (m0 + c16) : (cnt - 1);
+    const int p = (int)min<int64_t>(max(row_beg + rr, 0), TK - 1);
+    const int64_t arow = (MODE == 1) ? (int64_t)min(max(perm_token[p], 0), a_rows - 1) : (int64_t)p;
+    const uint16_t* asrc = A + arow * Kdim + g * 32;
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // two-step register pipeline: block blk in (wa, aa, sa), blk+1 in (wb, ab, sb)
+    u32x4_t wa[8], wbv[8];
+    bf16x8_t aa[4], ab[4];
+    float sa[8], sb[8];
+    auto load = [&](int blk, u32x4_t (&w)[8], bf16x8_t (&a)[4], float (&s)[8]) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * 128);
+        s[ct] = __uint_as_float((uint32_t)ssrc[(int64_t)blk * N + ct * 16] << 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t*>(asrc + (int64_t)blk * Q4G + 8 * j);
+    };
+    auto block = [&](const u32x4_t (&w)[8], const bf16x8_t (&a)[4], const float (&s)[8]) {
+      f32x4_t corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bias, corr, 0, 0, 0);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], dq4(w[ct][j]), t, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[ct][i] = fmaf(s[ct], t[i] - corr[i], acc[ct][i]);
+        // keep one tile's unpacked operands live at a time
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    int blk = wb0;
+    if (blk < wb1) load(blk, wa, aa, sa);
+    while (blk < wb1) {
+      if (blk + 1 < wb1) load(blk + 1, wbv, ab, sb);
+      block(wa, aa, sa);
+      if (blk + 2 < wb1) load(blk + 2, wa, aa, sa);
+      if (blk + 1 < wb1) block(wbv, ab, sb);
+      blk += 2;
+    }
+    // partial tiles -> LDS; slot q = ct*4 + i
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][ct * 4 + i][lane] = acc[ct][i];
+    __syncthreads();
+    const int qg = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int q = qg * 8 + k;
+      const int ct = q >> 2;
+      const int i = q & 3;
+      const int row = m0 + 4 * (lane >> 4) + i;  // D row of the 16x16 MFMA
+      const int colo = nb * 128 + ct * 16 + (lane & 15);
+      if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
+      if (MODE == 1) {
+        const float va = red[0][q][lane] + red[1][q][lane];
+        const float vb = red[2][q][lane] + red[3][q][lane];
+        hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
+      } else {
+        const float v = ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
+        oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_q4(const uint16_t* W, int n, int R, int C, uint8_t* codes, uint16_t* scales,
+                              hipStream_t s) {
+  const int G = R / Q4G;
+  const int cb = (C + 255) / 256;
+  hipLaunchKernelGGL(quantize_q4_kernel, dim3((unsigned)(n * G * cb)), dim3(256), 0, s, W, n, R, C, codes,
+                     scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4_up(const uint16_t* x, int64_t T, const int* perm_token, const uint8_t* Q1,
+                        const uint16_t* S1, const uint8_t* Q3, const uint16_t* S3, const int* offsets,
+                        int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s) {
+  const int NB = (f + 127) / 128;
+  hipLaunchKernelGGL((skinny_q4_kernel<1>), dim3((unsigned)(n * NB)), dim3(256), 0, s, x, perm_token, Q1, S1,
+                     Q3, S3, offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_q4_down(const uint16_t* h, const uint8_t* Q2, const uint16_t* S2, const int* offsets,
+                          int64_t TK, int n, int f, int d, int splits, float* o, hipStream_t s) {
+  const int NB = (d + 127) / 128;
+  hipLaunchKernelGGL((skinny_q4_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(256), 0, s, h,
+                     (const int*)nullptr, Q2, S2, (const uint8_t*)nullptr, (const uint16_t*)nullptr, offsets,
+                     n, f, d, splits, (int)TK, TK, (uint16_t*)nullptr, o);
+  return hipGetLastError();
+}
+
+}  // namespace moe

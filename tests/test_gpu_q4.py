@@ -1,0 +1,126 @@
+"""4-bit expert weights on the GPU: moe_quantize_q4 must reproduce the oracle's
+codes and scales bit for bit, and moe_forward_q4 must match the fp64 oracle run
+on the dequantised weights (bf16 bounds)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import config_inputs, log, sample_rows, to_dev, upload
+from parity import BF16_MAX_REL, BF16_MEAN_REL, assert_rows_close, check_routing
+from synth import bf16_bits_from_f32, bf16_bits_to_f32, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import sparse_mixture_experts_22_amd as moe
+    return moe
+
+
+def _gpu_quantize(bits):
+    """bf16 bit array [n][R][C] -> (codes tensor, scales tensor, codes int8 [n][R][C], scales f32)."""
+    import torch
+    W = to_dev(bits, "bf16")
+    q, s = _moe().quantize_q4(W)
+    torch.cuda.synchronize()
+    n, R, C = bits.shape
+    codes = oracle.unpack_q4(q.cpu().numpy(), n, R, C)
+    scales = bf16_bits_to_f32(s.view(torch.int16).cpu().numpy().view(np.uint16))
+    return q, s, codes, scales
+
+
+def _check_quant(bits):
+    _, _, codes, scales = _gpu_quantize(bits)
+    rc, rs = oracle.quantize_q4(bf16_bits_to_f32(bits))
+    np.testing.assert_array_equal(scales, rs)
+    np.testing.assert_array_equal(codes, rc)
+
+
+def test_quantize_matches_oracle_bit_for_bit():
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((3, 384, 192)) * 0.05).astype(np.float32)
+    W[1, 128:256, 7] = 0.0                          # zero group
+    W[2, 0:128, 9] = 0.0
+    W[2, 5, 9] = 3e-3                               # a single nonzero in its group
+    W[0, :, 11] = np.linspace(-1, 1, 384)          # many exact half-step ties
+    _check_quant(bf16_bits_from_f32(W))
+
+
+def test_quantize_full_size_expert():
+    inp = config_inputs("mixtral_decode")
+    log("quantize W1 expert 0 and W2 expert 7 at full size")
+    _check_quant(inp.W1[0:1])
+    _check_quant(inp.W2[7:8])
+
+
+def _run_q4(inp, rows=None):
+    import torch
+    moe = _moe()
+    dev = upload(inp)
+    q1 = moe.quantize_q4(dev["W1"])
+    q3 = moe.quantize_q4(dev["W3"])
+    q2 = moe.quantize_q4(dev["W2"])
+    y = moe.forward_q4(dev["x"], dev["Wg"], q1, q3, q2, inp.d, inp.f, inp.K)
+    rt = moe.route(dev["x"], dev["Wg"], inp.K, outputs=("topk_idx",))
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
+    sub = check_routing(r, {"topk_idx": rt["topk_idx"].cpu().numpy()}, inp.K)
+
+    def deq(name, e):
+        c, s = oracle.quantize_q4(bf16_bits_to_f32(getattr(inp, name)[e:e + 1]))
+        return oracle.dequantize_q4(c, s)[0]
+
+    rs = np.arange(inp.T) if rows is None else sample_rows(inp.T, rows)
+    ref = oracle.forward_with_selection(inp.f64("x")[rs], inp.f64("Wg"), lambda e: deq("W1", e),
+                                        lambda e: deq("W3", e), lambda e: deq("W2", e), sub[rs])
+    rel = assert_rows_close(y[rs], ref, BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  q4 forward T={inp.T} d={inp.d} f={inp.f} n={inp.n}: max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
+    return y
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (32, 256, 384, 8, 2),     # decode-like: a few rows per expert
+    (5, 128, 128, 4, 1),
+    (300, 256, 256, 8, 2),    # > 16 rows per expert: several passes over the weights
+    (64, 512, 640, 16, 4),
+])
+def test_forward_q4_shapes(T, d, f, n, K):
+    log(f"forward_q4: T={T} d={d} f={f} n={n} K={K}")
+    _run_q4(make_inputs(T, d, f, n, K, dtype="bf16", seed=5150 + T + n))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_q4_mixtral_decode():
+    log("forward_q4 on the Mixtral decode batch")
+    _run_q4(config_inputs("mixtral_decode"), rows=32)
+
+
+def test_forward_q4_of_representable_weights_matches_bf16_forward():
+    # weights q * 2^-k with |q| <= 7 (and 7 reached in every group) survive the
+    # quantizer exactly, so the 4-bit layer must agree with the bf16 layer
+    import torch
+    moe = _moe()
+    rng = np.random.default_rng(77)
+    inp = make_inputs(48, 256, 256, 8, 2, dtype="bf16", seed=78)
+    for name, (R, C) in (("W1", (256, 256)), ("W3", (256, 256)), ("W2", (256, 256))):
+        q = rng.integers(-7, 8, size=(8, R, C)).astype(np.float32)
+        q[:, ::128, :] = 7.0
+        setattr(inp, name, bf16_bits_from_f32(q * np.float32(2.0 ** -6)))
+    dev = upload(inp)
+    y16 = moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], 2)
+    y4 = moe.forward_q4(dev["x"], dev["Wg"], moe.quantize_q4(dev["W1"]), moe.quantize_q4(dev["W3"]),
+                        moe.quantize_q4(dev["W2"]), 256, 256, 2)
+    torch.cuda.synchronize()
+    rel = oracle_rel = np.linalg.norm(y4.cpu().numpy() - y16.cpu().numpy(), axis=1) / \
+        np.linalg.norm(y16.cpu().numpy(), axis=1)
+    assert rel.max() < 5e-3, rel.max()
+
+
+def test_q4_invalid_shapes():
+    import torch
+    moe = _moe()
+    W = torch.zeros((2, 96, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoEError):
+        moe.quantize_q4(W)                           # R not a multiple of 128
