@@ -13,9 +13,13 @@ from .moe_oracle import (  # noqa: F401
     dequantize_q4,
     dispatch,
     expert_capacity,
+    expert_choice_capacity,
+    expert_choice_dispatch,
+    expert_choice_select,
     expert_swiglu,
     forward,
     forward_capacity,
+    forward_expert_choice,
     forward_kept,
     forward_mask_form,
     forward_with_selection,

@@ -28,6 +28,10 @@ Readings where the pages leave a step open (each also listed in the design notes
   * y excludes the residual add that the surrounding block performs.
   * Router statistics (Part 5): f_i counts the T*K assignments once each,
     f_i = counts_i / (T*K), so both shares are 1/N when balanced.
+  * Expert-choice routing (named on the first page without details): the
+    score is the router's softmax probability over experts; each expert takes
+    its C = min(T, ceil(cf * T / n)) best tokens, ties to the lower token
+    index; a chosen (t, e) adds S[t][e] * SwiGLU_e(x_t).
   * 4-bit weights (the page sizes the model at 4 bits but gives no format):
     the format is defined with quantize_q4 below; the layer on such weights is
     the plain forward on the dequantised values.
@@ -151,6 +155,65 @@ def router_stats(logits: np.ndarray, sel: np.ndarray, alpha: float) -> dict:
     prob = full_softmax(lg).mean(axis=0)
     loss = alpha * n * float(np.sum(frac * prob))
     return dict(frac=frac, prob=prob, aux_loss=loss, counts=counts)
+
+
+def expert_choice_capacity(T: int, n: int, capacity_factor: float) -> int:
+    """Tokens each expert takes in expert-choice routing: the batch's tokens
+    spread over the experts times a capacity factor (the average number of
+    experts per token), at most T."""
+    return int(min(T, math.ceil(capacity_factor * T / n)))
+
+
+def expert_choice_select(logits: np.ndarray, C: int):
+    """Expert-based routing ("How Experts Are Chosen (Routing Methods)" in
+    "Mixtral of Experts? Mixture of Experts? Try to explain Mixtral 8x7B"): the
+    experts choose their tokens, each with a fixed capacity.  The score of
+    (token, expert) is the router's probability (softmax over the experts of
+    the token's logits); each expert takes its C best-scoring tokens, ties to
+    the lower token index.
+    Returns chosen [T][n] bool, the scores S [T][n] and, per expert, the gap
+    between its C-th and (C+1)-th best scores (inf when C = T)."""
+    S = full_softmax(logits)
+    T, n = S.shape
+    chosen = np.zeros((T, n), dtype=bool)
+    margin = np.full(n, np.inf)
+    for e in range(n):
+        order = np.argsort(-S[:, e], kind="stable")
+        chosen[order[:C], e] = True
+        if C < T:
+            margin[e] = S[order[C - 1], e] - S[order[C], e]
+    return chosen, S, margin
+
+
+def expert_choice_dispatch(chosen: np.ndarray, C: int):
+    """Rows of expert e are e*C .. e*C+C-1, its chosen tokens in ascending order.
+      perm_token[e*C + j] j-th chosen token of expert e
+      slot_pos[t][e]      row of (t, e), -1 if e did not choose t"""
+    T, n = chosen.shape
+    perm_token = np.empty(n * C, dtype=np.int64)
+    slot_pos = np.full((T, n), -1, dtype=np.int64)
+    for e in range(n):
+        toks = np.nonzero(chosen[:, e])[0]
+        perm_token[e * C:e * C + toks.size] = toks
+        slot_pos[toks, e] = e * C + np.arange(toks.size)
+    return perm_token, slot_pos
+
+
+def forward_expert_choice(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter,
+                          chosen: np.ndarray) -> np.ndarray:
+    """y[t] = sum over the experts that chose t of S[t][e] * SwiGLU_e(x[t]); a
+    token no expert chose gets y = 0 (it passes on through the residual)."""
+    x = _f64(x)
+    S = full_softmax(router_logits(x, Wg))
+    T, n = S.shape
+    y = np.zeros((T, x.shape[1]))
+    for e in range(n):
+        rows = np.nonzero(chosen[:, e])[0]
+        if rows.size == 0:
+            continue
+        out = expert_swiglu(x[rows], _expert(W1, e), _expert(W3, e), _expert(W2, e))
+        y[rows] += S[rows, e][:, None] * out
+    return y
 
 
 def brute_force_topk(logit_row: np.ndarray, K: int) -> tuple:

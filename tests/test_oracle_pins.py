@@ -559,3 +559,62 @@ def test_q4_bf16_round_ties_to_even():
     v = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -(1.0 + 2 ** -8)], dtype=np.float32)
     np.testing.assert_array_equal(oracle.bf16_round(v),
                                   np.array([1.0, 1.0 + 2 ** -6, 1.0, -1.0], dtype=np.float32))
+
+
+# ----------------------------------------------------- expert-choice routing
+# First page, "How Experts Are Chosen (Routing Methods)": experts choose the
+# tokens they process, each with a fixed capacity.
+
+def test_expert_choice_equals_brute_force_subsets():
+    rng = np.random.default_rng(41)
+    T, n, C = 7, 3, 3
+    logits = rng.standard_normal((T, n))
+    logits[4] = logits[2]                       # tokens 2 and 4 tie for every expert
+    chosen, S, _ = oracle.expert_choice_select(logits, C)
+    for e in range(n):
+        best, best_key = None, None
+        for sub in itertools.combinations(range(T), C):   # lexicographic order
+            key = sum(S[list(sub), e])
+            if best is None or key > best_key + 1e-15:
+                best, best_key = sub, key
+        np.testing.assert_array_equal(np.nonzero(chosen[:, e])[0], best)
+
+
+def test_expert_choice_full_capacity_is_dense_mixture():
+    # C = T: every expert takes every token, y = sum_e softmax_e * E_e(x), the
+    # token-choice layer with K = n
+    x, Wg, W1, W3, W2 = _small(T=20, n=4)
+    C = oracle.expert_choice_capacity(20, 4, 4.0)
+    assert C == 20
+    chosen, _, _ = oracle.expert_choice_select(oracle.router_logits(x, Wg), C)
+    assert chosen.all()
+    np.testing.assert_allclose(oracle.forward_expert_choice(x, Wg, W1, W3, W2, chosen),
+                               oracle.forward(x, Wg, W1, W3, W2, 4), rtol=0, atol=1e-12)
+
+
+def test_expert_choice_ties_take_earliest_tokens_and_unchosen_get_zero():
+    # W_g = 0: all scores tie at 1/n, every expert takes tokens 0..C-1
+    x, Wg, W1, W3, W2 = _small(T=24, n=6)
+    C = oracle.expert_choice_capacity(24, 6, 2.0)
+    assert C == 8
+    chosen, S, margin = oracle.expert_choice_select(np.zeros((24, 6)), C)
+    assert (chosen[:C].all()) and not chosen[C:].any() and (margin == 0).all()
+    y = oracle.forward_expert_choice(x, 0 * Wg, W1, W3, W2, chosen)
+    assert (y[C:] == 0).all()
+    ref = sum(oracle.expert_swiglu(x[:C], W1[e], W3[e], W2[e]) for e in range(6)) / 6.0
+    np.testing.assert_allclose(y[:C], ref, rtol=0, atol=1e-13)
+
+
+def test_expert_choice_dispatch_layout():
+    rng = np.random.default_rng(43)
+    T, n = 50, 5
+    C = oracle.expert_choice_capacity(T, n, 1.5)
+    assert C == 15
+    chosen, _, _ = oracle.expert_choice_select(rng.standard_normal((T, n)), C)
+    assert (chosen.sum(axis=0) == C).all()
+    perm, slot = oracle.expert_choice_dispatch(chosen, C)
+    for e in range(n):
+        toks = perm[e * C:(e + 1) * C]
+        assert (np.diff(toks) > 0).all()
+        np.testing.assert_array_equal(slot[toks, e], e * C + np.arange(C))
+    assert ((slot >= 0) == chosen).all()
