@@ -93,7 +93,8 @@ def _time_calls(fn, reps, stream):
 
 def time_extras(moe, x, wg, wsets, K, y, stream, reps):
     """The optional paths on the same resident inputs: router statistics with the
-    load-balancing loss, and the capacity-limited forward (capacity factor 1.0)."""
+    load-balancing loss, the capacity-limited forward (capacity factor 1.0) and
+    the expert-choice forward (capacity factor K: the same expert work as top-K)."""
     T = x.shape[0]
     n = wg.shape[1]
     stats_ms = _time_calls(lambda i=0: moe.route_stats(x, wg, K, 0.01), reps, stream)
@@ -106,11 +107,22 @@ def time_extras(moe, x, wg, wsets, K, y, stream, reps):
     cap_ms = _time_calls(cap_step, reps, stream)
     rc = moe.route_capacity(x, wg, K, 1.0, outputs=("offsets",))
     kept = int(rc["offsets"][-1].item())
+
+    def ec_step(i=0):
+        w1, w3, w2 = wsets[i % 2]
+        moe.forward_expert_choice(x, wg, w1, w3, w2, float(K), y=y)
+
+    ec_ms = _time_calls(ec_step, reps, stream)
+    ec_route_ms = _time_calls(lambda i=0: moe.route_expert_choice(x, wg, float(K), outputs=("slot_pos",)),
+                              reps, stream)
     return {
         "route_stats": {"ms_per_call": round(stats_ms, 4), "aux_loss_alpha_0.01": round(float(st["aux_loss"][0]), 6)},
         "forward_capacity_cf1": {"ms_per_step": round(cap_ms, 4), "tokens_per_s": round(T / (cap_ms * 1e-3), 1),
                                  "capacity": moe.expert_capacity(T, n, K, 1.0),
                                  "dropped_assignments": T * K - kept},
+        "forward_expert_choice_cf_K": {"ms_per_step": round(ec_ms, 4), "tokens_per_s": round(T / (ec_ms * 1e-3), 1),
+                                       "tokens_per_expert": moe.expert_choice_capacity(T, n, float(K)),
+                                       "routing_ms": round(ec_route_ms, 4)},
     }
 
 

@@ -177,6 +177,36 @@ moe_status_t moe_forward_capacity(const void* x, const void* Wg, const void* W1,
                                   int32_t K, double capacity_factor, float* y, moe_stream_t stream);
 
 /*
+ * Expert-choice routing: the second routing method of "How Experts Are Chosen
+ * (Routing Methods)" in "Mixtral of Experts? Mixture of Experts? Try to
+ * explain Mixtral 8x7B": instead of tokens choosing experts, each expert
+ * chooses the tokens it processes, with a fixed capacity.  Reading used here:
+ * the score of (t, e) is the router's probability S[t][e] (softmax of the
+ * token's n logits, fp32); expert e takes the C = min(T, ceil(cf * T / n))
+ * tokens with the largest S[t][e] (ties to the lower token index); a chosen
+ * pair adds S[t][e] * SwiGLU_e(x_t) to y_t, so a token may use 0 .. n experts
+ * and one that no expert chose gets y = 0.  With cf = K the experts do the
+ * same work as top-K token choice.
+ *   moe_expert_choice_capacity  returns C (0 if invalid).
+ *   moe_route_expert_choice     scores[T][n] fp32 (S), perm_token[n*C] int32
+ *                               (rows e*C .. e*C+C-1: expert e's tokens,
+ *                               ascending), slot_pos[T][n] int32 (row of (t, e)
+ *                               or -1); each optional, at least one given.
+ *   moe_forward_expert_choice   the layer (bf16 inputs, fp32 y).
+ * Limits as moe_forward, plus T*n < 2^31; invalid capacity_factor ->
+ * MOE_ERR_INVALID_ARG.
+ */
+int64_t moe_expert_choice_capacity(int64_t T, int32_t n, double capacity_factor);
+
+moe_status_t moe_route_expert_choice(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n,
+                                     double capacity_factor, float* scores, int32_t* perm_token,
+                                     int32_t* slot_pos, moe_stream_t stream);
+
+moe_status_t moe_forward_expert_choice(const void* x, const void* Wg, const void* W1, const void* W3,
+                                       const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                                       double capacity_factor, float* y, moe_stream_t stream);
+
+/*
  * 4-bit expert weights.  The explainer sizes the model at 16 and at 4 bits per
  * parameter ("Why total and active both matter", Part 4 of "Mixture of
  * Experts: Why Mixtral Only Wakes Up Two Specialists") but gives no format;

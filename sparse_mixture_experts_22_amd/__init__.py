@@ -9,8 +9,10 @@ from ._binding import (  # noqa: F401
     MoEError,
     STATUS,
     expert_capacity,
+    expert_choice_capacity,
     forward,
     forward_capacity,
+    forward_expert_choice,
     forward_q4,
     forward_f32,
     forward_traced,
@@ -21,6 +23,7 @@ from ._binding import (  # noqa: F401
     release,
     route,
     route_capacity,
+    route_expert_choice,
     route_f32,
     route_stats,
     route_stats_f32,
@@ -30,5 +33,6 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["forward", "forward_traced", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
            "expert_capacity", "route_capacity", "forward_capacity",
-           "quantize_q4", "forward_q4", "workspace_bytes", "release",
+           "quantize_q4", "forward_q4", "expert_choice_capacity", "route_expert_choice",
+           "forward_expert_choice", "workspace_bytes", "release",
            "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

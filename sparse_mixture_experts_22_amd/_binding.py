@@ -14,7 +14,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
 
 EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32",
            "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
-           "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4", "moe_workspace_bytes",
+           "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4",
+           "moe_expert_choice_capacity", "moe_route_expert_choice", "moe_forward_expert_choice",
+           "moe_workspace_bytes",
            "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
 
 
@@ -72,6 +74,12 @@ def lib() -> ctypes.CDLL:
     L.moe_quantize_q4.restype = ctypes.c_int
     L.moe_forward_q4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
     L.moe_forward_q4.restype = ctypes.c_int
+    L.moe_expert_choice_capacity.argtypes = [i64, i32, f64]
+    L.moe_expert_choice_capacity.restype = i64
+    L.moe_route_expert_choice.argtypes = [vp, vp, i64, i64, i32, f64, vp, vp, vp, vp]
+    L.moe_route_expert_choice.restype = ctypes.c_int
+    L.moe_forward_expert_choice.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, f64, vp, vp]
+    L.moe_forward_expert_choice.restype = ctypes.c_int
     L.moe_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     L.moe_workspace_bytes.restype = ctypes.c_size_t
     L.moe_release.argtypes = []
@@ -251,6 +259,37 @@ def forward_capacity(x, Wg, W1, W3, W2, K, capacity_factor, y=None, stream=None)
     import torch
     return _forward(lib().moe_forward_capacity, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream,
                     mid=(float(capacity_factor),))
+
+
+def expert_choice_capacity(T, n, capacity_factor) -> int:
+    """moe_expert_choice_capacity: min(T, ceil(capacity_factor * T / n)) (0 if invalid)."""
+    return int(lib().moe_expert_choice_capacity(int(T), int(n), float(capacity_factor)))
+
+
+def route_expert_choice(x, Wg, capacity_factor, outputs=("scores", "perm_token", "slot_pos"), stream=None):
+    """moe_route_expert_choice on bf16 x, Wg: dict of scores [T][n], perm_token [n*C], slot_pos [T][n]."""
+    import torch
+    _expect(x, torch.bfloat16, "x", 2)
+    _expect(Wg, torch.bfloat16, "Wg", 2)
+    T, d = x.shape
+    n = Wg.shape[1]
+    if Wg.shape[0] != d:
+        raise ValueError("Wg must be [d][n]")
+    C = max(expert_choice_capacity(T, n, capacity_factor), 0)
+    shapes = {"scores": ((T, n), torch.float32), "perm_token": ((n * C,), torch.int32),
+              "slot_pos": ((T, n), torch.int32)}
+    out = {k: torch.empty(shapes[k][0], dtype=shapes[k][1], device=x.device) for k in outputs}
+    _check(lib().moe_route_expert_choice(_ptr(x), _ptr(Wg), T, d, n, float(capacity_factor),
+                                         _ptr(out.get("scores")), _ptr(out.get("perm_token")),
+                                         _ptr(out.get("slot_pos")), _stream(stream)))
+    return out
+
+
+def forward_expert_choice(x, Wg, W1, W3, W2, capacity_factor, y=None, stream=None):
+    """moe_forward_expert_choice: the layer with expert-choice routing."""
+    import torch
+    return _forward(lambda *a: lib().moe_forward_expert_choice(*a[:9], float(capacity_factor), *a[10:]),
+                    torch.bfloat16, x, Wg, W1, W3, W2, 0, y, stream)
 
 
 def quantize_q4(W, stream=None):

@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 
+#include <algorithm>
 #include <cmath>
 
 #include "moe.h"
@@ -47,10 +48,12 @@ struct Plan {
   int splits = 1;
 };
 
+// `rows`: expert rows of the projections (T*K unless given).
 Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus_per_xcd = 0,
-               bool force_skinny = false) {
+               bool force_skinny = false, int64_t rows = -1) {
   Plan p;
   const int64_t TK = T * K;
+  const int64_t R = rows >= 0 ? rows : TK;
   const int BT = moe::route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   size_t off = 0;
@@ -70,10 +73,10 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
   p.slot_pos = take((size_t)TK * 4);
   if (path == Path::kStats) p.probsum = take((size_t)nb * n * 4);
   if (path == Path::kBf16) {
-    p.skinny = force_skinny || TK <= (int64_t)moe::kSkinnyMaxAvgRows * n;
+    p.skinny = force_skinny || R <= (int64_t)moe::kSkinnyMaxAvgRows * n;
     p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
-    p.h = take((size_t)TK * f * 2);
-    p.o = take((size_t)p.splits * TK * d * 4);
+    p.h = take((size_t)R * f * 2);
+    p.o = take((size_t)p.splits * R * d * 4);
     if (!p.skinny && cus_per_xcd >= 1 && cus_per_xcd <= 64) p.tail = take(moe::prefill_tail_bytes(cus_per_xcd));
   } else if (path == Path::kF32) {
     p.h = take((size_t)TK * f * 4);
@@ -363,6 +366,27 @@ moe_status_t forward_q4(const void* x, const void* Wg, const void* W1q, const vo
   return MOE_OK;
 }
 
+// Tokens per expert of expert-choice routing, min(T, ceil(cf * T / n)), or -1.
+int64_t ec_capacity_of(int64_t T, int32_t n, double cf) {
+  if (!(cf > 0.0) || !std::isfinite(cf) || n < 1 || T < 1) return -1;
+  const double c = std::ceil(cf * (double)T / (double)n);
+  if (c > (double)INT32_MAX) return -1;
+  return std::min<int64_t>(T, (int64_t)c);
+}
+
+moe_status_t check_ec(int64_t T, int64_t d, int64_t f, int32_t n, bool need_f, double cf, int64_t* C) {
+  moe_status_t st = check_shape(T, d, f, n, 1, need_f);
+  if (st != MOE_OK) return st;
+  if (T * (int64_t)n > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "T*n must be < 2^31");
+  if (T == 0) {
+    *C = 0;
+    return MOE_OK;
+  }
+  *C = ec_capacity_of(T, n, cf);
+  if (*C < 1) return fail(MOE_ERR_INVALID_ARG, "capacity_factor must be positive and finite");
+  return MOE_OK;
+}
+
 // Expert capacity ceil(cf * T * K / n), or -1 if cf is not a positive finite
 // number or the capacity does not fit an int.
 int64_t capacity_of(int64_t T, int32_t n, int32_t K, double cf) {
@@ -549,6 +573,85 @@ moe_status_t moe_forward_q4(const void* x, const void* Wg, const void* W1q, cons
                             int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream) {
   return forward_q4(x, Wg, W1q, W1s, W3q, W3s, W2q, W2s, T, d, f, n, K, y,
                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int64_t moe_expert_choice_capacity(int64_t T, int32_t n, double capacity_factor) {
+  const int64_t c = ec_capacity_of(T, n, capacity_factor);
+  return c < 0 ? 0 : c;
+}
+
+moe_status_t moe_route_expert_choice(const void* x, const void* Wg, int64_t T, int64_t d, int32_t n,
+                                     double capacity_factor, float* scores, int32_t* perm_token,
+                                     int32_t* slot_pos, moe_stream_t stream_) {
+  g_last_error.clear();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int64_t C = 0;
+  moe_status_t st = check_ec(T, d, 1, n, false, capacity_factor, &C);
+  if (st != MOE_OK) return st;
+  if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
+  if (!scores && !perm_token && !slot_pos) return fail(MOE_ERR_INVALID_ARG, "at least one output must be non-null");
+  st = check_bf16(d, 0, false, {x, Wg});
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(T, d, 0, n, n, Path::kRouteOnly);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const moe::RouteBuffers r = route_buffers(ws, p, RouteOut{nullptr, scores, nullptr, nullptr, perm_token, slot_pos});
+  MOE_LAUNCH(moe::launch_route_expert_choice(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(Wg),
+                                             T, d, n, (int)C, r, stream),
+             "expert-choice routing launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_expert_choice(const void* x, const void* Wg, const void* W1, const void* W3,
+                                       const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                                       double capacity_factor, float* y, moe_stream_t stream_) {
+  g_last_error.clear();
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  int64_t C = 0;
+  moe_status_t st = check_ec(T, d, f, n, true, capacity_factor, &C);
+  if (st != MOE_OK) return st;
+  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  if (st != MOE_OK) return st;
+  st = check_bf16(d, f, true, {x, Wg, W1, W3, W2, y});
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  int cus = 0;
+  st = cus_per_xcd(&cus);
+  if (st != MOE_OK) return st;
+  const int64_t rows = (int64_t)n * C;
+  const Plan p = make_plan(T, d, f, n, n, Path::kBf16, cus, false, rows);
+  char* ws = nullptr;
+  st = get_workspace(p.total, &ws);
+  if (st != MOE_OK) return st;
+  const moe::RouteBuffers r =
+      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  uint16_t* h = at<uint16_t>(ws, p.h);
+  float* o = at<float>(ws, p.o);
+  const auto* xb = static_cast<const uint16_t*>(x);
+  const auto* w1 = static_cast<const uint16_t*>(W1);
+  const auto* w3 = static_cast<const uint16_t*>(W3);
+  const auto* w2 = static_cast<const uint16_t*>(W2);
+  MOE_LAUNCH(moe::launch_route_expert_choice(xb, static_cast<const uint16_t*>(Wg), T, d, n, (int)C, r, stream),
+             "expert-choice routing launch");
+  if (p.skinny) {
+    MOE_LAUNCH(moe::launch_skinny_up(xb, T, r.perm_token, w1, w3, r.offsets, rows, n, (int)d, (int)f, h, stream),
+               "up-projection kernel launch");
+    MOE_LAUNCH(moe::launch_skinny_down(h, w2, r.offsets, rows, n, (int)f, (int)d, p.splits, o, stream),
+               "down-projection kernel launch");
+  } else {
+    MOE_LAUNCH(moe::launch_prefill_up(xb, T, r.perm_token, w1, w3, r.offsets, rows, n, (int)d, (int)f, cus, h,
+                                      stream),
+               "up-projection kernel launch");
+    float* tail = p.tail ? at<float>(ws, p.tail) : nullptr;
+    MOE_LAUNCH(moe::launch_prefill_down(h, w2, r.offsets, rows, n, (int)f, (int)d, cus, tail, o, stream),
+               "down-projection kernel launch");
+  }
+  // combine over the n (token, expert) slots: scores as weights, -1 = not chosen
+  MOE_LAUNCH(moe::launch_combine(o, p.splits, rows, r.topk_w, r.slot_pos, T, d, n, y, stream),
+             "combine kernel launch");
+  return MOE_OK;
 }
 
 }  // extern "C"

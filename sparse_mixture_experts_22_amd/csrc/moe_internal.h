@@ -67,6 +67,13 @@ hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_
 hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, int64_t d, int n, int K,
                                   float alpha, const RouteBuffers& rb, float* probsum, float* frac,
                                   float* prob, float* aux_loss, hipStream_t s);
+// Expert-choice routing: topk_w receives the scores [T][n] (each token's
+// softmax over the experts); expert e takes its C best tokens (ties to the
+// lower token index) into rows e*C .. e*C+C-1 in ascending token order:
+// perm_token [n*C], slot_pos [T][n] (-1 where e did not choose t),
+// counts[e] = C, offsets[e] = e*C.  1 <= C <= T.
+hipError_t launch_route_expert_choice(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                                     int C, const RouteBuffers& rb, hipStream_t s);
 // Scan + scatter from topk_idx and hist (used after a multi-block router).
 hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s,
                            int cap = INT32_MAX);

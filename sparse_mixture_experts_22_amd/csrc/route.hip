@@ -80,10 +80,29 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
                                int* __restrict__ hist, bool fused, int* __restrict__ counts,
                                int* __restrict__ offsets, int* __restrict__ perm_token,
                                int* __restrict__ slot_pos, int* sel_s, uint32_t* mask_s,
-                               int* hist_s, float* __restrict__ probsum, int cap) {
+                               int* hist_s, float* __restrict__ probsum, int cap,
+                               float* __restrict__ ec_probs) {
   const int tid = threadIdx.x;
   const int cnt = (int)((T - t0) < BT ? (T - t0) : BT);
   __shared__ float tmax_s[32], tsum_s[32];
+  if (ec_probs != nullptr) {
+    // expert-choice scores: each token's full softmax over the n experts
+    if (tid < cnt) {
+      float mx = -INFINITY;
+      for (int e = 0; e < n; ++e) mx = fmaxf(mx, logits_s[tid * ld + e]);
+      float sm = 0.0f;
+      for (int e = 0; e < n; ++e) sm += expf(logits_s[tid * ld + e] - mx);
+      tmax_s[tid] = mx;
+      tsum_s[tid] = sm;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < cnt * n; idx += blockDim.x) {
+      const int i = idx / n;
+      const int e = idx % n;
+      ec_probs[(t0 + i) * n + e] = expf(logits_s[i * ld + e] - tmax_s[i]) / tsum_s[i];
+    }
+    return;
+  }
   for (int e = tid; e < n; e += blockDim.x) {
     hist_s[e] = 0;
     mask_s[e] = 0u;
@@ -189,7 +208,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
     int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm_token,
-    int* __restrict__ slot_pos, float* __restrict__ probsum, int cap) {
+    int* __restrict__ slot_pos, float* __restrict__ probsum, int cap, float* __restrict__ ec_probs) {
   constexpr int BT = 16 * TT;
   constexpr int NP = 16 * NE;
   constexpr int LDL = NP + 1;
@@ -275,7 +294,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
   }
   __syncthreads();
   route_epilogue(logits_s, LDL, BT, t0, T, n, K, topk_idx, topk_w, hist, fused != 0, counts, offsets,
-                 perm_token, slot_pos, sel_s, mask_s, hist_s, probsum, cap);
+                 perm_token, slot_pos, sel_s, mask_s, hist_s, probsum, cap, ec_probs);
 }
 
 // ---------------------------------------------------------------------------
@@ -306,7 +325,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict
   }
   __syncthreads();
   route_epilogue(logits_s, ld, BT, t0, T, n, K, topk_idx, topk_w, hist, false, nullptr, nullptr,
-                 nullptr, nullptr, sel_s, mask_s, hist_s, probsum, INT32_MAX);
+                 nullptr, nullptr, sel_s, mask_s, hist_s, probsum, INT32_MAX, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -408,12 +427,13 @@ namespace {
 
 template <int NE, int TT, int W>
 void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t d, int n, int K,
-                     const RouteBuffers& rb, bool fused, float* probsum, int cap, hipStream_t s) {
+                     const RouteBuffers& rb, bool fused, float* probsum, int cap, float* ec_probs,
+                     hipStream_t s) {
   constexpr int BT = 16 * TT;
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
                      T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
-                     rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap);
+                     rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap, ec_probs);
 }
 
 // Router statistics from the per-block histograms and probability sums (one
@@ -451,18 +471,118 @@ __global__ __launch_bounds__(256) void route_stats_kernel(const int* __restrict_
 
 // Picks the router configuration for the expert count (WgT rows padded to 16).
 void launch_router_bf16(const uint16_t* x, int64_t T, int64_t d, int n, int K, const RouteBuffers& rb,
-                        bool fused, float* probsum, int cap, hipStream_t s) {
+                        bool fused, float* probsum, int cap, hipStream_t s, float* ec_probs = nullptr) {
   const int ne = route_padded_experts(n) / 16;
   if (ne <= 1)
-    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
+    launch_router_t<1, 2, 16>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, ec_probs, s);
   else if (ne <= 2)
-    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
+    launch_router_t<2, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, ec_probs, s);
   else if (ne <= 4)
-    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
+    launch_router_t<4, 2, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, ec_probs, s);
   else if (ne <= 8)
-    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
+    launch_router_t<8, 1, 8>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, ec_probs, s);
   else
-    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, s);
+    launch_router_t<16, 1, 4>(x, rb.wgT, T, d, n, K, rb, fused, probsum, cap, ec_probs, s);
+}
+
+// Expert-choice selection: workgroup e finds the C-th largest score of column
+// e of probs [T][n] by a 4-pass 8-bit radix select on the float bit patterns
+// (scores are >= 0, so their bits order like their values), then keeps every
+// token above that threshold and the earliest tokens equal to it.  Rows go to
+// e*C + j in ascending token order.
+__global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __restrict__ probs, int64_t T,
+                                                             int n, int C, int* __restrict__ perm_token,
+                                                             int* __restrict__ slot_pos,
+                                                             int* __restrict__ counts,
+                                                             int* __restrict__ offsets) {
+  __shared__ int hist[256];
+  __shared__ uint32_t prefix_s;
+  __shared__ int need_s;
+  __shared__ int scan_s[1024];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* col = probs + e;
+  auto key = [&](int64_t t) -> uint32_t { return __float_as_uint(col[t * n]); };
+  if (tid == 0) {
+    prefix_s = 0u;
+    need_s = C;
+    counts[e] = C;
+    offsets[e] = e * C;
+    if (e == n - 1) offsets[n] = n * C;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t himask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = prefix_s;
+    for (int64_t t = tid; t < T; t += 1024) {
+      const uint32_t k = key(t);
+      if ((k & himask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0;
+      int dg = 0;
+      for (dg = 255; dg > 0; --dg) {
+        if (cum + hist[dg] >= need_s) break;
+        cum += hist[dg];
+      }
+      need_s -= cum;
+      prefix_s = prefix | ((uint32_t)dg << shift);
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = prefix_s;  // the C-th largest key
+  const int need = need_s;        // tokens equal to it that are taken (earliest first)
+  // contiguous token chunk of this thread
+  const int64_t chunk = (T + 1023) / 1024;
+  const int64_t b0 = min<int64_t>(T, tid * chunk);
+  const int64_t b1 = min<int64_t>(T, b0 + chunk);
+  int n_eq = 0;
+  for (int64_t t = b0; t < b1; ++t) n_eq += key(t) == thr;
+  // exclusive scan of n_eq over threads (Hillis-Steele on LDS)
+  scan_s[tid] = n_eq;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? scan_s[tid - off] : 0;
+    __syncthreads();
+    scan_s[tid] += v;
+    __syncthreads();
+  }
+  const int eq_before = scan_s[tid] - n_eq;
+  __syncthreads();
+  int n_sel = 0;
+  {
+    int eq_seen = eq_before;
+    for (int64_t t = b0; t < b1; ++t) {
+      const uint32_t k = key(t);
+      if (k > thr) ++n_sel;
+      else if (k == thr) n_sel += (eq_seen++ < need);
+    }
+  }
+  scan_s[tid] = n_sel;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? scan_s[tid - off] : 0;
+    __syncthreads();
+    scan_s[tid] += v;
+    __syncthreads();
+  }
+  int pos = e * C + (scan_s[tid] - n_sel);
+  int eq_seen = eq_before;
+  for (int64_t t = b0; t < b1; ++t) {
+    const uint32_t k = key(t);
+    bool sel = k > thr;
+    if (k == thr) sel = eq_seen++ < need;
+    if (sel) {
+      perm_token[pos] = (int)t;
+      slot_pos[t * n + e] = pos;
+      ++pos;
+    } else {
+      slot_pos[t * n + e] = -1;
+    }
+  }
 }
 
 }  // namespace
@@ -504,6 +624,21 @@ hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_
   const int nb = (int)((T + BT - 1) / BT);
   hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(256), 0, s, rb.hist, probsum, nb, T, n, K, alpha,
                      frac, prob, aux_loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_expert_choice(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
+                                     int C, const RouteBuffers& rb, hipStream_t s) {
+  const int NP = route_padded_experts(n);
+  hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
+                     dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch_router_bf16(x, T, d, n, 1, rb, false, nullptr, INT32_MAX, s, rb.topk_w);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(expert_choice_kernel, dim3((unsigned)n), dim3(1024), 0, s, rb.topk_w, T, n, C,
+                     rb.perm_token, rb.slot_pos, rb.counts, rb.offsets);
   return hipGetLastError();
 }
 
