@@ -314,6 +314,8 @@ KERNEL_SOURCES = {
     "grouped_gemm_kernel<2>": ["csrc/gemm_prefill.hip", "csrc/moe_internal.h", "build.py"],
     "skinny_kernel<1>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
     "skinny_kernel<2>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
+    "skinny_q4_kernel<1>": ["csrc/quant4.hip", "csrc/moe_internal.h", "build.py"],
+    "skinny_q4_kernel<2>": ["csrc/quant4.hip", "csrc/moe_internal.h", "build.py"],
 }
 
 

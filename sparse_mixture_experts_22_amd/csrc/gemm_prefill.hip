@@ -484,30 +484,38 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
 }
 
 // Sums the k-pieces of each split tile in piece order and stores the rows of
-// o it owns.  Workgroup b covers 4 rows of leftover tile (b / 64) % 32 of XCD
-// b / 2048; it recomputes the XCD's plan exactly as the GEMM did.
+// o it owns.  Workgroup b covers 16 rows of leftover tile t = (b / 16) % tmax
+// of XCD b / (16 * tmax) (tmax = cus / 2 bounds the leftover tiles of an XCD
+// that are split); it recomputes the XCD's plan exactly as the GEMM did.
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict__ offsets, int n, int N,
                                                           int nk, int cus, const float* __restrict__ tail_ws,
                                                           float* __restrict__ o) {
   const int NT = (N + 255) / 256;
-  const int x = blockIdx.x / (32 * 64);
-  const int t = (blockIdx.x / 64) % 32;
-  const int rblk = blockIdx.x % 64;
+  const int tmax = cus / 2;
+  const int x = blockIdx.x / (16 * tmax);
+  const int t = (blockIdx.x / 16) % tmax;
+  const int rblk = blockIdx.x % 16;
   const XcdPlan pl = xcd_plan(count_tiles(offsets, n, NT), x, cus, nk, true);
   if (pl.s == 1 || t >= pl.r) return;
   Tile tc;
   if (!tile_at(offsets, n, NT, pl.beg + pl.q + t, tc)) return;
-  const int col = threadIdx.x;
-  const int c = tc.nt * 256 + col;
-  if (c >= N) return;
+  // thread -> (row of 4 in this block's 16, 4 consecutive columns)
+  const int c4 = (threadIdx.x & 63) * 4;
+  const int c = tc.nt * 256 + c4;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int row = rblk * 4 + rr;
+  for (int k = 0; k < 4; ++k) {
+    const int row = rblk * 16 + (threadIdx.x >> 6) * 4 + k;
     if (row >= tc.rows) break;
-    float sum = 0.0f;
+    f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < pl.s; ++p)
-      sum += tail_ws[(int64_t)(x * cus + p * pl.r + t) * (BM * BN) + row * BN + col];
-    o[(int64_t)(tc.row0 + row) * N + c] = sum;
+      sum += *reinterpret_cast<const f32x4_t*>(tail_ws + (int64_t)(x * cus + p * pl.r + t) * (BM * BN) +
+                                                row * BN + c4);
+    float* dst = o + (int64_t)(tc.row0 + row) * N + c;
+    if (c + 3 < N) {
+      *reinterpret_cast<f32x4_t*>(dst) = sum;
+    } else {
+      for (int j = 0; j < 4 && c + j < N; ++j) dst[j] = sum[j];
+    }
   }
 }
 
@@ -540,10 +548,10 @@ hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int*
                      h, (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, (int)TK,
                      (int)TK, cus_per_xcd, (uint16_t*)nullptr, o, tail_ws);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || tail_ws == nullptr) return e;
-  // leftover tiles per XCD are at most cus / 2 <= 32 (cus <= 64 is checked by the caller)
-  hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds * 32 * 64), dim3(256), 0, s, offsets, n, d, f / BK,
-                     cus_per_xcd, tail_ws, o);
+  if (e != hipSuccess || tail_ws == nullptr || cus_per_xcd < 2) return e;  // fewer CUs never split
+  // split leftover tiles per XCD are at most cus / 2; 16 workgroups of 16 rows per tile
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds * (cus_per_xcd / 2) * 16), dim3(256), 0, s, offsets, n, d,
+                     f / BK, cus_per_xcd, tail_ws, o);
   return hipGetLastError();
 }
 

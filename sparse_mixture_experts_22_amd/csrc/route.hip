@@ -489,20 +489,26 @@ void launch_router_bf16(const uint16_t* x, int64_t T, int64_t d, int n, int K, c
 // e of probs [T][n] by a 4-pass 8-bit radix select on the float bit patterns
 // (scores are >= 0, so their bits order like their values), then keeps every
 // token above that threshold and the earliest tokens equal to it.  Rows go to
-// e*C + j in ascending token order.
+// e*C + j in ascending token order.  The column is staged in LDS when it fits.
+constexpr int kEcLdsKeys = 32768;  // 128 KiB of keys
 __global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __restrict__ probs, int64_t T,
                                                              int n, int C, int* __restrict__ perm_token,
                                                              int* __restrict__ slot_pos,
                                                              int* __restrict__ counts,
                                                              int* __restrict__ offsets) {
+  __shared__ uint32_t keys_s[kEcLdsKeys];
   __shared__ int hist[256];
+  __shared__ int suffix[256];
   __shared__ uint32_t prefix_s;
   __shared__ int need_s;
   __shared__ int scan_s[1024];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
   const float* col = probs + e;
-  auto key = [&](int64_t t) -> uint32_t { return __float_as_uint(col[t * n]); };
+  const bool staged = T <= kEcLdsKeys;
+  if (staged)
+    for (int64_t t = tid; t < T; t += 1024) keys_s[t] = __float_as_uint(col[t * n]);
+  auto key = [&](int64_t t) -> uint32_t { return staged ? keys_s[t] : __float_as_uint(col[t * n]); };
   if (tid == 0) {
     prefix_s = 0u;
     need_s = C;
@@ -513,23 +519,31 @@ __global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __rest
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t himask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
     const uint32_t prefix = prefix_s;
+    const int need = need_s;
     for (int64_t t = tid; t < T; t += 1024) {
       const uint32_t k = key(t);
       if ((k & himask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      int dg = 0;
-      for (dg = 255; dg > 0; --dg) {
-        if (cum + hist[dg] >= need_s) break;
-        cum += hist[dg];
+    // suffix[dg] = number of candidates with digit >= dg (inclusive scan from the top)
+    if (tid < 256) suffix[tid] = hist[tid];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int v = (tid < 256 && tid + off < 256) ? suffix[tid + off] : 0;
+      __syncthreads();
+      if (tid < 256) suffix[tid] += v;
+      __syncthreads();
+    }
+    // the selected digit: its suffix reaches `need`, the next one's does not
+    if (tid < 256) {
+      const int above = tid < 255 ? suffix[tid + 1] : 0;
+      if (suffix[tid] >= need && above < need) {
+        need_s = need - above;
+        prefix_s = prefix | ((uint32_t)tid << shift);
       }
-      need_s -= cum;
-      prefix_s = prefix | ((uint32_t)dg << shift);
     }
     __syncthreads();
   }
