@@ -7,11 +7,14 @@
 // small batch every expert is still touched, and the layer is bound by reading
 // 3*d*f bf16 weights per touched expert.
 //
-// Work unit: one workgroup (4 waves) per (expert, 128-column block[, K split]).
-// The 4 waves split the reduction dimension; each lane loads 8 rows x 16 bytes
-// of the weight block (one 8x8 bf16 block), transposes it in registers and
-// feeds eight v_mfma_f32_16x16x32_bf16 directly as B operands - the weights
-// never pass through LDS.  The MFMA column index c of fragment j stands for
+// Work unit: one workgroup (4 waves) per (expert, 256-column block[, K split]);
+// each wave streams one 128-column half.  A workgroup thus reads 512
+// contiguous bytes of every weight row it touches (its two column halves at
+// the same rows), the pattern that streamed fastest in probes (6.2 TB/s
+// against 5.8 for 256-byte segments), and a decode launch is resident in one
+// round.  Each lane loads 8 rows x 16 bytes of the weight block (one 8x8 bf16
+// block), transposes it in registers and feeds eight v_mfma_f32_16x16x32_bf16
+// directly as B operands - the weights never pass through LDS.  The MFMA column index c of fragment j stands for
 // weight column col0 + c*8 + j.  A fragments (16 token rows) come straight
 // from global memory (x or h is tiny and stays in L2).  Loads of the next K
 // step are issued before the MFMAs of the current one.  The 4 partial tiles
@@ -58,10 +61,11 @@ __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t&
     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fr[c], acc[c], 0, 0, 0);
 }
 
-// MODE 1: up.  Waves 0-1 stream W1, waves 2-3 stream W3, each over half of K;
-//         A rows are gathered from x via perm_token; h = SiLU(a) * b in bf16.
-// MODE 2: down.  The 4 waves stream W2 over quarters of this split's K range;
-//         A rows are h; o[split] receives the fp32 partial sum.
+// MODE 1: up.  Wave w streams matrix w/2 (W1, W3) over the whole of K for
+//         column half w%2; A rows are gathered from x via perm_token;
+//         h = SiLU(a) * b in bf16.
+// MODE 2: down.  Wave w streams W2 for column half w/2 over half w%2 of this
+//         split's K range; A rows are h; o[split] receives the fp32 partial sum.
 // With the ping-pong buffers a wave keeps two K steps of loads in flight
 // (2 workgroups per CU).  The variant without them fits 4 workgroups per CU
 // (a decode launch is resident in one round) but measured slower: per-wave
@@ -79,7 +83,7 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
   __shared__ float red[4][32][64];  // per-wave partial accumulators
 
-  const int NB = (N + 127) / 128;
+  const int NB = (N + 255) / 256;
   int bid = blockIdx.x;
   const int sp = bid % splits;
   bid /= splits;
@@ -96,16 +100,17 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  // reduction range of this wave, in steps of 32
-  constexpr int KPARTS = (MODE == 1) ? 2 : 4;
-  const int part = (MODE == 1) ? (wave & 1) : wave;
+  // reduction range and column half of this wave, in steps of 32
+  constexpr int KPARTS = (MODE == 1) ? 1 : 2;
+  const int part = (MODE == 1) ? 0 : (wave & 1);
+  const int half = (MODE == 1) ? (wave & 1) : (wave >> 1);
   const int nkc = Kdim / 32;
   const int kc0 = (int)((int64_t)sp * nkc / splits);
   const int kc1 = (int)((int64_t)(sp + 1) * nkc / splits);
   const int wk0 = kc0 + (int)((int64_t)part * (kc1 - kc0) / KPARTS);
   const int wk1 = kc0 + (int)((int64_t)(part + 1) * (kc1 - kc0) / KPARTS);
 
-  const int col0 = nb * 128 + r16 * 8;
+  const int col0 = nb * 256 + half * 128 + r16 * 8;
   const bool b_ok = col0 < N;
   const uint16_t* bmat = (MODE == 1 && wave >= 2) ? B3 : B1;
   const uint16_t* bsrc = bmat + (int64_t)e * Kdim * N + (b_ok ? col0 : 0) + (int64_t)(g * 8) * N;
@@ -158,25 +163,29 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) red[wave][c * 4 + j][lane] = acc[c][j];
     __syncthreads();
-    // thread (qg = tid/64, lane) finishes slots q = qg*8 .. qg*8+7
+    // thread (qg = tid/64, lane) finishes slots q = qg*8 .. qg*8+7 of both
+    // column halves.  MODE 1: a of half ch is wave ch's, b is wave 2+ch's;
+    // MODE 2: the two k halves of column half ch are waves 2ch and 2ch+1.
     const int qg = tid >> 6;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = qg * 8 + i;
-      const int c = q >> 2;
-      const int j = q & 3;
-      const int row = m0 + 4 * (lane >> 4) + j;  // D row of the 16x16 MFMA
-      const int colo = nb * 128 + (lane & 15) * 8 + c;
-      if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
-      if (MODE == 1) {
-        const float va = red[0][q][lane] + red[1][q][lane];
-        const float vb = red[2][q][lane] + red[3][q][lane];
-        hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
-      } else {
-        const float v = ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
-        oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = qg * 8 + i;
+        const int c = q >> 2;
+        const int j = q & 3;
+        const int row = m0 + 4 * (lane >> 4) + j;  // D row of the 16x16 MFMA
+        const int colo = nb * 256 + ch * 128 + (lane & 15) * 8 + c;
+        if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
+        if (MODE == 1) {
+          const float va = red[ch][q][lane];
+          const float vb = red[2 + ch][q][lane];
+          hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
+        } else {
+          const float v = red[2 * ch][q][lane] + red[2 * ch + 1][q][lane];
+          oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+        }
       }
-    }
   }
 }
 
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
 hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                             const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
                             uint16_t* h, hipStream_t s) {
-  const int NB = (f + 127) / 128;
+  const int NB = (f + 255) / 256;
   hipLaunchKernelGGL((skinny_kernel<1>), dim3((unsigned)(n * NB)), dim3(256), 0, s, x, perm_token,
                      W1, W3, offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr);
   return hipGetLastError();
@@ -193,7 +202,7 @@ hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token,
 
 hipError_t launch_skinny_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
                               int n, int f, int d, int splits, float* o, hipStream_t s) {
-  const int NB = (d + 127) / 128;
+  const int NB = (d + 255) / 256;
   hipLaunchKernelGGL((skinny_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(256), 0, s, h,
                      (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, splits,
                      (int)TK, TK, (uint16_t*)nullptr, o);

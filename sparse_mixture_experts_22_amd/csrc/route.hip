@@ -203,7 +203,9 @@ __global__ __launch_bounds__(256) void wg_transpose_kernel(const uint16_t* __res
 // bf16 router.  NE expert tiles of 16, TT token tiles of 16 (BT = 16*TT), W
 // waves splitting the reduction over d in steps of 32.  Lane (r = l%16,
 // g = l/16) supplies A = x[token r][k + 8g ..] and B = WgT[expert r][k + 8g ..].
-template <int NE, int TT, int W>
+// DIRECT (one routing block, n <= 16): B is gathered from W_g [d][n] itself
+// (8 two-byte loads per fragment), so no transposed copy has to be made first.
+template <int NE, int TT, int W, bool DIRECT = false>
 __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
     int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
@@ -235,6 +237,17 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
   const uint16_t* bp[NE];
 #pragma unroll
   for (int et = 0; et < NE; ++et) bp[et] = WgT + (int64_t)(et * 16 + r) * d + g * 8;
+  // DIRECT: WgT is W_g [d][n]; lane r < n reads column r, rows k + 8g + i
+  const bool b_col = !DIRECT || r < n;
+  const uint16_t* bcol = WgT + (int64_t)(g * 8) * n + (b_col ? r : 0);
+  auto load_b = [&](int et, int kc) -> bf16x8_t {
+    if (!DIRECT) return *reinterpret_cast<const bf16x8_t*>(bp[et] + kc * 32);
+    typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+    u16x8_t v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = b_col ? bcol[(int64_t)(kc * 32 + i) * n] : (uint16_t)0;
+    return *reinterpret_cast<bf16x8_t*>(&v);
+  };
 
   f32x4_t acc[TT][NE];
 #pragma unroll
@@ -255,8 +268,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
       for (int tt = 0; tt < TT; ++tt)
         a[u][tt] = *reinterpret_cast<const bf16x8_t*>(ap[tt] + (kc + u) * 32);
 #pragma unroll
-      for (int et = 0; et < NE; ++et)
-        b[u][et] = *reinterpret_cast<const bf16x8_t*>(bp[et] + (kc + u) * 32);
+      for (int et = 0; et < NE; ++et) b[u][et] = load_b(et, kc + u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -269,7 +281,7 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
   for (; kc < kc1; ++kc) {
 #pragma unroll
     for (int et = 0; et < NE; ++et) {
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(bp[et] + kc * 32);
+      const bf16x8_t b = load_b(et, kc);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ap[tt] + kc * 32);
@@ -425,13 +437,13 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int* __restrict__ top
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int NE, int TT, int W>
+template <int NE, int TT, int W, bool DIRECT = false>
 void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t d, int n, int K,
                      const RouteBuffers& rb, bool fused, float* probsum, int cap, float* ec_probs,
                      hipStream_t s) {
   constexpr int BT = 16 * TT;
   const int64_t nb = (T + BT - 1) / BT;
-  hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
+  hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W, DIRECT>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
                      T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
                      rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap, ec_probs);
 }
@@ -608,15 +620,21 @@ int route_padded_experts(int n) { return (n + 15) / 16 * 16; }
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
                              int K, const RouteBuffers& rb, hipStream_t s, hipEvent_t after_router,
                              int cap) {
-  const int NP = route_padded_experts(n);
-  hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
-                     dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int BT = route_block_tokens(n);
   const int64_t nb = (T + BT - 1) / BT;
   const bool fused = nb == 1;
-  launch_router_bf16(x, T, d, n, K, rb, fused, nullptr, cap, s);
+  hipError_t e;
+  if (fused && n <= 16) {
+    // one routing block (decode batches): read W_g in place, no transposed copy
+    launch_router_t<1, 2, 16, true>(x, Wg, T, d, n, K, rb, true, nullptr, cap, nullptr, s);
+  } else {
+    const int NP = route_padded_experts(n);
+    hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
+                       dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_router_bf16(x, T, d, n, K, rb, fused, nullptr, cap, s);
+  }
   e = hipGetLastError();
   if (e == hipSuccess && after_router != nullptr) e = hipEventRecord(after_router, s);
   if (e != hipSuccess || fused) return e;
