@@ -17,13 +17,13 @@
 // 4t) gives two bf16 values 128 + u = 136 + q of an MFMA B operand.
 //
 // Projection kernel (one workgroup of 4 waves per (expert, 128 columns[, K
-// split])): lane (c = l%16, g = l/16) of column tile ct loads the 16 bytes of
-// column ct*16 + c, chunk 4*blk + g: reduction indices 128blk + 32g + 0..31,
+// split])): lane (c = l%16, g = l/16) of a wave's column tile ct loads the 16
+// bytes of the tile's column c, chunk 4*blk + g: reduction indices 128blk + 32g + 0..31,
 // four MFMA B operands (word j: 128blk + 32g + 8j + 0..7).  The A operand of
 // lane (row, g) uses the same reduction indices, so each 16x16x32 MFMA j sums
 // over 32 indices of one 128-group.  Per group and column tile the MFMAs give
 // sum_k x_k (136 + q_k); one extra MFMA chain against a splat of 136 gives
-// 136 sum_k x_k (shared by the 8 column tiles), and
+// 136 sum_k x_k (shared by the wave's column tiles), and
 //   acc += s[g][col] * (tile - correction)
 // applies the scale once per group.  The rest follows the bf16 weight-
 // streaming kernels: waves split the reduction, partials are summed in LDS in
@@ -35,6 +35,11 @@ namespace moe {
 namespace {
 
 constexpr int Q4G = 128;            // reduction indices per scale group
+#ifndef MOE_Q4_STAGES
+#define MOE_Q4_STAGES 3
+#endif
+constexpr int Q4_STAGES = MOE_Q4_STAGES;  // blocks of codes in the register ring
+constexpr int Q4_TILES = 4;               // 16-column MFMA tiles per wave
 constexpr uint32_t kBias136 = 0x4308u;  // bf16 136.0
 
 __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ W, int n, int R,
@@ -84,17 +89,21 @@ __device__ __forceinline__ bf16x8_t dq4(uint32_t w) {
   return *reinterpret_cast<bf16x8_t*>(&r);
 }
 
-// MODE 1: up.  Waves 0-1 stream W1 codes, waves 2-3 W3, each over half of
-//         the groups; A rows gathered from x; h = SiLU(a) * b in bf16.
-// MODE 2: down.  The 4 waves split this split's groups; o[split] partials.
+// A workgroup covers 128 columns; a wave streams Q4_TILES = 4 column tiles
+// (64 columns), which keeps every in-flight load in a VGPR (no register
+// spilling, two to three waves per SIMD).
+// MODE 1: up.  Wave w streams matrix w/2 (W1, W3) for column half w%2 over
+//         all groups; A rows gathered from x; h = SiLU(a) * b in bf16.
+// MODE 2: down.  Wave w streams column half w/2 over half w%2 of this split's
+//         groups; o[split] receives the fp32 partial sums.
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
+__global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint8_t* __restrict__ Q1, const uint16_t* __restrict__ S1,
     const uint8_t* __restrict__ Q3, const uint16_t* __restrict__ S3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ float red[4][32][64];
+  __shared__ float red[4][4 * Q4_TILES][64];
 
   const int NB = (N + 127) / 128;
   int bid = blockIdx.x;
@@ -113,8 +122,9 @@ __global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
   const int c16 = lane & 15;
   const int g = lane >> 4;
 
-  constexpr int KPARTS = (MODE == 1) ? 2 : 4;
-  const int part = (MODE == 1) ? (wave & 1) : wave;
+  constexpr int KPARTS = (MODE == 1) ? 1 : 2;
+  const int part = (MODE == 1) ? 0 : (wave & 1);
+  const int half = (MODE == 1) ? (wave & 1) : (wave >> 1);
   const int ngr = Kdim / Q4G;
   const int kb0 = (int)((int64_t)sp * ngr / splits);
   const int kb1 = (int)((int64_t)(sp + 1) * ngr / splits);
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
   // column tile 0's code chunk of block 0 and scale column; tile ct adds 8
   // column pairs (8 * Kdim bytes of codes) and 16 scale columns.  N is a
   // multiple of 128 (checked by the caller), so every column exists.
-  const int col0 = nb * 128 + c16;
+  const int col0 = nb * 128 + half * 64 + c16;
   const uint8_t* qsrc = Q + ((((int64_t)e * (N / 2) + col0 / 2) * (Kdim / 32) + g) * 2 + (col0 & 1)) * 16;
   const int64_t qtile = (int64_t)8 * Kdim;
   const uint16_t* ssrc = S + (int64_t)e * ngr * N + col0;
@@ -144,29 +154,30 @@ __global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
     const int64_t arow = (MODE == 1) ? (int64_t)min(max(perm_token[p], 0), a_rows - 1) : (int64_t)p;
     const uint16_t* asrc = A + arow * Kdim + g * 32;
 
-    f32x4_t acc[8];
+    f32x4_t acc[Q4_TILES];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < Q4_TILES; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // two-step register pipeline: block blk in (wa, aa, sa), blk+1 in (wb, ab, sb)
-    u32x4_t wa[8], wbv[8];
-    bf16x8_t aa[4], ab[4];
-    float sa[8], sb[8];
-    auto load = [&](int blk, u32x4_t (&w)[8], bf16x8_t (&a)[4], float (&s)[8]) {
+    // register ring of Q4_STAGES blocks: the loads of the next Q4_STAGES-1
+    // blocks are in flight while one block is multiplied
+    u32x4_t wq[Q4_STAGES][Q4_TILES];
+    bf16x8_t aq[Q4_STAGES][4];
+    float sq[Q4_STAGES][Q4_TILES];
+    auto load = [&](int blk, u32x4_t (&w)[Q4_TILES], bf16x8_t (&a)[4], float (&s)[Q4_TILES]) {
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
+      for (int ct = 0; ct < Q4_TILES; ++ct) {
         w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * 128);
         s[ct] = __uint_as_float((uint32_t)ssrc[(int64_t)blk * N + ct * 16] << 16);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t*>(asrc + (int64_t)blk * Q4G + 8 * j);
     };
-    auto block = [&](const u32x4_t (&w)[8], const bf16x8_t (&a)[4], const float (&s)[8]) {
+    auto block = [&](const u32x4_t (&w)[Q4_TILES], const bf16x8_t (&a)[4], const float (&s)[Q4_TILES]) {
       f32x4_t corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bias, corr, 0, 0, 0);
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
+      for (int ct = 0; ct < Q4_TILES; ++ct) {
         f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], dq4(w[ct][j]), t, 0, 0, 0);
@@ -176,38 +187,47 @@ __global__ __launch_bounds__(256, 1) void skinny_q4_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    int blk = wb0;
-    if (blk < wb1) load(blk, wa, aa, sa);
-    while (blk < wb1) {
-      if (blk + 1 < wb1) load(blk + 1, wbv, ab, sb);
-      block(wa, aa, sa);
-      if (blk + 2 < wb1) load(blk + 2, wa, aa, sa);
-      if (blk + 1 < wb1) block(wbv, ab, sb);
-      blk += 2;
+#pragma unroll
+    for (int st = 0; st < Q4_STAGES - 1; ++st)
+      if (wb0 + st < wb1) load(wb0 + st, wq[st], aq[st], sq[st]);
+    for (int blk = wb0; blk < wb1; blk += Q4_STAGES) {
+#pragma unroll
+      for (int st = 0; st < Q4_STAGES; ++st) {
+        const int ahead = blk + st + Q4_STAGES - 1;
+        if (ahead < wb1)
+          load(ahead, wq[(st + Q4_STAGES - 1) % Q4_STAGES], aq[(st + Q4_STAGES - 1) % Q4_STAGES],
+               sq[(st + Q4_STAGES - 1) % Q4_STAGES]);
+        if (blk + st < wb1) block(wq[st], aq[st], sq[st]);
+      }
     }
-    // partial tiles -> LDS; slot q = ct*4 + i
+    // partial tiles -> LDS; slot q = ct*4 + i.  MODE 1: a of column half ch
+    // is wave ch's, b is wave 2+ch's; MODE 2: the k halves of column half ch
+    // are waves 2ch and 2ch+1.
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+    for (int ct = 0; ct < Q4_TILES; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][ct * 4 + i][lane] = acc[ct][i];
     __syncthreads();
-    const int qg = tid >> 6;
+    {
+      const int ch = tid >> 7;           // column half finished by this thread
+      const int q0 = ((tid >> 6) & 1) * 8;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int q = qg * 8 + k;
-      const int ct = q >> 2;
-      const int i = q & 3;
-      const int row = m0 + 4 * (lane >> 4) + i;  // D row of the 16x16 MFMA
-      const int colo = nb * 128 + ct * 16 + (lane & 15);
-      if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
-      if (MODE == 1) {
-        const float va = red[0][q][lane] + red[1][q][lane];
-        const float vb = red[2][q][lane] + red[3][q][lane];
-        hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
-      } else {
-        const float v = ((red[0][q][lane] + red[1][q][lane]) + red[2][q][lane]) + red[3][q][lane];
-        oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+      for (int k = 0; k < 8; ++k) {
+        const int q = q0 + k;
+        const int ct = q >> 2;
+        const int i = q & 3;
+        const int row = m0 + 4 * (lane >> 4) + i;  // D row of the 16x16 MFMA
+        const int colo = nb * 128 + ch * 64 + ct * 16 + (lane & 15);
+        if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
+        if (MODE == 1) {
+          const float va = red[ch][q][lane];
+          const float vb = red[2 + ch][q][lane];
+          hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
+        } else {
+          const float v = red[2 * ch][q][lane] + red[2 * ch + 1][q][lane];
+          oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
+        }
       }
     }
   }
