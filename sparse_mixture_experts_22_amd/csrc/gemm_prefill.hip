@@ -190,6 +190,12 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 constexpr int SA = MOE_RING_A;  // A super-stages (64 k each)
 constexpr int SB = MOE_RING_B;  // B stages (32 k each)
 static_assert(SA >= 2 && SB >= 2 && 2 * SA + SB <= 10, "LDS budget is 160 KiB");
+// Row blocks of a wave's second MFMA burst that are issued before the step's
+// refill loads (0..4).
+#ifndef MOE_LOAD_AFTER
+#define MOE_LOAD_AFTER 2
+#endif
+constexpr int LOAD_AFTER = MOE_LOAD_AFTER;
 constexpr int A_LOADS = 8;  // 1 KiB loads per A-loader wave per super-stage
 constexpr int B_LOADS = 4;  // 1 KiB loads per B-loader wave per stage
 // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
@@ -373,11 +379,11 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   // The barrier that publishes step kt+1 sits between them: before it, each
   // wave has its sub-step-1 fragments of step kt in registers (lgkmcnt(0))
   // and waits until its own loads holding step kt+1 have landed (vmcnt);
-  // after it, the slots that only step kt used are free and are refilled
-  // (B: every step, with the step SB ahead; A: after odd steps, when a whole
-  // super-stage has been consumed, with the super-stage SA ahead), while the
-  // sub-step-0 fragments of step kt+1 are read during the sub-step-1 MFMAs of
-  // step kt.  Loads past the end reload the last k-slice into slots nobody
+  // after it, the sub-step-0 fragments of step kt+1 are read during the
+  // sub-step-1 MFMAs of step kt, and then the slots that only step kt used
+  // are refilled (B: every step, with the step SB ahead; A: after odd steps,
+  // when a whole super-stage has been consumed, with the super-stage SA
+  // ahead).  Loads past the end reload the last k-slice into slots nobody
   // reads again, so the count of outstanding loads never changes.  The loop
   // runs over pairs of steps so the parity of kt is a compile-time constant.
   const int nk = tc.k1 - tc.k0;  // even: Kdim and the pieces are multiples of 64 k
@@ -397,15 +403,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   auto step = [&](int kt, auto par_c) {
     constexpr int par = decltype(par_c)::value;
     read_frags(kt, par, 1, fa1, fb1);
-#if MOE_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
     mfma_step(fa0, fb0);
     interleave();
-#if MOE_SETPRIO
-    fence();
-    __builtin_amdgcn_s_setprio(0);
-#endif
     if (b_loader)
       __builtin_amdgcn_s_waitcnt(WAIT_AHEAD_B);
     else
@@ -414,19 +413,35 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
     __builtin_amdgcn_s_barrier();
     fence();
     read_frags(kt + 1, par ^ 1, 0, fa0, fb0);
+    // sub-step-1 MFMAs in two parts with the refill loads between them: a
+    // load the CU cannot accept yet stalls this wave only after part of its
+    // burst is queued, and the loads still go out early in the step
+#pragma unroll
+    for (int i = 0; i < LOAD_AFTER; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * LOAD_AFTER; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    }
+    fence();
     if (b_loader)
       issue_b(kt + SB, min(kt + SB, nk - 1));
     else if (par)
       issue_a((kt >> 1) + SA, min((kt >> 1) + SA, nks - 1));
-#if MOE_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-    mfma_step(fa1, fb1);
-    interleave();
-#if MOE_SETPRIO
     fence();
-    __builtin_amdgcn_s_setprio(0);
-#endif
+#pragma unroll
+    for (int i = LOAD_AFTER; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8 - 2 * LOAD_AFTER; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
   };
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, std::integral_constant<int, 0>{});
