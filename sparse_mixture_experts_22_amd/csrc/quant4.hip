@@ -80,12 +80,22 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
   }
 }
 
-__device__ __forceinline__ bf16x8_t dq4(uint32_t w) {
+// (x & m) | c in one VALU instruction (the three-operand form takes no
+// literal constants and at most one scalar operand, so m is kept in a vector
+// register and c in a scalar one; the compiler would otherwise emit a
+// separate AND and OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "s"(c));
+  return r;
+}
+
+__device__ __forceinline__ bf16x8_t dq4(uint32_t w, uint32_t m, uint32_t c) {
   u32x4_t r;
-  r[0] = (w & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r[0] = and_or(w, m, c);
+  r[1] = and_or(w >> 4, m, c);
+  r[2] = and_or(w >> 8, m, c);
+  r[3] = and_or(w >> 12, m, c);
   return *reinterpret_cast<bf16x8_t*>(&r);
 }
 
@@ -141,6 +151,10 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
   const uint8_t* qsrc = Q + ((((int64_t)e * (N / 2) + col0 / 2) * (Kdim / 32) + g) * 2 + (col0 & 1)) * 16;
   const int64_t qtile = (int64_t)8 * Kdim;
   const uint16_t* ssrc = S + (int64_t)e * ngr * N + col0;
+  // nibble mask and bf16 exponent pattern, uniform (kept in scalar registers)
+  uint32_t nib_mask = 0x000F000Fu;
+  asm volatile("" : "+v"(nib_mask));  // materialise once in a vector register
+  const uint32_t nib_base = __builtin_amdgcn_readfirstlane(0x43004300u);
   bf16x8_t bias;
   {
     const uint32_t bb = kBias136 | (kBias136 << 16);
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
       for (int ct = 0; ct < Q4_TILES; ++ct) {
         f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], dq4(w[ct][j]), t, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], dq4(w[ct][j], nib_mask, nib_base), t, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[ct][i] = fmaf(s[ct], t[i] - corr[i], acc[ct][i]);
         // keep one tile's unpacked operands live at a time
