@@ -52,6 +52,12 @@ def test_route_full_configs(name):
 
 @pytest.mark.parametrize("T,d,n,K,dtype", [
     (1, 64, 8, 2, "bf16"),
+    (32, 192, 8, 2, "bf16"),       # one routing block: W_g read in place, fused dispatch
+    (20, 128, 5, 3, "bf16"),       # one block, n not a multiple of 8
+    (32, 64, 16, 4, "bf16"),       # one block, 16 experts
+    (17, 64, 1, 1, "bf16"),        # one block, one expert
+    (32, 2048, 16, 2, "bf16"),     # one block, wide d
+    (32, 64, 17, 2, "bf16"),       # one block, n > 16: transposed W_g copy, fused dispatch
     (129, 128, 8, 2, "bf16"),      # ragged tail of a 128-token block
     (1000, 192, 8, 2, "bf16"),
     (300, 64, 1, 1, "bf16"),       # one expert
