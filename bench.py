@@ -413,7 +413,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -21,7 +21,9 @@
  *     caller keeps buffers alive until that work completes.
  *   - Every argument is validated before anything is enqueued; on an error
  *     nothing is enqueued and the status says why (moe_last_error() has the
- *     detail).  T == 0 is a valid no-op.  No C++ exception crosses the ABI.
+ *     detail).  T == 0 is a valid no-op; then the per-token arrays (x, y and
+ *     the per-token routing outputs) may be null, since none of them is
+ *     accessed.  No C++ exception crosses the ABI.
  *   - Layouts: x[T][d], W_g[d][n] (so logits = x . W_g; a PyTorch nn.Linear
  *     router weight [n][d] is passed transposed), W1[n][d][f], W3[n][d][f],
  *     W2[n][f][d].  bf16 entry points take bf16 storage (uint16 bit patterns).

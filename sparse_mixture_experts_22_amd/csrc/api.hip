@@ -202,8 +202,8 @@ moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int
                         const RouteOut& user, hipStream_t stream, int cap = INT32_MAX) {
   moe_status_t st = check_shape(T, d, 1, n, K, false);
   if (st != MOE_OK) return st;
-  if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
-  if (!user.topk_idx && !user.topk_w && !user.counts && !user.offsets && !user.perm_token &&
+  if ((!x && T > 0) || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
+  if (T > 0 && !user.topk_idx && !user.topk_w && !user.counts && !user.offsets && !user.perm_token &&
       !user.slot_pos)
     return fail(MOE_ERR_INVALID_ARG, "at least one routing output must be non-null");
   if (BF16) {
@@ -227,9 +227,10 @@ moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int
   return MOE_OK;
 }
 
-moe_status_t check_forward_ptrs(const void* x, const void* Wg, const void* W1, const void* W3,
+// x and y hold T rows: with T == 0 they may be null (an empty array).
+moe_status_t check_forward_ptrs(int64_t T, const void* x, const void* Wg, const void* W1, const void* W3,
                                 const void* W2, const void* y) {
-  if (!x || !Wg || !W1 || !W3 || !W2 || !y)
+  if (!Wg || !W1 || !W3 || !W2 || (T > 0 && (!x || !y)))
     return fail(MOE_ERR_INVALID_ARG, "x, Wg, W1, W3, W2 and y must be non-null");
   return MOE_OK;
 }
@@ -244,7 +245,7 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   g_last_error.clear();
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
-  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  st = check_forward_ptrs(T, x, Wg, W1, W3, W2, y);
   if (st != MOE_OK) return st;
   st = check_bf16(d, f, true, {x, Wg, W1, W3, W2, y});
   if (st != MOE_OK) return st;
@@ -336,7 +337,7 @@ moe_status_t forward_q4(const void* x, const void* Wg, const void* W1q, const vo
   g_last_error.clear();
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
-  if (!x || !Wg || !W1q || !W1s || !W3q || !W3s || !W2q || !W2s || !y)
+  if (!Wg || !W1q || !W1s || !W3q || !W3s || !W2q || !W2s || (T > 0 && (!x || !y)))
     return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
   if (d % 128 != 0 || f % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "4-bit path needs d % 128 == 0 and f % 128 == 0");
   st = check_bf16(d, f, true, {x, Wg, W1q, W3q, W2q, y});
@@ -422,7 +423,7 @@ moe_status_t moe_forward_f32(const float* x, const float* Wg, const float* W1, c
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
-  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  st = check_forward_ptrs(T, x, Wg, W1, W3, W2, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   const Plan p = make_plan(T, d, f, n, K, Path::kF32);
@@ -588,8 +589,9 @@ moe_status_t moe_route_expert_choice(const void* x, const void* Wg, int64_t T, i
   int64_t C = 0;
   moe_status_t st = check_ec(T, d, 1, n, false, capacity_factor, &C);
   if (st != MOE_OK) return st;
-  if (!x || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
-  if (!scores && !perm_token && !slot_pos) return fail(MOE_ERR_INVALID_ARG, "at least one output must be non-null");
+  if ((!x && T > 0) || !Wg) return fail(MOE_ERR_INVALID_ARG, "x and Wg must be non-null");
+  if (T > 0 && !scores && !perm_token && !slot_pos)
+    return fail(MOE_ERR_INVALID_ARG, "at least one output must be non-null");
   st = check_bf16(d, 0, false, {x, Wg});
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -612,7 +614,7 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* Wg, const void
   int64_t C = 0;
   moe_status_t st = check_ec(T, d, f, n, true, capacity_factor, &C);
   if (st != MOE_OK) return st;
-  st = check_forward_ptrs(x, Wg, W1, W3, W2, y);
+  st = check_forward_ptrs(T, x, Wg, W1, W3, W2, y);
   if (st != MOE_OK) return st;
   st = check_bf16(d, f, true, {x, Wg, W1, W3, W2, y});
   if (st != MOE_OK) return st;

@@ -87,6 +87,29 @@ def test_empty_batch_is_a_noop_without_gpu():
     assert L.moe_route(P[0], P[1], 0, 64, 8, 2, P[2], None, None, None, None, None, None) == 0
 
 
+def test_empty_batch_optional_paths_without_gpu():
+    # T == 0 is a valid no-op for every entry point that takes a batch, except
+    # the router statistics (their means over tokens need T >= 1)
+    _, L = _lib()
+    assert L.moe_route_capacity(P[0], P[1], 0, 64, 8, 2, 1.0, P[2], None, None, None, None, None, None) == 0
+    assert L.moe_forward_capacity(P[0], P[1], P[2], P[3], P[4], 0, 64, 64, 8, 2, 1.0, P[5], None) == 0
+    assert L.moe_forward_q4(P[0], P[1], P[2], P[3], P[4], P[5], P[2], P[3], 0, 128, 128, 8, 2, P[4],
+                            None) == 0
+    assert L.moe_route_expert_choice(P[0], P[1], 0, 64, 8, 1.0, P[2], None, None, None) == 0
+    assert L.moe_forward_expert_choice(P[0], P[1], P[2], P[3], P[4], 0, 64, 64, 8, 1.0, P[5], None) == 0
+    out = (ctypes.c_float * 8)()
+    assert L.moe_route_stats(P[0], P[1], 0, 64, 8, 2, 0.01, out, None, None, None) == 1
+    # with T == 0 the per-token arrays may be null (an empty array has no storage)
+    assert L.moe_forward(None, P[1], P[2], P[3], P[4], 0, 64, 64, 8, 2, None, None) == 0
+    assert L.moe_route(None, P[1], 0, 64, 8, 2, None, None, P[2], P[3], None, None, None) == 0
+    assert L.moe_forward_q4(None, P[1], P[2], P[3], P[4], P[5], P[2], P[3], 0, 128, 128, 8, 2, None,
+                            None) == 0
+    assert L.moe_route_expert_choice(None, P[1], 0, 64, 8, 1.0, None, None, None, None) == 0
+    # ... but not when there are tokens
+    assert L.moe_forward(None, P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, P[5], None) == 1
+    assert L.moe_forward(P[0], P[1], P[2], P[3], P[4], 4, 64, 64, 8, 2, None, None) == 1
+
+
 def test_route_validation():
     moe, L = _lib()
     # no output requested

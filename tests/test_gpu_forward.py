@@ -64,6 +64,8 @@ def test_forward_tiny_fp32():
     (257, 64, 128, 1, 1),     # n = K = 1: dense SwiGLU FFN
     (1, 64, 64, 8, 2),        # single token
     (600, 64, 128, 130, 4),   # 64-token routing blocks
+    (300, 64, 64, 256, 8),    # maximum n and K, weight-streaming path
+    (3000, 64, 128, 256, 8),  # maximum n and K, tiled path (256 experts of ~94 rows)
 ])
 def test_forward_bf16_shapes(T, d, f, n, K):
     _check_full(make_inputs(T, d, f, n, K, dtype="bf16", seed=T + 31 * n + K))
@@ -112,6 +114,23 @@ def test_forward_is_deterministic():
         a, _ = _run(inp, dev)
         b, _ = _run(inp, dev)
         np.testing.assert_array_equal(a, b)
+
+
+def test_empty_batch_writes_nothing():
+    import torch
+    moe = _moe()
+    inp = make_inputs(4, 64, 64, 8, 2, dtype="bf16", seed=2)
+    dev = upload(inp)
+    x0 = dev["x"][:0]
+    w = (dev["Wg"], dev["W1"], dev["W3"], dev["W2"])
+    assert tuple(moe.forward(x0, *w, 2).shape) == (0, 64)
+    assert tuple(moe.forward_capacity(x0, *w, 2, 1.0).shape) == (0, 64)
+    assert tuple(moe.forward_expert_choice(x0, *w, 1.0).shape) == (0, 64)
+    rt = moe.route(x0, dev["Wg"], 2)
+    assert rt["offsets"].shape[0] == 9 and rt["topk_idx"].shape[0] == 0
+    rc = moe.route_capacity(x0, dev["Wg"], 2, 1.0)
+    assert rc["perm_token"].shape[0] == 0
+    torch.cuda.synchronize()
 
 
 def test_invalid_call_enqueues_nothing():
