@@ -216,13 +216,15 @@ moe_status_t moe_forward_expert_choice(const void* x, const void* Wg, const void
  *   scales [n][R/128][C] bf16: s = bf16_rne(max |W| over 128 consecutive r of
  *           a column / 7), computed in fp32;
  *   codes   n*R*C/2 bytes: q = clamp(rint(W / s), -7, 7) (fp32 division, q = 0
- *           where s = 0), nibble q + 8; per expert, by column pair c/2, then
- *           chunk r/32, then column parity, 16 bytes = 4 little-endian words,
- *           word m holding r = 32j + 8m + i with element i = 2t in bits
- *           4t..4t+3 and element 2t+1 in bits 16+4t..16+4t+3.
+ *           where s = 0), nibble q + 8; per expert, by group b = r/128, then
+ *           column tile c/16, then chunk g = (r%128)/32, then column c%16,
+ *           16 bytes = 4 little-endian words, word m holding
+ *           r = 128b + 32g + 8m + i with element i = 2t in bits 4t..4t+3 and
+ *           element 2t+1 in bits 16+4t..16+4t+3 (a 16-column tile of a group
+ *           is one contiguous kilobyte).
  * The dequantised weight is q * s.
  *
- * moe_quantize_q4 -- W bf16 [n][R][C] (R % 128 == 0, C even; W and codes
+ * moe_quantize_q4 -- W bf16 [n][R][C] (R % 128 == 0, C % 16 == 0; W and codes
  *   16-byte aligned) -> codes, scales.  Deterministic, bit-exact to the format.
  * moe_forward_q4  -- the layer with 4-bit W1, W3 (R = d, C = f) and W2 (R = f,
  *   C = d) given as (codes, scales) pairs; x, Wg bf16, y fp32.  Needs d % 128

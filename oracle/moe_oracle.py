@@ -343,10 +343,12 @@ def forward_kept(x, Wg, W1: ArrayOrGetter, W3: ArrayOrGetter, W2: ArrayOrGetter,
 #   scale s[e][g][c] = bf16_rne(max_r |W[e][r][c]| / 7) (fp32 division);
 #   code q = clamp(rint(W / s), -7, 7) with the division in fp32 (q = 0 where
 #   s = 0); dequantised weight q * s.
-# Storage of the codes (nibble u = q + 8), per expert e: column pair p = c // 2,
-# chunk j = r // 32, column parity c % 2, then 16 bytes = 4 little-endian
-# 32-bit words; word m holds r = 32j + 8m + i for i = 0..7, element i = 2t in
-# bits 4t..4t+3 and element i = 2t + 1 in bits 16+4t..16+4t+3.
+# Storage of the codes (nibble u = q + 8), per expert e: group b = r // 128,
+# column tile t = c // 16, chunk g = (r % 128) // 32, column c % 16, then 16
+# bytes = 4 little-endian 32-bit words; word m holds r = 128b + 32g + 8m + i
+# for i = 0..7, element i = 2k in bits 4k..4k+3 and element i = 2k + 1 in bits
+# 16+4k..16+4k+3.  (C is a multiple of 16.)  So one group of 16 columns is one
+# contiguous kilobyte, and one group of all C columns C*64 contiguous bytes.
 Q4_GROUP = 128
 
 
@@ -383,14 +385,15 @@ def dequantize_q4(codes, scales) -> np.ndarray:
 
 def unpack_q4(packed, n: int, R: int, C: int) -> np.ndarray:
     """Packed code bytes (the storage described above) -> codes int8 [n][R][C]."""
-    words = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").reshape(n, C // 2, R // 32, 2, 4)
+    # words[e][b][t][g][c16][m]
+    words = np.ascontiguousarray(packed, dtype=np.uint8).view("<u4").reshape(n, R // 128, C // 16, 4, 16, 4)
     codes = np.empty((n, R, C), dtype=np.int8)
+    view = codes.reshape(n, R // 128, 4, 4, 8, C // 16, 16)  # [e][b][g][m][i][t][c16]
     for i in range(8):
         shift = 4 * (i // 2) + 16 * (i % 2)
-        u = ((words >> np.uint32(shift)) & np.uint32(15)).astype(np.int16) - 8  # [e][p][j][s][m]
-        # r = 32j + 8m + i, c = 2p + s
-        v = u.transpose(0, 2, 4, 1, 3)  # [e][j][m][p][s]
-        codes.reshape(n, R // 32, 4, 8, C // 2, 2)[:, :, :, i, :, :] = v
+        u = ((words >> np.uint32(shift)) & np.uint32(15)).astype(np.int16) - 8
+        # r = 128b + 32g + 8m + i, c = 16t + c16
+        view[:, :, :, :, i, :, :] = u.transpose(0, 1, 3, 5, 2, 4)
     return codes
 
 

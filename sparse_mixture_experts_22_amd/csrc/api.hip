@@ -557,7 +557,8 @@ moe_status_t moe_quantize_q4(const void* W, int32_t n, int64_t R, int64_t C, voi
   g_last_error.clear();
   if (!W || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
   if (n < 1 || R < 1 || C < 1) return fail(MOE_ERR_INVALID_ARG, "n, R and C must be >= 1");
-  if (R % 128 != 0 || C % 2 != 0) return fail(MOE_ERR_UNSUPPORTED, "4-bit format needs R % 128 == 0 and C even");
+  if (R % 128 != 0 || C % 16 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "4-bit format needs R % 128 == 0 and C % 16 == 0");
   if (R > INT32_MAX || C > INT32_MAX || (int64_t)n * R * C / 2 > ((int64_t)1 << 40))
     return fail(MOE_ERR_UNSUPPORTED, "weight stack too large");
   if (!aligned16(W) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 1u) != 0)

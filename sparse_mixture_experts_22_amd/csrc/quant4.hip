@@ -9,16 +9,20 @@
 //   scale s[e][g][c] = bf16_rne(max_{r in group g} |W[e][r][c]| / 7), groups
 //   of 128 reduction indices; code q = clamp(rint(W / s), -7, 7) (q = 0 where
 //   s = 0), both divisions in fp32; nibble u = q + 8.
-//   Codes of expert e: column pair p = c/2, chunk j = r/32, parity c%2, then
-//   16 bytes = 4 little-endian words; word m holds r = 32j + 8m + i, element
-//   i = 2t in bits 4t..4t+3 and i = 2t+1 in bits 16+4t..16+4t+3.
-// A 128-byte line thus holds 256 reduction indices of one column pair, and
-// one word ORed into 0x43004300 after masking with 0x000F000F (shifted by
-// 4t) gives two bf16 values 128 + u = 136 + q of an MFMA B operand.
+//   Codes of expert e: group b = r/128, column tile t = c/16, chunk g =
+//   (r%128)/32, column c%16, then 16 bytes = 4 little-endian words; word m
+//   holds r = 128b + 32g + 8m + i, element i = 2k in bits 4k..4k+3 and
+//   i = 2k+1 in bits 16+4k..16+4k+3 (C a multiple of 16).
+// One load instruction of a wave (lane = 16g + c%16) thus reads one
+// contiguous kilobyte - a tile's 128 reduction indices - and a wave's four
+// tiles are four adjacent kilobytes: streamed in such runs the codes reach
+// higher HBM throughput than as separate 128-byte lines per column pair.
+// One word ORed into 0x43004300 after masking with 0x000F000F (shifted by
+// 4k) gives two bf16 values 128 + u = 136 + q of an MFMA B operand.
 //
 // Projection kernel (one workgroup of 4 waves per (expert, 128 columns[, K
 // split])): lane (c = l%16, g = l/16) of a wave's column tile ct loads the 16
-// bytes of the tile's column c, chunk 4*blk + g: reduction indices 128blk + 32g + 0..31,
+// bytes of the tile's column c, group blk, chunk g: reduction indices 128blk + 32g + 0..31,
 // four MFMA B operands (word j: 128blk + 32g + 8j + 0..7).  The A operand of
 // lane (row, g) uses the same reduction indices, so each 16x16x32 MFMA j sums
 // over 32 indices of one 128-group.  Per group and column tile the MFMAs give
@@ -60,8 +64,8 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
   const uint16_t sbits = f32_to_bf16_rne(amax / 7.0f);
   const float s = __uint_as_float((uint32_t)sbits << 16);
   scales[((int64_t)e * G + g) * C + c] = sbits;
-  uint8_t* dst = codes + ((((int64_t)e * (C / 2) + c / 2) * (R / 32) + 4 * g) * 2 + (c & 1)) * 16;
-  for (int jj = 0; jj < 4; ++jj) {  // chunk 4g + jj
+  uint8_t* dst = codes + (int64_t)e * R * (C / 2) + (int64_t)g * C * 64 + (int64_t)(c / 16) * 1024 + (c % 16) * 16;
+  for (int jj = 0; jj < 4; ++jj) {  // chunk jj of group g
     u32x4_t out;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __rest
       }
       out[m] = word;
     }
-    *reinterpret_cast<u32x4_t*>(dst + (int64_t)jj * 32) = out;
+    *reinterpret_cast<u32x4_t*>(dst + (int64_t)jj * 256) = out;
   }
 }
 
@@ -144,12 +148,12 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
   const bool third = MODE == 1 && wave >= 2;
   const uint8_t* Q = third ? Q3 : Q1;
   const uint16_t* S = third ? S3 : S1;
-  // column tile 0's code chunk of block 0 and scale column; tile ct adds 8
-  // column pairs (8 * Kdim bytes of codes) and 16 scale columns.  N is a
-  // multiple of 128 (checked by the caller), so every column exists.
+  // this lane's 16 bytes of column tile 0 in group 0, and its scale column;
+  // tile ct adds 1 KiB of codes and 16 scale columns, group blk N*64 bytes.
+  // N is a multiple of 128 (checked by the caller), so every column exists.
   const int col0 = nb * 128 + half * 64 + c16;
-  const uint8_t* qsrc = Q + ((((int64_t)e * (N / 2) + col0 / 2) * (Kdim / 32) + g) * 2 + (col0 & 1)) * 16;
-  const int64_t qtile = (int64_t)8 * Kdim;
+  const uint8_t* qsrc = Q + (int64_t)e * Kdim * (N / 2) + (int64_t)((nb * 128 + half * 64) / 16) * 1024 + lane * 16;
+  const int64_t qtile = 1024;
   const uint16_t* ssrc = S + (int64_t)e * ngr * N + col0;
   // nibble mask and bf16 exponent pattern, uniform (kept in scalar registers)
   uint32_t nib_mask = 0x000F000Fu;
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     auto load = [&](int blk, u32x4_t (&w)[Q4_TILES], bf16x8_t (&a)[4], float (&s)[Q4_TILES]) {
 #pragma unroll
       for (int ct = 0; ct < Q4_TILES; ++ct) {
-        w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * 128);
+        w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * N * 64);
         s[ct] = __uint_as_float((uint32_t)ssrc[(int64_t)blk * N + ct * 16] << 16);
       }
 #pragma unroll

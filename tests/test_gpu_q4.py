@@ -124,3 +124,6 @@ def test_q4_invalid_shapes():
     W = torch.zeros((2, 96, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(moe.MoEError):
         moe.quantize_q4(W)                           # R not a multiple of 128
+    W = torch.zeros((2, 128, 24), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoEError):
+        moe.quantize_q4(W)                           # C not a multiple of 16

@@ -505,20 +505,30 @@ def test_capacity_forward_keeps_only_kept_terms():
 # ------------------------------------------------------------ 4-bit weights
 
 def test_q4_word_layout_hand_example():
+    # one expert, R = 256 (two groups of 128), C = 32 (two tiles of 16 columns)
+    n, R, C = 1, 256, 32
+    base = np.full(n * R * C // 2, 0x88, dtype=np.uint8)  # every code 0
     # codes -7..0 for r = 0..7 of column 0: nibbles u = 1..8; even elements in
-    # the low half (1, 3, 5, 7 -> 0x7531), odd ones in the high half (0x8642)
-    n, R, C = 1, 128, 2
-    packed = np.full(n * R * C // 2, 0x88, dtype=np.uint8)  # every other code 0
+    # the low half-word (1, 3, 5, 7 -> 0x7531), odd ones in the high half-word (0x8642)
+    packed = base.copy()
     packed[0:4] = [0x31, 0x75, 0x42, 0x86]
     codes = oracle.unpack_q4(packed, n, R, C)
     np.testing.assert_array_equal(codes[0, 0:8, 0], np.arange(-7, 1))
     codes[0, 0:8, 0] = 0
     assert (codes == 0).all()
-    # chunk order: column parity before the next chunk; the 17th..32nd bytes are column 1
-    packed2 = np.full_like(packed, 0x88)
-    packed2[16] = 0x9A  # column 1, r = 0 (low nibble 0xA -> +2) and r = 2 (0x9 -> +1)
-    codes2 = oracle.unpack_q4(packed2, n, R, C)
-    assert codes2[0, 0, 1] == 2 and codes2[0, 2, 1] == 1 and codes2[0, 1, 1] == 0
+    # the first byte of a word: low nibble element 0 (+2 from 0xA), high
+    # nibble element 2 (+1 from 0x9).  Strides from the stated order: 4 bytes
+    # per word (8 reduction indices), 16 per column, 256 per 32-index chunk,
+    # 1024 per 16-column tile, C*64 = 2048 per 128-index group.
+    for off, (r, c) in [(16, (0, 1)), (4, (8, 0)), (256, (32, 0)), (1024, (0, 16)),
+                        (2048, (128, 0)), (2048 + 1024 + 256 + 16 + 4, (168, 17))]:
+        p = base.copy()
+        p[off] = 0x9A
+        cd = oracle.unpack_q4(p, n, R, C)
+        assert cd[0, r, c] == 2 and cd[0, r + 2, c] == 1, off
+        cd[0, r, c] = 0
+        cd[0, r + 2, c] = 0
+        assert (cd == 0).all(), off
 
 
 def test_q4_exactly_representable_weights_round_trip():
