@@ -351,13 +351,26 @@ def short_kernel_name(name):
 
 
 def summarize_trace(d):
+    """Per-kernel rows of a rocprofv3 --kernel-trace --stats run: the profiler's
+    call count, average, min, max and share, plus the median duration of the
+    individual dispatches (robust to the cold first calls that lift the average)."""
+    import collections
     import csv
     import glob
     path = glob.glob(os.path.join(d, "*kernel_stats.csv"))[0]
     rows = list(csv.DictReader(open(path)))
-    print(f"{'kernel':58s} {'calls':>5s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'%':>6s}")
+    durations = collections.defaultdict(list)
+    for tpath in glob.glob(os.path.join(d, "*kernel_trace.csv")):
+        for r in csv.DictReader(open(tpath)):
+            durations[short_kernel_name(r["Kernel_Name"])].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"{'kernel':58s} {'calls':>5s} {'avg_us':>10s} {'median_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+          f"{'%':>6s}")
     for r in rows:
-        print(f"{short_kernel_name(r['Name'])[:58]:58s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:10.1f} "
+        name = short_kernel_name(r["Name"])
+        v = sorted(durations.get(name, []))
+        med = f"{v[len(v) // 2]:10.1f}" if v else f"{'-':>10s}"
+        print(f"{name[:58]:58s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e3:10.1f} {med} "
               f"{float(r['MinNs']) / 1e3:10.1f} {float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}")
 
 
