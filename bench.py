@@ -46,6 +46,8 @@ def parse():
                     help="first run a 1 GiB device-to-device copy (reference for traffic counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a summary of a rocprofv3 --kernel-trace --stats csv directory and exit")
+    ap.add_argument("--summarize-clock", metavar="DIR",
+                    help="print the engine clock under each kernel from a GRBM_GUI_ACTIVE/GRBM_COUNT pass")
     ap.add_argument("--summarize-counters", metavar="DIR", nargs="+",
                     help="print a summary of rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE "
                          "scaled by the 1 GiB calibration copy) and exit")
@@ -287,11 +289,20 @@ def cpu_baseline(name, sample):
     import oracle
     from synth import make_config_inputs
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+        pools = threadpool_info()
+        threads = max([int(i.get("num_threads", 1)) for i in pools] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools if i.get("user_api") == "blas")
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    host_cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            host_cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     inp = make_config_inputs(name)
     x = inp.f64("x")[:sample]
     t0 = time.perf_counter()
@@ -301,7 +312,8 @@ def cpu_baseline(name, sample):
     assert np.isfinite(y).all()
     return {"value": round(sample / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {sample} of the {inp.T} tokens of {name}: fp64 routing and every "
-                      f"touched expert (weights widened per expert), {el:.1f} s"}
+                      f"touched expert (weights widened per expert), {el:.1f} s",
+            "host_cpu": host_cpu, "blas": blas}
 
 
 # ---------------------------------------------------------------- profiles
@@ -416,6 +428,30 @@ def summarize_counters(dirs, traffic_json=None):
             fh.write("\n")
 
 
+def summarize_clock(d):
+    """Engine clock under each kernel, from a counter pass with GRBM_GUI_ACTIVE
+    and GRBM_COUNT: both are clock counts summed over the device's 8 XCDs, so
+    count / (8 x dispatch duration) is the clock in GHz (GUI_ACTIVE counts the
+    busy cycles, GRBM_COUNT every cycle)."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            if dur <= 0:
+                continue
+            per[short_kernel_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]) / dur)
+    print(f"{'kernel':44s} {'n':>4s} {'GHz (GRBM_COUNT)':>17s} {'GHz (GUI_ACTIVE)':>17s}")
+    for name, cs in sorted(per.items()):
+        cnt = sorted(cs.get("GRBM_COUNT", []))
+        act = sorted(cs.get("GRBM_GUI_ACTIVE", []))
+        if not cnt or not act:
+            continue
+        print(f"{name[:44]:44s} {len(cnt):4d} {cnt[len(cnt) // 2] / 8e9:17.3f} {act[len(act) // 2] / 8e9:17.3f}")
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -423,6 +459,9 @@ def main():
         return
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.traffic_json)
+        return
+    if args.summarize_clock:
+        summarize_clock(args.summarize_clock)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
