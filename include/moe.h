@@ -242,8 +242,10 @@ moe_status_t moe_forward_q4(const void* x, const void* Wg, const void* W1q, cons
                             moe_stream_t stream);
 
 /* Bytes of library workspace a call of this shape needs on any supported
- * device (an upper bound: the prefill path's leftover-tile buffer scales with
- * the device's compute units per XCD); 0 on invalid shapes. */
+ * device, for every entry point that takes (T, d, f, n, K) (an upper bound:
+ * the prefill path's leftover-tile buffer scales with the device's compute
+ * units per XCD).  For the expert-choice entry points pass K = n (K may
+ * exceed the per-call limit of 8 here).  0 on invalid shapes. */
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K);
 
 /* Frees the workspace of every device (synchronises each device first). */

@@ -464,11 +464,17 @@ moe_status_t moe_route_f32(const float* x, const float* Wg, int64_t T, int64_t d
 }
 
 size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K) {
-  if (check_shape(T, d, f, n, K, true) != MOE_OK) return 0;
-  // sized for the largest device layout the tile scheduler uses (64 CUs per XCD)
+  // a size query: K may exceed the per-call limit kMaxK (K = n sizes the
+  // expert-choice entry points, whose rows never exceed T*n)
+  if (T < 0 || d < 1 || f < 1 || n < 1 || n > moe::kMaxN || K < 1 || K > n) return 0;
+  if (T * (int64_t)K > INT32_MAX || d > INT32_MAX || f > INT32_MAX) return 0;
+  // the largest of: the tiled plan on the largest device layout the tile
+  // scheduler uses (64 CUs per XCD), the weight-streaming plan (4-bit path
+  // and few rows per expert), and the fp32 plan
   const Plan a = make_plan(T, d, f, n, K, Path::kBf16, 64);
-  const Plan b = make_plan(T, d, f, n, K, Path::kF32);
-  return a.total > b.total ? a.total : b.total;
+  const Plan b = make_plan(T, d, f, n, K, Path::kBf16, 0, true);
+  const Plan c = make_plan(T, d, f, n, K, Path::kF32);
+  return std::max(a.total, std::max(b.total, c.total));
 }
 
 moe_status_t moe_release(void) {
