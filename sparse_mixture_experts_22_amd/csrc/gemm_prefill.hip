@@ -190,12 +190,6 @@ typedef __attribute__((address_space(1))) const void gbl_void;
 constexpr int SA = MOE_RING_A;  // A super-stages (64 k each)
 constexpr int SB = MOE_RING_B;  // B stages (32 k each)
 static_assert(SA >= 2 && SB >= 2 && 2 * SA + SB <= 10, "LDS budget is 160 KiB");
-// Row blocks of a wave's second MFMA burst that are issued before the step's
-// refill loads (0..4).
-#ifndef MOE_LOAD_AFTER
-#define MOE_LOAD_AFTER 2
-#endif
-constexpr int LOAD_AFTER = MOE_LOAD_AFTER;
 constexpr int A_LOADS = 8;  // 1 KiB loads per A-loader wave per super-stage
 constexpr int B_LOADS = 4;  // 1 KiB loads per B-loader wave per stage
 // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
@@ -221,12 +215,17 @@ __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
 }
 
-__device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) {
+// A B fragment is two transposing LDS reads (k 0..3 and 4..7 of the lane's column).
+__device__ __forceinline__ i16x4_t read_b_half(const char* p) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8_t join_b_halves(i16x4_t lo, i16x4_t hi) {
   const i16x4_t both[2] = {lo, hi};
   return *reinterpret_cast<const bf16x8_t*>(both);
+}
+__device__ __forceinline__ bf16x8_t read_b_frag(const char* p0, const char* p1) {
+  return join_b_halves(read_b_half(p0), read_b_half(p1));
 }
 
 template <int MODE>
@@ -412,36 +411,40 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
     fence();
     __builtin_amdgcn_s_barrier();
     fence();
-    read_frags(kt + 1, par ^ 1, 0, fa0, fb0);
-    // sub-step-1 MFMAs in two parts with the refill loads between them: a
-    // load the CU cannot accept yet stalls this wave only after part of its
-    // burst is queued, and the loads still go out early in the step
+    // Sub-step 1 of step kt, one row block (two MFMAs) at a time; after each
+    // block come two of step kt+1's sub-step-0 fragment reads and a quarter
+    // of this step's refill loads (one B load, or two A loads after odd
+    // steps).  A load the CU cannot accept yet then stalls this wave with
+    // MFMAs still queued behind it, rather than with the whole refill batch
+    // ahead of them.
+    const char* as = a_lds + (((kt + 1) >> 1) % SA) * A_SUPER + a_off[par ^ 1][0];
+    const char* bs = b_lds + ((kt + 1) % SB) * B_STAGE;
+    const uint32_t b_dst = b_ld_base + ((kt + SB) % SB) * B_STAGE;
+    const int64_t b_koff = (int64_t)(tc.k0 + min(kt + SB, nk - 1)) * BK * N;
+    const uint32_t a_dst = a_ld_base + (((kt >> 1) + SA) % SA) * A_SUPER;
+    const int64_t a_koff = (int64_t)(tc.k0 / 2 + min((kt >> 1) + SA, nks - 1)) * 64;
+    i16x4_t bhalf[2][2];  // transposed halves of fb0[j]
 #pragma unroll
-    for (int i = 0; i < LOAD_AFTER; ++i)
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * LOAD_AFTER; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      fa0[i] = *reinterpret_cast<const bf16x8_t*>(as + i * 4096);
+      bhalf[i >> 1][i & 1] = read_b_half(bs + b_off[0][i >> 1][i & 1]);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // the other MFMA
+      fence();
+      if (b_loader) {
+        load_lds16(ld_ptr[i] + b_koff, b_dst + i * 1024);
+      } else if (par) {
+        load_lds16(ld_ptr[2 * i] + a_koff, a_dst + (2 * i) * 1024);
+        load_lds16(ld_ptr[2 * i + 1] + a_koff, a_dst + (2 * i + 1) * 1024);
+      }
+      fence();
     }
-    fence();
-    if (b_loader)
-      issue_b(kt + SB, min(kt + SB, nk - 1));
-    else if (par)
-      issue_a((kt >> 1) + SA, min((kt >> 1) + SA, nks - 1));
-    fence();
 #pragma unroll
-    for (int i = LOAD_AFTER; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa1[i], fb1[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8 - 2 * LOAD_AFTER; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
+    for (int j = 0; j < 2; ++j) fb0[j] = join_b_halves(bhalf[j][0], bhalf[j][1]);
   };
   for (int kt = 0; kt < nk; kt += 2) {
     step(kt, std::integral_constant<int, 0>{});
