@@ -192,6 +192,9 @@ constexpr int SB = MOE_RING_B;  // B stages (32 k each)
 static_assert(SA >= 2 && SB >= 2 && 2 * SA + SB <= 10, "LDS budget is 160 KiB");
 constexpr int A_LOADS = 8;  // 1 KiB loads per A-loader wave per super-stage
 constexpr int B_LOADS = 4;  // 1 KiB loads per B-loader wave per stage
+// the main loop spreads a step's refill over the 4 row blocks of a burst:
+// one B load, or two A loads, per block
+static_assert(B_LOADS == 4 && A_LOADS == 8, "refill spread assumes 4 B and 8 A loads per wave");
 // s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
 constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
