@@ -31,10 +31,14 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Top-K + softmax for token i of a block from logits_s[i*ld + e]; ties keep the
-// lower expert index first (a later expert only displaces a strictly smaller
-// score); an empty slot takes any score, so every slot ends up holding a valid
-// expert even for NaN input.  Returns the kept experts in id[].
+// Top-K + softmax for token i of a block from logits_s[i*ld + e]: an insertion
+// over the experts in index order into K slots kept in (score descending, index
+// ascending) order.  The element being placed takes slot j if that slot is
+// empty, holds a smaller score, or holds an equal score of a higher index (this
+// last case arises only for an element pushed down from an earlier slot, whose
+// index is lower than every later expert's); so ties keep the lower expert
+// index, also below a larger later score.  NaN scores count as -inf, and every
+// slot ends up holding a valid expert.  Returns the kept experts in id[].
 __device__ void topk_softmax(const float* logits_s, int ld, int i, int n, int K, int (&id)[kMaxK],
                              float (&w)[kMaxK]) {
   float v[kMaxK];
@@ -49,7 +53,7 @@ __device__ void topk_softmax(const float* logits_s, int ld, int i, int n, int K,
     int ci = e;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
-      if (j < K && (id[j] < 0 || cv > v[j])) {
+      if (j < K && (id[j] < 0 || cv > v[j] || (cv == v[j] && ci < id[j]))) {
         const float tv = v[j];
         const int ti = id[j];
         v[j] = cv;

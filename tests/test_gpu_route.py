@@ -86,6 +86,41 @@ def test_route_all_ties_pick_lowest_indices(dtype):
     assert gpu["counts"].tolist() == [200, 200, 200, 0, 0, 0, 0, 0]
 
 
+# Logit rows with exact ties below a strictly larger later logit: the tied
+# experts must still be kept in ascending index order (the displaced earlier
+# expert outranks an equal later one).
+_TIE_PATTERNS = np.array([
+    [1, 1, 2, -4, -4, -4, -4, -4],
+    [1, 1, 1, 2, -4, -4, -4, -4],
+    [-4, 0.5, 0.5, 0.5, 3, 0.5, -4, -4],
+    [2, 1, 1, 3, -4, -4, -4, -4],
+    [0.25, 0.25, 0.25, 0.25, 0.25, 0.25, 0.25, 1],
+], dtype=np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [20, 200])    # one routing block (fused dispatch) and several
+@pytest.mark.parametrize("K", [2, 3])
+def test_route_ties_below_a_larger_later_logit(dtype, T, K):
+    from synth import bf16_bits_from_f32
+    inp = make_inputs(T, 64, 64, 8, K, dtype=dtype, seed=17, router_only=True)
+    P = len(_TIE_PATTERNS)
+    x = np.zeros((T, 64), dtype=np.float32)
+    x[np.arange(T), np.arange(T) % P] = 1.0       # token t's logits are pattern t % P, exactly
+    wg = np.zeros((64, 8), dtype=np.float32)
+    wg[:P] = _TIE_PATTERNS
+    if dtype == "bf16":
+        inp.x, inp.Wg = bf16_bits_from_f32(x), bf16_bits_from_f32(wg)
+    else:
+        inp.x, inp.Wg = x, wg
+    gpu = _gpu_route(inp, K)
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), K)
+    np.testing.assert_array_equal(gpu["topk_idx"], r["sel"])
+    np.testing.assert_allclose(gpu["topk_w"], r["w"], rtol=0, atol=1e-6)
+    for name in ("counts", "offsets", "perm_token", "slot_pos"):
+        np.testing.assert_array_equal(gpu[name].reshape(np.shape(r[name])), r[name])
+
+
 def test_route_partial_outputs():
     inp = make_inputs(500, 128, 64, 8, 2, dtype="bf16", seed=8, router_only=True)
     full = _gpu_route(inp, 2)
