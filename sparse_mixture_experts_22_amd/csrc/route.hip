@@ -41,6 +41,35 @@ namespace moe {
 // slot ends up holding a valid expert.  Returns the kept experts in id[].
 __device__ void topk_softmax(const float* logits_s, int ld, int i, int n, int K, int (&id)[kMaxK],
                              float (&w)[kMaxK]) {
+  if (K == 2) {
+    // the same insertion with two slots, unrolled: the element pushed down
+    // from slot 0 always outranks slot 1 (higher score, or an equal score of
+    // a lower index), so it simply moves there
+    float v0 = -INFINITY, v1 = -INFINITY;
+    int i0 = -1, i1 = -1;
+    for (int e = 0; e < n; ++e) {
+      float cv = logits_s[i * ld + e];
+      if (cv != cv) cv = -INFINITY;
+      if (i0 < 0 || cv > v0) {
+        v1 = v0;
+        i1 = i0;
+        v0 = cv;
+        i0 = e;
+      } else if (i1 < 0 || cv > v1) {
+        v1 = cv;
+        i1 = e;
+      }
+    }
+    // the generic path's softmax, term by term (same values, same order)
+    const float w0 = expf(v0 - v0);
+    const float w1 = expf(v1 - v0);
+    const float sum = (0.0f + w0) + w1;
+    id[0] = i0;
+    id[1] = i1;
+    w[0] = w0 / sum;
+    w[1] = w1 / sum;
+    return;
+  }
   float v[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
