@@ -1,7 +1,7 @@
 """fp64 CPU oracle of the Mixtral-style sparse mixture-of-experts layer.
 
-TEST INFRASTRUCTURE: only tests/, the graft smoke check and the benchmark's
-CPU-baseline leg may use it.  It shares no code with the HIP path.
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and the
+benchmark's CPU-baseline leg may use it.  It shares no code with the HIP path.
 
 What it computes is the plain definition of the layer, written out in NumPy
 float64 (every input is widened losslessly from its bf16/fp32 storage):
