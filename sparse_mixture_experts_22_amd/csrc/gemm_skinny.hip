@@ -45,12 +45,12 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t (&in)[8], bf16x8_t (&
   }
 }
 
-__device__ __forceinline__ void load_block(u32x4_t (&q)[8], const uint16_t* src, int64_t row_stride,
-                                           bool ok) {
+// Lanes whose columns lie past N read column 0's rows instead (the caller
+// clamps src), so every load is in bounds; those columns are never stored.
+__device__ __forceinline__ void load_block(u32x4_t (&q)[8], const uint16_t* src, int64_t row_stride) {
 #pragma unroll
   for (int r = 0; r < 8; ++r)
-    q[r] = ok ? *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * row_stride)
-              : u32x4_t{0u, 0u, 0u, 0u};
+    q[r] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * row_stride);
 }
 
 __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t& a, f32x4_t (&acc)[8]) {
@@ -127,31 +127,41 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
     for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #if MOE_SKINNY_PINGPONG
-    // ping-pong: step kc in (qa, aa), step kc+1 in (qb, ab)
+    // ping-pong: step kc in (qa, aa), step kc+1 in (qb, ab).  The loads are
+    // unconditional (indices clamped to the last step) and scheduling
+    // barriers fence each phase, so the compiler waits only for the buffer
+    // about to be multiplied; a conditional load here makes it wait for all.
     u32x4_t qa[8], qb[8];
     bf16x8_t aa, ab;
     int kc = wk0;
     if (kc < wk1) {
-      load_block(qa, bsrc + kc * kstep, N, b_ok);
+      load_block(qa, bsrc + kc * kstep, N);
       aa = *reinterpret_cast<const bf16x8_t*>(asrc + kc * 32);
     }
     while (kc < wk1) {
-      if (kc + 1 < wk1) {
-        load_block(qb, bsrc + (kc + 1) * kstep, N, b_ok);
-        ab = *reinterpret_cast<const bf16x8_t*>(asrc + (kc + 1) * 32);
+      {
+        const int k1 = min(kc + 1, wk1 - 1);
+        load_block(qb, bsrc + k1 * kstep, N);
+        ab = *reinterpret_cast<const bf16x8_t*>(asrc + k1 * 32);
       }
+      __builtin_amdgcn_sched_barrier(0);
       mma_block(qa, aa, acc);
-      if (kc + 2 < wk1) {
-        load_block(qa, bsrc + (kc + 2) * kstep, N, b_ok);
-        aa = *reinterpret_cast<const bf16x8_t*>(asrc + (kc + 2) * 32);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int k2 = min(kc + 2, wk1 - 1);
+        load_block(qa, bsrc + k2 * kstep, N);
+        aa = *reinterpret_cast<const bf16x8_t*>(asrc + k2 * 32);
       }
-      if (kc + 1 < wk1) mma_block(qb, ab, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc + 1 >= wk1) ab = bf16x8_t{};  // past the end: a zero A fragment adds nothing
+      mma_block(qb, ab, acc);
+      __builtin_amdgcn_sched_barrier(0);
       kc += 2;
     }
 #else
     for (int kc = wk0; kc < wk1; ++kc) {
       u32x4_t q[8];
-      load_block(q, bsrc + kc * kstep, N, b_ok);
+      load_block(q, bsrc + kc * kstep, N);
       const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(asrc + kc * 32);
       mma_block(q, a, acc);
     }
