@@ -320,21 +320,25 @@ def cpu_baseline(name, sample):
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic_counters.json")
 CALIB_BYTES = 1 << 30  # the --calibrate-copy copy: 1 GiB read, 1 GiB written
-# Sources that determine each measured kernel's code (a change voids its counters).
+# Sources that determine each measured kernel's code (a change voids its counters), by the
+# kernel's name without template arguments: every instance of a template shares them.
+_Q = ["csrc/moe_internal.h", "build.py"]
 KERNEL_SOURCES = {
-    "grouped_gemm_kernel<1>": ["csrc/gemm_prefill.hip", "csrc/moe_internal.h", "build.py"],
-    "grouped_gemm_kernel<2>": ["csrc/gemm_prefill.hip", "csrc/moe_internal.h", "build.py"],
-    "skinny_kernel<1>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
-    "skinny_kernel<2>": ["csrc/gemm_skinny.hip", "csrc/moe_internal.h", "build.py"],
-    "skinny_q4_kernel<1>": ["csrc/quant4.hip", "csrc/moe_internal.h", "build.py"],
-    "skinny_q4_kernel<2>": ["csrc/quant4.hip", "csrc/moe_internal.h", "build.py"],
+    "grouped_gemm_kernel": ["csrc/gemm_prefill.hip"] + _Q,
+    "skinny_kernel": ["csrc/gemm_skinny.hip"] + _Q,
+    "skinny_q4_kernel": ["csrc/quant4.hip"] + _Q,
 }
+
+
+def kernel_sources(kernel):
+    """Source files of `kernel` ("skinny_q4_kernel<1, 7>" -> those of skinny_q4_kernel), or None."""
+    return KERNEL_SOURCES.get(kernel.split("<")[0])
 
 
 def sources_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[kernel]:
+    for rel in kernel_sources(kernel):
         with open(os.path.join(ROOT, "sparse_mixture_experts_22_amd", rel), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -417,7 +421,7 @@ def summarize_counters(dirs, traffic_json=None):
             rb = cs["FETCH_SIZE"] * 1024 * fetch_factor
             wb = cs["WRITE_SIZE"] * 1024 * write_factor
             line += f" -> read {rb / 1e9:.4f} GB, written {wb / 1e9:.4f} GB per launch"
-            if kname in KERNEL_SOURCES and int(key.split("grid=")[1]) >= out["kernels"].get(kname, {}).get("grid", 0):
+            if kernel_sources(kname) and int(key.split("grid=")[1]) >= out["kernels"].get(kname, {}).get("grid", 0):
                 out["kernels"][kname] = {"grid": int(key.split("grid=")[1]),"fetch_kib": cs["FETCH_SIZE"], "write_kib": cs["WRITE_SIZE"],
                                        "read_bytes": rb, "write_bytes": wb, "hbm_bytes": rb + wb,
                                        "sources_sha256": sources_hash(kname)}

@@ -343,6 +343,9 @@ moe_status_t forward_q4(const void* x, const void* Wg, const void* W1q, const vo
   st = check_bf16(d, f, true, {x, Wg, W1q, W3q, W2q, y});
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
+  int cus = 0;
+  st = cus_per_xcd(&cus);
+  if (st != MOE_OK) return st;
   const Plan p = make_plan(T, d, f, n, K, Path::kBf16, 0, true);
   char* ws = nullptr;
   st = get_workspace(p.total, &ws);
@@ -357,10 +360,11 @@ moe_status_t forward_q4(const void* x, const void* Wg, const void* W1q, const vo
              "routing kernel launch");
   MOE_LAUNCH(moe::launch_q4_up(xb, T, r.perm_token, static_cast<const uint8_t*>(W1q),
                                static_cast<const uint16_t*>(W1s), static_cast<const uint8_t*>(W3q),
-                               static_cast<const uint16_t*>(W3s), r.offsets, TK, n, (int)d, (int)f, h, stream),
+                               static_cast<const uint16_t*>(W3s), r.offsets, TK, n, (int)d, (int)f, 8 * cus, h,
+                               stream),
              "up-projection kernel launch");
   MOE_LAUNCH(moe::launch_q4_down(h, static_cast<const uint8_t*>(W2q), static_cast<const uint16_t*>(W2s),
-                                 r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
+                                 r.offsets, TK, n, (int)f, (int)d, p.splits, 8 * cus, o, stream),
              "down-projection kernel launch");
   MOE_LAUNCH(moe::launch_combine(o, p.splits, TK, r.topk_w, r.slot_pos, T, d, K, y, stream),
              "combine kernel launch");

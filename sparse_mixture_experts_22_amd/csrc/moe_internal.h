@@ -111,9 +111,9 @@ hipError_t launch_quantize_q4(const uint16_t* W, int n, int R, int C, uint8_t* c
 // Decode-size projections on 4-bit weights (same row layout as the bf16 ones).
 hipError_t launch_q4_up(const uint16_t* x, int64_t T, const int* perm_token, const uint8_t* Q1,
                         const uint16_t* S1, const uint8_t* Q3, const uint16_t* S3, const int* offsets,
-                        int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s);
+                        int64_t TK, int n, int d, int f, int cus, uint16_t* h, hipStream_t s);
 hipError_t launch_q4_down(const uint16_t* h, const uint8_t* Q2, const uint16_t* S2, const int* offsets,
-                          int64_t TK, int n, int f, int d, int splits, float* o, hipStream_t s);
+                          int64_t TK, int n, int f, int d, int splits, int cus, float* o, hipStream_t s);
 
 // ----------------------------------------------------------------- combine
 // y[t][:] = sum_k topk_w[t][k] * (sum_s o[s][slot_pos[t][k]][:]), k and s ascending.

@@ -43,7 +43,6 @@ constexpr int Q4G = 128;            // reduction indices per scale group
 #define MOE_Q4_STAGES 3
 #endif
 constexpr int Q4_STAGES = MOE_Q4_STAGES;  // blocks of codes in the register ring
-constexpr int Q4_TILES = 4;               // 16-column MFMA tiles per wave
 constexpr uint32_t kBias136 = 0x4308u;  // bf16 136.0
 
 __global__ __launch_bounds__(256) void quantize_q4_kernel(const uint16_t* __restrict__ W, int n, int R,
@@ -103,23 +102,25 @@ __device__ __forceinline__ bf16x8_t dq4(uint32_t w, uint32_t m, uint32_t c) {
   return *reinterpret_cast<bf16x8_t*>(&r);
 }
 
-// A workgroup covers 128 columns; a wave streams Q4_TILES = 4 column tiles
-// (64 columns), which keeps every in-flight load in a VGPR (no register
-// spilling, two to three waves per SIMD).
+// A wave streams TPW 16-column tiles and a workgroup covers 32*TPW columns;
+// the launcher picks TPW so that the grid fills whole rounds of resident
+// workgroups (two per CU).  Every in-flight load stays in a VGPR.
 // MODE 1: up.  Wave w streams matrix w/2 (W1, W3) for column half w%2 over
 //         all groups; A rows gathered from x; h = SiLU(a) * b in bf16.
 // MODE 2: down.  Wave w streams column half w/2 over half w%2 of this split's
 //         groups; o[split] receives the fp32 partial sums.
-template <int MODE>
+template <int MODE, int TPW>
 __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint8_t* __restrict__ Q1, const uint16_t* __restrict__ S1,
     const uint8_t* __restrict__ Q3, const uint16_t* __restrict__ S3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ float red[4][4 * Q4_TILES][64];
+  // ring depth: three blocks while they fit in registers, two for wide waves
+  constexpr int STAGES = TPW <= 5 ? Q4_STAGES : 2;
+  __shared__ float red[4][4 * TPW][64];
 
-  const int NB = (N + 127) / 128;
+  const int NB = N / (32 * TPW);  // the launcher picks TPW with N % (32*TPW) == 0
   int bid = blockIdx.x;
   const int sp = bid % splits;
   bid /= splits;
@@ -150,9 +151,10 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
   const uint16_t* S = third ? S3 : S1;
   // this lane's 16 bytes of column tile 0 in group 0, and its scale column;
   // tile ct adds 1 KiB of codes and 16 scale columns, group blk N*64 bytes.
-  // N is a multiple of 128 (checked by the caller), so every column exists.
-  const int col0 = nb * 128 + half * 64 + c16;
-  const uint8_t* qsrc = Q + (int64_t)e * Kdim * (N / 2) + (int64_t)((nb * 128 + half * 64) / 16) * 1024 + lane * 16;
+  // N is a multiple of 32*TPW (chosen by the launcher), so every column exists.
+  const int tile0 = nb * 2 * TPW + half * TPW;  // first 16-column tile of this wave
+  const int col0 = tile0 * 16 + c16;
+  const uint8_t* qsrc = Q + (int64_t)e * Kdim * (N / 2) + (int64_t)tile0 * 1024 + lane * 16;
   const int64_t qtile = 1024;
   const uint16_t* ssrc = S + (int64_t)e * ngr * N + col0;
   // nibble mask and bf16 exponent pattern, uniform (kept in scalar registers)
@@ -172,30 +174,30 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     const int64_t arow = (MODE == 1) ? (int64_t)min(max(perm_token[p], 0), a_rows - 1) : (int64_t)p;
     const uint16_t* asrc = A + arow * Kdim + g * 32;
 
-    f32x4_t acc[Q4_TILES];
+    f32x4_t acc[TPW];
 #pragma unroll
-    for (int ct = 0; ct < Q4_TILES; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < TPW; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // register ring of Q4_STAGES blocks: the loads of the next Q4_STAGES-1
+    // register ring of STAGES blocks: the loads of the next STAGES-1
     // blocks are in flight while one block is multiplied
-    u32x4_t wq[Q4_STAGES][Q4_TILES];
-    bf16x8_t aq[Q4_STAGES][4];
-    float sq[Q4_STAGES][Q4_TILES];
-    auto load = [&](int blk, u32x4_t (&w)[Q4_TILES], bf16x8_t (&a)[4], float (&s)[Q4_TILES]) {
+    u32x4_t wq[STAGES][TPW];
+    bf16x8_t aq[STAGES][4];
+    float sq[STAGES][TPW];
+    auto load = [&](int blk, u32x4_t (&w)[TPW], bf16x8_t (&a)[4], float (&s)[TPW]) {
 #pragma unroll
-      for (int ct = 0; ct < Q4_TILES; ++ct) {
+      for (int ct = 0; ct < TPW; ++ct) {
         w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * N * 64);
         s[ct] = __uint_as_float((uint32_t)ssrc[(int64_t)blk * N + ct * 16] << 16);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8_t*>(asrc + (int64_t)blk * Q4G + 8 * j);
     };
-    auto block = [&](const u32x4_t (&w)[Q4_TILES], const bf16x8_t (&a)[4], const float (&s)[Q4_TILES]) {
+    auto block = [&](const u32x4_t (&w)[TPW], const bf16x8_t (&a)[4], const float (&s)[TPW]) {
       f32x4_t corr = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) corr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], bias, corr, 0, 0, 0);
 #pragma unroll
-      for (int ct = 0; ct < Q4_TILES; ++ct) {
+      for (int ct = 0; ct < TPW; ++ct) {
         f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], dq4(w[ct][j], nib_mask, nib_base), t, 0, 0, 0);
@@ -206,15 +208,15 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
       }
     };
 #pragma unroll
-    for (int st = 0; st < Q4_STAGES - 1; ++st)
+    for (int st = 0; st < STAGES - 1; ++st)
       if (wb0 + st < wb1) load(wb0 + st, wq[st], aq[st], sq[st]);
-    for (int blk = wb0; blk < wb1; blk += Q4_STAGES) {
+    for (int blk = wb0; blk < wb1; blk += STAGES) {
 #pragma unroll
-      for (int st = 0; st < Q4_STAGES; ++st) {
-        const int ahead = blk + st + Q4_STAGES - 1;
+      for (int st = 0; st < STAGES; ++st) {
+        const int ahead = blk + st + STAGES - 1;
         if (ahead < wb1)
-          load(ahead, wq[(st + Q4_STAGES - 1) % Q4_STAGES], aq[(st + Q4_STAGES - 1) % Q4_STAGES],
-               sq[(st + Q4_STAGES - 1) % Q4_STAGES]);
+          load(ahead, wq[(st + STAGES - 1) % STAGES], aq[(st + STAGES - 1) % STAGES],
+               sq[(st + STAGES - 1) % STAGES]);
         if (blk + st < wb1) block(wq[st], aq[st], sq[st]);
       }
     }
@@ -223,20 +225,20 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     // are waves 2ch and 2ch+1.
     __syncthreads();
 #pragma unroll
-    for (int ct = 0; ct < Q4_TILES; ++ct)
+    for (int ct = 0; ct < TPW; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][ct * 4 + i][lane] = acc[ct][i];
     __syncthreads();
     {
       const int ch = tid >> 7;           // column half finished by this thread
-      const int q0 = ((tid >> 6) & 1) * 8;
+      const int q0 = ((tid >> 6) & 1) * 2 * TPW;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 2 * TPW; ++k) {
         const int q = q0 + k;
         const int ct = q >> 2;
         const int i = q & 3;
         const int row = m0 + 4 * (lane >> 4) + i;  // D row of the 16x16 MFMA
-        const int colo = nb * 128 + ch * 64 + ct * 16 + (lane & 15);
+        const int colo = (nb * 2 * TPW + ch * TPW + ct) * 16 + (lane & 15);
         if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
         if (MODE == 1) {
           const float va = red[ch][q][lane];
@@ -262,21 +264,61 @@ hipError_t launch_quantize_q4(const uint16_t* W, int n, int R, int C, uint8_t* c
   return hipGetLastError();
 }
 
+namespace {
+// Tiles per wave for a projection with N output columns.  The grid has
+// N / (32 * tpw) * mult workgroups, two resident per CU, and a launch takes
+// about (rounds of resident workgroups) x (work per workgroup, ~ tpw).  On a
+// tie the wider waves win: fewer rounds measured faster (Mixtral decode down
+// projection: 512 workgroups of tpw 8 beat 1024 of tpw 4 by 0.7% per layer).
+int pick_tpw(int N, int64_t mult, int cus) {
+  const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+  int best = 4;
+  int64_t best_cost = -1;
+  for (int tpw : {4, 5, 6, 7, 8}) {
+    if (N % (32 * tpw) != 0) continue;
+    const int64_t wgs = (int64_t)(N / (32 * tpw)) * mult;
+    const int64_t cost = (wgs + slots - 1) / slots * tpw;
+    if (best_cost < 0 || cost <= best_cost) { best = tpw; best_cost = cost; }
+  }
+  return best;
+}
+}  // namespace
+
 hipError_t launch_q4_up(const uint16_t* x, int64_t T, const int* perm_token, const uint8_t* Q1,
                         const uint16_t* S1, const uint8_t* Q3, const uint16_t* S3, const int* offsets,
-                        int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s) {
-  const int NB = (f + 127) / 128;
-  hipLaunchKernelGGL((skinny_q4_kernel<1>), dim3((unsigned)(n * NB)), dim3(256), 0, s, x, perm_token, Q1, S1,
-                     Q3, S3, offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr);
+                        int64_t TK, int n, int d, int f, int cus, uint16_t* h, hipStream_t s) {
+  const int tpw = pick_tpw(f, n, cus);
+  const dim3 grid((unsigned)(n * (f / (32 * tpw))));
+#define MOE_Q4_UP(TPW_)                                                                                   \
+  hipLaunchKernelGGL((skinny_q4_kernel<1, TPW_>), grid, dim3(256), 0, s, x, perm_token, Q1, S1, Q3, S3, \
+                     offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr)
+  switch (tpw) {
+    case 5: MOE_Q4_UP(5); break;
+    case 6: MOE_Q4_UP(6); break;
+    case 7: MOE_Q4_UP(7); break;
+    case 8: MOE_Q4_UP(8); break;
+    default: MOE_Q4_UP(4); break;
+  }
+#undef MOE_Q4_UP
   return hipGetLastError();
 }
 
 hipError_t launch_q4_down(const uint16_t* h, const uint8_t* Q2, const uint16_t* S2, const int* offsets,
-                          int64_t TK, int n, int f, int d, int splits, float* o, hipStream_t s) {
-  const int NB = (d + 127) / 128;
-  hipLaunchKernelGGL((skinny_q4_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(256), 0, s, h,
-                     (const int*)nullptr, Q2, S2, (const uint8_t*)nullptr, (const uint16_t*)nullptr, offsets,
-                     n, f, d, splits, (int)TK, TK, (uint16_t*)nullptr, o);
+                          int64_t TK, int n, int f, int d, int splits, int cus, float* o, hipStream_t s) {
+  const int tpw = pick_tpw(d, (int64_t)n * splits, cus);
+  const dim3 grid((unsigned)(n * (d / (32 * tpw)) * splits));
+#define MOE_Q4_DOWN(TPW_)                                                                                  \
+  hipLaunchKernelGGL((skinny_q4_kernel<2, TPW_>), grid, dim3(256), 0, s, h, (const int*)nullptr, Q2, S2, \
+                     (const uint8_t*)nullptr, (const uint16_t*)nullptr, offsets, n, f, d, splits, (int)TK, TK, \
+                     (uint16_t*)nullptr, o)
+  switch (tpw) {
+    case 5: MOE_Q4_DOWN(5); break;
+    case 6: MOE_Q4_DOWN(6); break;
+    case 7: MOE_Q4_DOWN(7); break;
+    case 8: MOE_Q4_DOWN(8); break;
+    default: MOE_Q4_DOWN(4); break;
+  }
+#undef MOE_Q4_DOWN
   return hipGetLastError();
 }
 

@@ -55,6 +55,21 @@ def test_traffic_is_scaled_by_the_calibration_copy(tmp_path, capsys):
     assert k["sources_sha256"] == bench.sources_hash("grouped_gemm_kernel<1>")
 
 
+def test_template_instances_share_their_kernels_sources(tmp_path, capsys):
+    q4 = "void moe::(anonymous namespace)::skinny_q4_kernel<1, 7>(unsigned short const*)"
+    _write_counters(str(tmp_path / "f"), [_row(1, "__amd_rocclr_copyBuffer", 4096, "FETCH_SIZE", 524288.0),
+                                          _row(2, q4, 131072, "FETCH_SIZE", 100.0)])
+    _write_counters(str(tmp_path / "w"), [_row(1, "__amd_rocclr_copyBuffer", 4096, "WRITE_SIZE", 1048576.0),
+                                          _row(2, q4, 131072, "WRITE_SIZE", 10.0)])
+    out_json = str(tmp_path / "traffic.json")
+    bench.summarize_counters([str(tmp_path / "f"), str(tmp_path / "w")], out_json)
+    capsys.readouterr()
+    k = json.load(open(out_json))["kernels"]["skinny_q4_kernel<1, 7>"]
+    assert k["sources_sha256"] == bench.sources_hash("skinny_q4_kernel<2, 8>") == bench.sources_hash("skinny_q4_kernel")
+    assert bench.sources_hash("skinny_q4_kernel") != bench.sources_hash("skinny_kernel")
+    assert bench.kernel_sources("combine_kernel<4>") is None
+
+
 def test_stored_traffic_is_dropped_when_the_sources_change(tmp_path, monkeypatch):
     path = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_JSON", str(path))

@@ -84,6 +84,11 @@ def _run_q4(inp, rows=None):
     (5, 128, 128, 4, 1),
     (300, 256, 256, 8, 2),    # > 16 rows per expert: several passes over the weights
     (64, 512, 640, 16, 4),
+    # wide grids, where the launcher gives each wave more column tiles so the
+    # grid fills whole rounds of resident workgroups:
+    (24, 256, 7168, 16, 2),   # up projection: 512 workgroups of 7 tiles per wave instead of 896 of 4
+    (24, 7168, 256, 16, 2),   # down projection: 7 tiles per wave
+    (32, 4096, 256, 8, 2),    # down projection as at the Mixtral decode shape: 8 tiles per wave
 ])
 def test_forward_q4_shapes(T, d, f, n, K):
     log(f"forward_q4: T={T} d={d} f={f} n={n} K={K}")
