@@ -68,48 +68,81 @@ struct Tile {
   int slot;    // >= 0: a k-piece of a split tile, partial sums go to this slot
 };
 
-__device__ int count_tiles(const int* __restrict__ offsets, int n, int NT) {
-  int total = 0;
-  for (int e = 0; e < n; ++e) {
-    const int c = offsets[e + 1] - offsets[e];
-    total += ((c + BM - 1) / BM) * NT;
+// Row tiles per expert, gathered by each wave in parallel: lane l holds
+// experts 4l .. 4l+3 (n <= 256), `pre` counts the row tiles of the experts
+// before 4l and `total` those of all experts.  Serial loops over the experts
+// here cost several microseconds per workgroup at n = 64, on the critical path
+// between one tile and the next on a CU.
+static_assert(kMaxN <= 256, "expert_tiles covers 4 experts per lane");
+struct ExpertTiles {
+  int mt[4];
+  int pre, total;
+};
+
+__device__ ExpertTiles expert_tiles(const int* __restrict__ offsets, int n) {
+  const int lane = threadIdx.x & 63;
+  ExpertTiles t;
+  int s = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    const int c = e < n ? offsets[e + 1] - offsets[e] : 0;
+    t.mt[j] = (c + BM - 1) / BM;
+    s += t.mt[j];
   }
-  return total;
+  int incl = s;  // inclusive scan over the lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  t.pre = incl - s;
+  t.total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+  return t;
 }
 
 // Position L of the tile list -> expert, row tile, column tile.  The list is
-// expert-major, then groups of NGROUP column tiles, then row tiles.
-__device__ bool tile_at(const int* __restrict__ offsets, int n, int NT, int L, Tile& tc) {
-  for (int e = 0; e < n; ++e) {
-    const int c = offsets[e + 1] - offsets[e];
-    const int mt = (c + BM - 1) / BM;
-    const int cnt = mt * NT;
-    if (L < cnt) {
-      const int ng = NT / NGROUP;
-      const int gsz = mt * NGROUP;
-      const int grp = L / gsz;
-      int m, nt;
-      if (grp < ng) {
-        const int rem = L - grp * gsz;
-        m = rem / NGROUP;
-        nt = grp * NGROUP + rem % NGROUP;
-      } else {
-        const int rem = L - ng * gsz;
-        const int gt = NT - ng * NGROUP;
-        m = rem / gt;
-        nt = ng * NGROUP + rem % gt;
-      }
-      tc.e = e;
-      tc.m = m;
-      tc.nt = nt;
-      tc.row0 = offsets[e] + m * BM;
-      const int left = offsets[e + 1] - tc.row0;
-      tc.rows = left < BM ? left : BM;
-      return true;
+// expert-major, then groups of NGROUP column tiles, then row tiles; expert e
+// owns positions [NT * P(e), NT * P(e+1)) with P the running sum of row tiles.
+__device__ bool tile_at(const int* __restrict__ offsets, const ExpertTiles& et, int NT, int L, Tile& tc) {
+  int hit = -1, base = 0, mt = 0;
+  int p = et.pre;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (et.mt[j] > 0 && L >= NT * p && L < NT * (p + et.mt[j])) {
+      hit = j;
+      base = p;
+      mt = et.mt[j];
     }
-    L -= cnt;
+    p += et.mt[j];
   }
-  return false;
+  const unsigned long long owner = __ballot(hit >= 0);  // at most one lane
+  if (owner == 0) return false;
+  const int src = __ffsll(owner) - 1;
+  const int e = __builtin_amdgcn_readfirstlane(4 * src + __shfl(hit, src));
+  mt = __builtin_amdgcn_readfirstlane(__shfl(mt, src));
+  L -= NT * __builtin_amdgcn_readfirstlane(__shfl(base, src));
+  const int ng = NT / NGROUP;
+  const int gsz = mt * NGROUP;
+  const int grp = L / gsz;
+  int m, nt;
+  if (grp < ng) {
+    const int rem = L - grp * gsz;
+    m = rem / NGROUP;
+    nt = grp * NGROUP + rem % NGROUP;
+  } else {
+    const int rem = L - ng * gsz;
+    const int gt = NT - ng * NGROUP;
+    m = rem / gt;
+    nt = ng * NGROUP + rem % gt;
+  }
+  tc.e = e;
+  tc.m = m;
+  tc.nt = nt;
+  tc.row0 = offsets[e] + m * BM;
+  const int left = offsets[e + 1] - tc.row0;
+  tc.rows = left < BM ? left : BM;
+  return true;
 }
 
 // Work of one XCD: the contiguous tiles [beg, beg + cnt) of the list.  `q`
@@ -141,10 +174,11 @@ __device__ XcdPlan xcd_plan(int total, int x, int cus, int nk, bool may_split) {
 }
 
 // Maps this workgroup to its tile (or k-piece of a tile); false if it has none.
-// All threads compute the same answer from offsets[0..n] (uniform loads).
+// Every wave computes the same answer from offsets[0..n].
 __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int nk, int cus,
                             bool may_split, Tile& tc) {
-  const int total = count_tiles(offsets, n, NT);
+  const ExpertTiles et = expert_tiles(offsets, n);
+  const int total = et.total * NT;
   const int x = blockIdx.x % kXcds;
   const int i = blockIdx.x / kXcds;
   const XcdPlan t = xcd_plan(total, x, cus, nk, may_split);
@@ -166,7 +200,7 @@ __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int 
     tc.k1 = min(nk, tc.k0 + t.chunk);
     tc.slot = x * cus + u;
   }
-  return tile_at(offsets, n, NT, L, tc);
+  return tile_at(offsets, et, NT, L, tc);
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -516,10 +550,11 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict_
   const int x = blockIdx.x / (16 * tmax);
   const int t = (blockIdx.x / 16) % tmax;
   const int rblk = blockIdx.x % 16;
-  const XcdPlan pl = xcd_plan(count_tiles(offsets, n, NT), x, cus, nk, true);
+  const ExpertTiles et = expert_tiles(offsets, n);
+  const XcdPlan pl = xcd_plan(et.total * NT, x, cus, nk, true);
   if (pl.s == 1 || t >= pl.r) return;
   Tile tc;
-  if (!tile_at(offsets, n, NT, pl.beg + pl.q + t, tc)) return;
+  if (!tile_at(offsets, et, NT, pl.beg + pl.q + t, tc)) return;
   // thread -> (row of 4 in this block's 16, 4 consecutive columns)
   const int c4 = (threadIdx.x & 63) * 4;
   const int c = tc.nt * 256 + c4;
