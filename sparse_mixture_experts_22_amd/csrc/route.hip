@@ -485,31 +485,56 @@ void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t 
 // workgroup, thread e per expert; blocks summed in order in double):
 //   frac[e] = counts[e] / (T*K), prob[e] = sum_t p_t[e] / T,
 //   aux_loss = alpha * n * sum_e frac[e] * prob[e]   (summed in expert order).
-__global__ __launch_bounds__(256) void route_stats_kernel(const int* __restrict__ hist,
-                                                          const float* __restrict__ probsum, int nb,
-                                                          int64_t T, int n, int K, float alpha,
-                                                          float* __restrict__ frac,
-                                                          float* __restrict__ prob,
-                                                          float* __restrict__ aux_loss) {
+// One workgroup of 1024 threads.  Thread (part p, expert e), e fastest, sums
+// the routing blocks [p*nb/P, (p+1)*nb/P) of expert e in block order
+// (consecutive threads read consecutive experts of a block), and the parts
+// are then added in part order, so the result is deterministic.  P gives each
+// part about 8 blocks, within the 1024/n parts the workgroup holds.
+constexpr int kStatsThreads = 1024;
+__global__ __launch_bounds__(kStatsThreads) void route_stats_kernel(const int* __restrict__ hist,
+                                                                    const float* __restrict__ probsum, int nb,
+                                                                    int64_t T, int n, int K, float alpha,
+                                                                    float* __restrict__ frac,
+                                                                    float* __restrict__ prob,
+                                                                    float* __restrict__ aux_loss) {
+  __shared__ long long cnt_s[kStatsThreads];
+  __shared__ double p_s[kStatsThreads];
   __shared__ double fp_s[kMaxN];
   const int tid = threadIdx.x;
-  for (int e = tid; e < n; e += blockDim.x) {
+  const int P = max(1, min(kStatsThreads / n, nb / 8));  // n <= kMaxN = 256
+  const int e = tid % n;
+  const int part = tid / n;
+  if (part < P) {
+    const int b0 = (int)((int64_t)part * nb / P);
+    const int b1 = (int)((int64_t)(part + 1) * nb / P);
     long long c = 0;
     double p = 0.0;
-    for (int b = 0; b < nb; ++b) {
+#pragma unroll 8
+    for (int b = b0; b < b1; ++b) {
       c += hist[(int64_t)b * n + e];
       p += (double)probsum[(int64_t)b * n + e];
     }
+    cnt_s[tid] = c;
+    p_s[tid] = p;
+  }
+  __syncthreads();
+  if (tid < n) {
+    long long c = 0;
+    double p = 0.0;
+    for (int q = 0; q < P; ++q) {
+      c += cnt_s[q * n + tid];
+      p += p_s[q * n + tid];
+    }
     const double fe = (double)c / ((double)T * K);
     const double pe = p / (double)T;
-    if (frac != nullptr) frac[e] = (float)fe;
-    if (prob != nullptr) prob[e] = (float)pe;
-    fp_s[e] = fe * pe;
+    if (frac != nullptr) frac[tid] = (float)fe;
+    if (prob != nullptr) prob[tid] = (float)pe;
+    fp_s[tid] = fe * pe;
   }
   __syncthreads();
   if (tid == 0 && aux_loss != nullptr) {
     double acc = 0.0;
-    for (int e = 0; e < n; ++e) acc += fp_s[e];
+    for (int q = 0; q < n; ++q) acc += fp_s[q];
     aux_loss[0] = (float)((double)alpha * n * acc);
   }
 }
@@ -687,7 +712,7 @@ hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_
   if (e != hipSuccess) return e;
   const int BT = route_block_tokens(n);
   const int nb = (int)((T + BT - 1) / BT);
-  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(256), 0, s, rb.hist, probsum, nb, T, n, K, alpha,
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(kStatsThreads), 0, s, rb.hist, probsum, nb, T, n, K, alpha,
                      frac, prob, aux_loss);
   return hipGetLastError();
 }
@@ -727,7 +752,7 @@ hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, in
                      rb.topk_idx, rb.topk_w, rb.hist, probsum);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(256), 0, s, rb.hist, probsum, (int)nb, T, n, K,
+  hipLaunchKernelGGL(route_stats_kernel, dim3(1), dim3(kStatsThreads), 0, s, rb.hist, probsum, (int)nb, T, n, K,
                      alpha, frac, prob, aux_loss);
   return hipGetLastError();
 }
