@@ -124,12 +124,69 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__
   }
 }
 
+// The same sum when a token has many slots of which few are set (expert-choice
+// routing passes one slot per expert).  A workgroup takes 1024 columns of one
+// token; wave 0 reads the token's K slots in parallel and lists the set ones in
+// slot order, then every thread adds only those, in that order, so the result
+// equals combine_kernel's bit for bit.
+constexpr int kSparseCombineMinK = 8;
+__global__ __launch_bounds__(256) void combine_sparse_kernel(const float* __restrict__ o, int splits,
+                                                             int64_t TK, const float* __restrict__ topk_w,
+                                                             const int* __restrict__ slot_pos, int64_t d,
+                                                             int K, float* __restrict__ y) {
+  __shared__ int pos_s[kMaxN];
+  __shared__ float w_s[kMaxN];
+  __shared__ int cnt_s;
+  const int64_t chunks = (d + 1023) / 1024;
+  const int64_t t = blockIdx.x / chunks;
+  const int64_t c = (blockIdx.x % chunks) * 1024 + threadIdx.x * 4;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int cnt = 0;
+    for (int base = 0; base < K; base += 64) {
+      const int k = base + lane;
+      const int sp = k < K ? slot_pos[t * K + k] : -1;
+      const unsigned long long set = __ballot(sp >= 0);
+      if (sp >= 0) {
+        const int r = cnt + __popcll(set & ((1ull << lane) - 1));
+        pos_s[r] = (int)min<int64_t>(sp, TK - 1);
+        w_s[r] = topk_w[t * K + k];
+      }
+      cnt += __popcll(set);
+    }
+    if (lane == 0) cnt_s = cnt;
+  }
+  __syncthreads();
+  if (c >= d) return;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int cnt = cnt_s;
+  for (int r = 0; r < cnt; ++r) {
+    const int64_t pos = pos_s[r];
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(o + pos * d + c);
+    for (int sidx = 1; sidx < splits; ++sidx) {
+      const f32x4_t q = *reinterpret_cast<const f32x4_t*>(o + ((int64_t)sidx * TK + pos) * d + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += q[j];
+    }
+    const float w = w_s[r];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = acc[j] + w * v[j];
+  }
+  *reinterpret_cast<f32x4_t*>(y + t * d + c) = acc;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* o, int splits, int64_t TK, const float* topk_w,
                           const int* slot_pos, int64_t T, int64_t d, int K, float* y, hipStream_t s) {
   const bool vec = (d % 4) == 0 && (reinterpret_cast<uintptr_t>(o) % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(y) % 16) == 0;
+  if (vec && K >= kSparseCombineMinK && K <= kMaxN && T * ((d + 1023) / 1024) <= INT32_MAX) {
+    const int64_t blocks = T * ((d + 1023) / 1024);
+    hipLaunchKernelGGL(combine_sparse_kernel, dim3((unsigned)blocks), dim3(256), 0, s, o, splits, TK, topk_w,
+                       slot_pos, d, K, y);
+    return hipGetLastError();
+  }
   const int64_t items = T * (vec ? d / 4 : d);
   const unsigned blocks = (unsigned)((items + 255) / 256);
   if (vec)
