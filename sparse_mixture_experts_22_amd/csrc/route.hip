@@ -133,6 +133,7 @@ __device__ void route_epilogue(const float* logits_s, int ld, int BT, int64_t t0
       const int i = idx / n;
       const int e = idx % n;
       ec_probs[(t0 + i) * n + e] = expf(logits_s[i * ld + e] - tmax_s[i]) / tsum_s[i];
+      slot_pos[(t0 + i) * n + e] = -1;  // the selection writes only the chosen slots
     }
     return;
   }
@@ -559,25 +560,34 @@ void launch_router_bf16(const uint16_t* x, int64_t T, int64_t d, int n, int K, c
 // e of probs [T][n] by a 4-pass 8-bit radix select on the float bit patterns
 // (scores are >= 0, so their bits order like their values), then keeps every
 // token above that threshold and the earliest tokens equal to it.  Rows go to
-// e*C + j in ascending token order.  The column is staged in LDS when it fits.
+// e*C + j in ascending token order; slot_pos was set to -1 by the router, so
+// only the chosen slots are written.  The column is staged in LDS when it fits.
+// Scores cluster near 1/n, so most keys share their upper digits: each wave
+// keeps its own histogram and adds a run of equal digits with one atomic.
+// The compaction gives each wave a contiguous token range and ranks within it
+// by ballot, so LDS reads are consecutive and the order is the token order.
 constexpr int kEcLdsKeys = 32768;  // 128 KiB of keys
-__global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __restrict__ probs, int64_t T,
-                                                             int n, int C, int* __restrict__ perm_token,
-                                                             int* __restrict__ slot_pos,
-                                                             int* __restrict__ counts,
-                                                             int* __restrict__ offsets) {
+constexpr int kEcWaves = 16;
+__global__ __launch_bounds__(kEcWaves * 64) void expert_choice_kernel(const float* __restrict__ probs, int64_t T,
+                                                                      int n, int C, int* __restrict__ perm_token,
+                                                                      int* __restrict__ slot_pos,
+                                                                      int* __restrict__ counts,
+                                                                      int* __restrict__ offsets) {
   __shared__ uint32_t keys_s[kEcLdsKeys];
-  __shared__ int hist[256];
+  __shared__ int hist_s[kEcWaves][256];
   __shared__ int suffix[256];
   __shared__ uint32_t prefix_s;
   __shared__ int need_s;
-  __shared__ int scan_s[1024];
+  __shared__ int wcnt_s[kEcWaves][2];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1;  // lanes before this one
   const float* col = probs + e;
   const bool staged = T <= kEcLdsKeys;
   if (staged)
-    for (int64_t t = tid; t < T; t += 1024) keys_s[t] = __float_as_uint(col[t * n]);
+    for (int64_t t = tid; t < T; t += kEcWaves * 64) keys_s[t] = __float_as_uint(col[t * n]);
   auto key = [&](int64_t t) -> uint32_t { return staged ? keys_s[t] : __float_as_uint(col[t * n]); };
   if (tid == 0) {
     prefix_s = 0u;
@@ -589,17 +599,33 @@ __global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __rest
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
     const uint32_t himask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < kEcWaves * 256; i += kEcWaves * 64) (&hist_s[0][0])[i] = 0;
     __syncthreads();
     const uint32_t prefix = prefix_s;
     const int need = need_s;
-    for (int64_t t = tid; t < T; t += 1024) {
+    for (int64_t t = tid; t < T; t += kEcWaves * 64) {
       const uint32_t k = key(t);
-      if ((k & himask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      const bool match = (k & himask) == prefix;
+      const int dg = (int)((k >> shift) & 255u);
+      const unsigned long long act = __ballot(match);
+      if (act != 0ull) {
+        const int lead = __ffsll((long long)act) - 1;
+        const int dl = __shfl(dg, lead);
+        const unsigned long long same = __ballot(match && dg == dl);
+        if (lane == lead)
+          atomicAdd(&hist_s[wave][dl], __popcll(same));
+        else if (match && dg != dl)
+          atomicAdd(&hist_s[wave][dg], 1);
+      }
     }
     __syncthreads();
     // suffix[dg] = number of candidates with digit >= dg (inclusive scan from the top)
-    if (tid < 256) suffix[tid] = hist[tid];
+    if (tid < 256) {
+      int h = 0;
+#pragma unroll
+      for (int w = 0; w < kEcWaves; ++w) h += hist_s[w][tid];
+      suffix[tid] = h;
+    }
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
       const int v = (tid < 256 && tid + off < 256) ? suffix[tid + off] : 0;
@@ -619,53 +645,46 @@ __global__ __launch_bounds__(1024) void expert_choice_kernel(const float* __rest
   }
   const uint32_t thr = prefix_s;  // the C-th largest key
   const int need = need_s;        // tokens equal to it that are taken (earliest first)
-  // contiguous token chunk of this thread
-  const int64_t chunk = (T + 1023) / 1024;
-  const int64_t b0 = min<int64_t>(T, tid * chunk);
-  const int64_t b1 = min<int64_t>(T, b0 + chunk);
-  int n_eq = 0;
-  for (int64_t t = b0; t < b1; ++t) n_eq += key(t) == thr;
-  // exclusive scan of n_eq over threads (Hillis-Steele on LDS)
-  scan_s[tid] = n_eq;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? scan_s[tid - off] : 0;
-    __syncthreads();
-    scan_s[tid] += v;
-    __syncthreads();
+  // wave w ranks tokens [w*span, (w+1)*span), span a multiple of 64
+  const int64_t span = ((T + kEcWaves - 1) / kEcWaves + 63) / 64 * 64;
+  const int64_t wb0 = min<int64_t>(T, wave * span);
+  const int64_t wb1 = min<int64_t>(T, wb0 + span);
+  int n_gt = 0, n_eq = 0;
+  for (int64_t t0 = wb0; t0 < wb1; t0 += 64) {
+    const int64_t t = t0 + lane;
+    const bool in = t < wb1;
+    const uint32_t k = in ? key(t) : 0u;
+    n_gt += __popcll(__ballot(in && k > thr));
+    n_eq += __popcll(__ballot(in && k == thr));
   }
-  const int eq_before = scan_s[tid] - n_eq;
-  __syncthreads();
-  int n_sel = 0;
-  {
-    int eq_seen = eq_before;
-    for (int64_t t = b0; t < b1; ++t) {
-      const uint32_t k = key(t);
-      if (k > thr) ++n_sel;
-      else if (k == thr) n_sel += (eq_seen++ < need);
-    }
+  if (lane == 0) {
+    wcnt_s[wave][0] = n_gt;
+    wcnt_s[wave][1] = n_eq;
   }
-  scan_s[tid] = n_sel;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? scan_s[tid - off] : 0;
-    __syncthreads();
-    scan_s[tid] += v;
-    __syncthreads();
+  // tokens equal to the threshold and tokens chosen in the ranges before this wave's
+  int eq_seen = 0, pos = e * C;
+  for (int w = 0; w < wave; ++w) {
+    const int gt_w = wcnt_s[w][0];
+    const int eq_w = wcnt_s[w][1];
+    pos += gt_w + min(max(need - eq_seen, 0), eq_w);
+    eq_seen += eq_w;
   }
-  int pos = e * C + (scan_s[tid] - n_sel);
-  int eq_seen = eq_before;
-  for (int64_t t = b0; t < b1; ++t) {
-    const uint32_t k = key(t);
-    bool sel = k > thr;
-    if (k == thr) sel = eq_seen++ < need;
+  for (int64_t t0 = wb0; t0 < wb1; t0 += 64) {
+    const int64_t t = t0 + lane;
+    const bool in = t < wb1;
+    const uint32_t k = in ? key(t) : 0u;
+    const bool eq = in && k == thr;
+    const unsigned long long eqm = __ballot(eq);
+    const bool sel = in && (k > thr || (eq && eq_seen + __popcll(eqm & below) < need));
+    const unsigned long long selm = __ballot(sel);
     if (sel) {
-      perm_token[pos] = (int)t;
-      slot_pos[t * n + e] = pos;
-      ++pos;
-    } else {
-      slot_pos[t * n + e] = -1;
+      const int p = pos + __popcll(selm & below);
+      perm_token[p] = (int)t;
+      slot_pos[t * n + e] = p;
     }
+    eq_seen += __popcll(eqm);
+    pos += __popcll(selm);
   }
 }
 
@@ -727,7 +746,7 @@ hipError_t launch_route_expert_choice(const uint16_t* x, const uint16_t* Wg, int
   launch_router_bf16(x, T, d, n, 1, rb, false, nullptr, INT32_MAX, s, rb.topk_w);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(expert_choice_kernel, dim3((unsigned)n), dim3(1024), 0, s, rb.topk_w, T, n, C,
+  hipLaunchKernelGGL(expert_choice_kernel, dim3((unsigned)n), dim3(kEcWaves * 64), 0, s, rb.topk_w, T, n, C,
                      rb.perm_token, rb.slot_pos, rb.counts, rb.offsets);
   return hipGetLastError();
 }

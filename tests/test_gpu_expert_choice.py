@@ -58,7 +58,9 @@ def _check_ec(inp, g, cf):
     (1000, 192, 8, 2.0, False),
     (257, 64, 130, 4.0, False),
     (200, 128, 8, 2.0, True),      # all scores tie: every expert takes tokens 0..C-1
+    (5000, 64, 8, 2.0, True),      # all tie, the C earliest tokens spread over many waves' ranges
     (100, 64, 4, 100.0, False),    # C = T
+    (40000, 64, 16, 1.0, False),   # T above the 32768 scores a workgroup stages in LDS
 ])
 def test_route_expert_choice_shapes(T, d, n, cf, zero):
     inp = make_inputs(T, d, 64, n, 2, dtype="bf16", seed=60 + T + n, wg_zero=zero, router_only=True)
