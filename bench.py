@@ -79,9 +79,12 @@ def upload(inp, dev, copies):
     return x, wg, w
 
 
-def _time_calls(fn, reps, stream):
+def _time_calls(fn, reps, stream, warm=3):
+    """Mean ms per call over `reps` calls, after `warm` untimed ones: the first calls after
+    the GPU has idled (host work, synchronisation) run at a lower engine clock."""
     import torch
-    fn()
+    for i in range(warm):
+        fn(i)
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
