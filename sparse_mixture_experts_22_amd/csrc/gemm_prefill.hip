@@ -518,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
           if (row < tc.rows && tc.row0 + row < TK) {
             const float a = acc[i][0][r];
             const float b = acc[i][1][r];
-            hout[(int64_t)(tc.row0 + row) * N + c] = f32_to_bf16_rne(silu_f32(a) * b);
+            hout[(int64_t)(tc.row0 + row) * N + c] = f32_to_bf16_rne(silu_bf16out(a) * b);
           }
         }
     }

@@ -129,4 +129,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
 
+// SiLU for outputs that are rounded to bf16 right away: a * 1/(1 + 2^(-a*log2 e))
+// with the hardware base-2 exponential and reciprocal (about 1 ulp each, a few
+// 1e-7 relative after the argument's rounding), far below bf16's 2^-9 step.
+// Saturates like the exact form: 2^(large) = inf gives 1/inf = 0, so -0.
+__device__ __forceinline__ float silu_bf16out(float a) {
+  return a * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a * 1.44269504088896341f));
+}
+
 }  // namespace moe

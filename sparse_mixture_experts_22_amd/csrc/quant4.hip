@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
         if (MODE == 1) {
           const float va = red[ch][q][lane];
           const float vb = red[2 + ch][q][lane];
-          hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_f32(va) * vb);
+          hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_bf16out(va) * vb);
         } else {
           const float v = red[2 * ch][q][lane] + red[2 * ch + 1][q][lane];
           oout[((int64_t)sp * TK + row_beg + row) * N + colo] = v;
