@@ -493,7 +493,38 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   const int lrow = m;
   const int lk = kg;
   // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
-  if (MODE == 2 && tc.slot >= 0) {
+  // Up projection: the h tile goes through LDS (the rings are idle now), so
+  // that each lane stores 16 contiguous bytes of one row: whole lines, and 8
+  // store instructions per wave instead of 64 two-byte ones.  Rows r and r + 4
+  // of a 32x32 block (the two half-waves) would share LDS banks, so the
+  // 16-byte chunk index is XOR-swizzled by bit 2 of the row.  (The same
+  // staging for the down projection's fp32 tile, in two 128 KiB halves, was
+  // slower: half the waves idle behind three barriers.)
+  if (MODE == 1) {
+    __syncthreads();  // every wave's ring loads have landed and its LDS reads are done
+    // h: 256 rows x 128 bf16 (64 KiB); chunk c of row r at c ^ (4 * ((r >> 2) & 1))
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+    const int cl = wn * 32 + lrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
+        const int ch = (cl >> 3) ^ (4 * ((row >> 2) & 1));
+        hs[row * 128 + ch * 8 + (cl & 7)] = f32_to_bf16_rne(silu_bf16out(acc[i][0][r]) * acc[i][1][r]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = q * 512 + tid;  // chunk idx % 16 (8 columns) of row idx / 16
+      const int row = idx >> 4;
+      const int ch = idx & 15;
+      const int col = tc.nt * 128 + ch * 8;  // N % 64 == 0: a chunk is wholly in or out
+      if (row < tc.rows && tc.row0 + row < TK && col < N)
+        *reinterpret_cast<u32x4_t*>(hout + (int64_t)(tc.row0 + row) * N + col) =
+            *reinterpret_cast<const u32x4_t*>(hs + row * 128 + (ch ^ (4 * ((row >> 2) & 1))) * 8);
+    }
+  } else if (tc.slot >= 0) {
     // a k-piece: the whole 256 x 256 partial tile goes to its slot
     float* dst = tail_ws + (int64_t)tc.slot * (BM * BN);
 #pragma unroll
@@ -505,23 +536,6 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
           const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
           dst[row * BN + wn * 64 + j * 32 + lrow] = acc[i][j][r];
         }
-    return;
-  }
-  if (MODE == 1) {
-    const int c = tc.nt * 128 + wn * 32 + lrow;
-    if (c < N) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * lk + (r & 3);
-          if (row < tc.rows && tc.row0 + row < TK) {
-            const float a = acc[i][0][r];
-            const float b = acc[i][1][r];
-            hout[(int64_t)(tc.row0 + row) * N + c] = f32_to_bf16_rne(silu_bf16out(a) * b);
-          }
-        }
-    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
