@@ -7,6 +7,8 @@ configurations run at full size in the same launch configuration the benchmark
 times; their routing is checked on every token and y on a seeded row sample
 (the oracle evaluates those rows one expert at a time).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -14,7 +16,7 @@ import oracle
 from gpu_util import config_inputs, log, sample_rows, upload
 from parity import (BF16_MAX_REL, BF16_MEAN_REL, F32_MAX_REL, F32_MEAN_REL, assert_rows_close,
                     check_routing)
-from synth import bf16_bits_from_f32, make_inputs
+from synth import bf16_bits_from_f32, bf16_bits_to_f32, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -172,3 +174,31 @@ def test_forward_full_configs(name, rows):
     assert np.isfinite(y).all()
     log(f"  {name}: rows={len(rs)} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} "
         f"near-ties={(r['margin'] <= 1e-3).sum()}")
+
+
+def _scaled_x(inp, factor):
+    """The same draw with x multiplied by `factor` and rounded to bf16 again."""
+    x = bf16_bits_to_f32(inp.x) * np.float32(factor)
+    return dataclasses.replace(inp, x=bf16_bits_from_f32(x))
+
+
+def max_gate_preactivation(inp):
+    """max |x . W1_e| over the tokens and experts (fp64, every expert; small shapes only)."""
+    x = inp.f64("x")
+    return max(float(np.abs(x @ inp.expert_f64("W1", e)).max()) for e in range(inp.n))
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (2000, 192, 320, 4, 2),   # tiled path
+    (40, 256, 320, 8, 2),     # weight-streaming path
+])
+def test_forward_large_activations(T, d, f, n, K):
+    """x scaled by 30: gate pre-activations reach well past 90 in both signs, where e^|a|
+    overflows fp32.  SiLU must saturate to a (large positive a) and to -0 (large negative a)
+    as the exact form does, and y must stay finite and match the oracle."""
+    inp = _scaled_x(make_inputs(T, d, f, n, K, dtype="bf16", seed=7070 + T), 30.0)
+    amax = max_gate_preactivation(inp)
+    log(f"  max |gate pre-activation| = {amax:.1f}")
+    assert amax > 90.0
+    y = _check_full(inp)
+    assert np.isfinite(y).all()

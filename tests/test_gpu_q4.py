@@ -1,6 +1,8 @@
 """4-bit expert weights on the GPU: moe_quantize_q4 must reproduce the oracle's
 codes and scales bit for bit, and moe_forward_q4 must match the fp64 oracle run
 on the dequantised weights (bf16 bounds)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -93,6 +95,15 @@ def _run_q4(inp, rows=None):
 def test_forward_q4_shapes(T, d, f, n, K):
     log(f"forward_q4: T={T} d={d} f={f} n={n} K={K}")
     _run_q4(make_inputs(T, d, f, n, K, dtype="bf16", seed=5150 + T + n))
+
+
+def test_forward_q4_large_activations():
+    """x scaled by 30, as in the bf16 test of the same name: SiLU saturates in both directions
+    on the 4-bit path too, and y stays finite."""
+    inp = make_inputs(40, 256, 384, 8, 2, dtype="bf16", seed=7171)
+    inp = dataclasses.replace(inp, x=bf16_bits_from_f32(bf16_bits_to_f32(inp.x) * np.float32(30.0)))
+    y = _run_q4(inp)
+    assert np.isfinite(y).all()
 
 
 @pytest.mark.slow
