@@ -44,8 +44,10 @@ constexpr int kPrefillBM = 256;
 // Average assignments per expert at or below which the weight-streaming
 // ("skinny") expert kernels are used instead of the tiled grouped GEMM.
 constexpr int kSkinnyMaxAvgRows = 24;
-// Split of the down projection's reduction in the skinny path.
-constexpr int kSkinnyDownSplits = 4;
+// Split of the down projection's reduction in the skinny path.  Two splits
+// (each wave streams half of its split's rows) beat four at the Mixtral decode
+// shape: longer weight streams per wave, and half the partial sums to combine.
+constexpr int kSkinnyDownSplits = 2;
 
 // ---------------------------------------------------------------- routing
 // Router + top-K + softmax + dispatch; fills every RouteBuffers output.
