@@ -53,7 +53,9 @@ def test_stats_full_configs(name):
 
 
 @pytest.mark.parametrize("T,d,n,K", [(1, 64, 8, 2), (129, 128, 8, 1), (300, 64, 5, 3), (257, 64, 130, 4),
-                                     (200, 64, 256, 8), (96, 64, 8, 8)])
+                                     (200, 64, 256, 8), (96, 64, 8, 8),
+                                     # block sums split into uneven parts: 94 blocks in 11 parts, 313 in 7
+                                     (3000, 64, 8, 2), (5000, 64, 130, 2)])
 def test_stats_shapes(T, d, n, K):
     _run(make_inputs(T, d, 64, n, K, dtype="bf16", seed=1234 + T + n, router_only=True), K, 0.01)
 
