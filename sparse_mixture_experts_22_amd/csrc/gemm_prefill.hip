@@ -572,14 +572,26 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict_
   // thread -> (row of 4 in this block's 16, 4 consecutive columns)
   const int c4 = (threadIdx.x & 63) * 4;
   const int c = tc.nt * 256 + c4;
+  const int row0 = rblk * 16 + (threadIdx.x >> 6) * 4;
+  // Every piece of the thread's 4 rows is loaded before any is added, so the
+  // loads travel together instead of one round trip per piece; loads past the
+  // piece count re-read the last piece (every piece holds all 256 rows) and
+  // are not added.  The sum runs in piece order, as the pieces' order fixes.
+  f32x4_t v[4][kMaxTailSplit];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int p = 0; p < kMaxTailSplit; ++p)
+      v[k][p] = *reinterpret_cast<const f32x4_t*>(
+          tail_ws + (int64_t)(x * cus + min(p, pl.s - 1) * pl.r + t) * (BM * BN) + (row0 + k) * BN + c4);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int row = rblk * 16 + (threadIdx.x >> 6) * 4 + k;
+    const int row = row0 + k;
     if (row >= tc.rows) break;
     f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int p = 0; p < pl.s; ++p)
-      sum += *reinterpret_cast<const f32x4_t*>(tail_ws + (int64_t)(x * cus + p * pl.r + t) * (BM * BN) +
-                                                row * BN + c4);
+#pragma unroll
+    for (int p = 0; p < kMaxTailSplit; ++p)
+      if (p < pl.s) sum += v[k][p];
     float* dst = o + (int64_t)(tc.row0 + row) * N + c;
     if (c + 3 < N) {
       *reinterpret_cast<f32x4_t*>(dst) = sum;
