@@ -482,8 +482,8 @@ void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t 
                      rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap, ec_probs);
 }
 
-// Router statistics from the per-block histograms and probability sums (one
-// workgroup, thread e per expert; blocks summed in order in double):
+// Router statistics from the per-block histograms and probability sums
+// (summed in double):
 //   frac[e] = counts[e] / (T*K), prob[e] = sum_t p_t[e] / T,
 //   aux_loss = alpha * n * sum_e frac[e] * prob[e]   (summed in expert order).
 // One workgroup of 1024 threads.  Thread (part p, expert e), e fastest, sums
