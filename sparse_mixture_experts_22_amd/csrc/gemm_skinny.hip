@@ -7,17 +7,21 @@
 // small batch every expert is still touched, and the layer is bound by reading
 // 3*d*f bf16 weights per touched expert.
 //
-// Work unit: one workgroup (4 waves) per (expert, 256-column block[, K split]);
-// each wave streams one 128-column half.  A workgroup thus reads 512
-// contiguous bytes of every weight row it touches (its two column halves at
-// the same rows), the pattern that streamed fastest in probes (6.2 TB/s
-// against 5.8 for 256-byte segments), and a decode launch is resident in one
-// round.  Each lane loads 8 rows x 16 bytes of the weight block (one 8x8 bf16
+// Work unit: one workgroup per (expert, column block[, K split]); each wave
+// streams a 128-column chunk of one matrix.  The up projection's workgroup has
+// 8 waves over 512 columns of W1 and the same 512 of W3, so it reads 1 KiB
+// contiguous bytes of each weight row it touches; the down projection's has 4
+// waves over 256 columns of W2, two per K half.  Longer row segments and fewer
+// concurrent streams read faster (probes: 1 KiB segments 6.3-6.5 TB/s, 512 B
+// 6.0-6.3, 256 B 5.7); the 1 KiB up blocks took the Mixtral decode up
+// projection from 313 to 301 us, while 512-column down blocks (four K splits
+// to fill the chip) measured slower than these.  A decode launch is resident
+// in one round.  Each lane loads 8 rows x 16 bytes of the weight block (one 8x8 bf16
 // block), transposes it in registers and feeds eight v_mfma_f32_16x16x32_bf16
 // directly as B operands - the weights never pass through LDS.  The MFMA column index c of fragment j stands for
 // weight column col0 + c*8 + j.  A fragments (16 token rows) come straight
 // from global memory (x or h is tiny and stays in L2).  Loads of the next K
-// step are issued before the MFMAs of the current one.  The 4 partial tiles
+// step are issued before the MFMAs of the current one.  The waves' partial tiles
 // are summed in LDS in wave order (fixed order, deterministic), then the
 // SwiGLU epilogue (up) or the fp32 store of a partial sum (down) follows.
 // Rows beyond 16 per expert are handled by further passes over the weights.
@@ -61,13 +65,13 @@ __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t&
     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fr[c], acc[c], 0, 0, 0);
 }
 
-// MODE 1: up.  Wave w streams matrix w/2 (W1, W3) over the whole of K for
-//         column half w%2; A rows are gathered from x via perm_token;
+// MODE 1: up.  Wave w streams matrix w/4 (W1, W3) over the whole of K for
+//         column chunk w%4; A rows are gathered from x via perm_token;
 //         h = SiLU(a) * b in bf16.
-// MODE 2: down.  Wave w streams W2 for column half w/2 over half w%2 of this
+// MODE 2: down.  Wave w streams W2 for column chunk w/2 over half w%2 of this
 //         split's K range; A rows are h; o[split] receives the fp32 partial sum.
 // With the ping-pong buffers a wave keeps two K steps of loads in flight
-// (2 workgroups per CU).  The variant without them fits 4 workgroups per CU
+// (8 waves per CU).  The variant without them fits 4 workgroups per CU
 // (a decode launch is resident in one round) but measured slower: per-wave
 // memory parallelism matters more here than occupancy.
 #ifndef MOE_SKINNY_PINGPONG
@@ -75,15 +79,26 @@ __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t&
 #endif
 constexpr int SKINNY_OCC = MOE_SKINNY_PINGPONG ? 2 : 4;
 
+// Waves per workgroup and weight columns per workgroup: the up projection
+// runs 8 waves (4 column quarters of W1 and the same 4 of W3), so a workgroup
+// reads 1 KiB of each of its two matrices' rows; the down projection runs 4.
+template <int MODE> struct SkinnyShape {
+  static constexpr int kWaves = MODE == 1 ? 8 : 4;
+  static constexpr int kCols = MODE == 1 ? 512 : 256;
+};
+
 template <int MODE>
-__global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
+__global__ __launch_bounds__(SkinnyShape<MODE>::kWaves * 64, SKINNY_OCC * 4 / SkinnyShape<MODE>::kWaves) void skinny_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ B3,
     const int* __restrict__ offsets, int n, int Kdim, int N, int splits, int a_rows, int64_t TK,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
-  __shared__ float red[4][32][64];  // per-wave partial accumulators
+  constexpr int NW = SkinnyShape<MODE>::kWaves;
+  constexpr int NCOL = SkinnyShape<MODE>::kCols;
+  constexpr int NCH = NCOL / 128;  // 128-column chunks per workgroup
+  __shared__ float red[NW][32][64];  // per-wave partial accumulators
 
-  const int NB = (N + 255) / 256;
+  const int NB = (N + NCOL - 1) / NCOL;
   int bid = blockIdx.x;
   const int sp = bid % splits;
   bid /= splits;
@@ -100,19 +115,19 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  // reduction range and column half of this wave, in steps of 32
+  // reduction range and column chunk of this wave, in steps of 32
   constexpr int KPARTS = (MODE == 1) ? 1 : 2;
   const int part = (MODE == 1) ? 0 : (wave & 1);
-  const int half = (MODE == 1) ? (wave & 1) : (wave >> 1);
+  const int half = (MODE == 1) ? (wave % NCH) : (wave >> 1);
   const int nkc = Kdim / 32;
   const int kc0 = (int)((int64_t)sp * nkc / splits);
   const int kc1 = (int)((int64_t)(sp + 1) * nkc / splits);
   const int wk0 = kc0 + (int)((int64_t)part * (kc1 - kc0) / KPARTS);
   const int wk1 = kc0 + (int)((int64_t)(part + 1) * (kc1 - kc0) / KPARTS);
 
-  const int col0 = nb * 256 + half * 128 + r16 * 8;
+  const int col0 = nb * NCOL + half * 128 + r16 * 8;
   const bool b_ok = col0 < N;
-  const uint16_t* bmat = (MODE == 1 && wave >= 2) ? B3 : B1;
+  const uint16_t* bmat = (MODE == 1 && wave >= NCH) ? B3 : B1;
   const uint16_t* bsrc = bmat + (int64_t)e * Kdim * N + (b_ok ? col0 : 0) + (int64_t)(g * 8) * N;
   const int64_t kstep = (int64_t)32 * N;
 
@@ -173,23 +188,24 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) red[wave][c * 4 + j][lane] = acc[c][j];
     __syncthreads();
-    // thread (qg = tid/64, lane) finishes slots q = qg*8 .. qg*8+7 of both
-    // column halves.  MODE 1: a of half ch is wave ch's, b is wave 2+ch's;
-    // MODE 2: the two k halves of column half ch are waves 2ch and 2ch+1.
+    // thread (qg = tid/64, lane) finishes slots q = qg*QPT .. qg*QPT+QPT-1 of
+    // every 128-column chunk.  MODE 1: a of chunk ch is wave ch's, b is wave
+    // NCH+ch's; MODE 2: the two k halves of chunk ch are waves 2ch and 2ch+1.
+    constexpr int QPT = 32 / NW;
     const int qg = tid >> 6;
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
+    for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = qg * 8 + i;
+      for (int i = 0; i < QPT; ++i) {
+        const int q = qg * QPT + i;
         const int c = q >> 2;
         const int j = q & 3;
         const int row = m0 + 4 * (lane >> 4) + j;  // D row of the 16x16 MFMA
-        const int colo = nb * 256 + ch * 128 + (lane & 15) * 8 + c;
+        const int colo = nb * NCOL + ch * 128 + (lane & 15) * 8 + c;
         if (row >= cnt || colo >= N || row_beg + row >= TK) continue;
         if (MODE == 1) {
           const float va = red[ch][q][lane];
-          const float vb = red[2 + ch][q][lane];
+          const float vb = red[NCH + ch][q][lane];
           hout[(int64_t)(row_beg + row) * N + colo] = f32_to_bf16_rne(silu_bf16out(va) * vb);
         } else {
           const float v = red[2 * ch][q][lane] + red[2 * ch + 1][q][lane];
@@ -204,16 +220,18 @@ __global__ __launch_bounds__(256, SKINNY_OCC) void skinny_kernel(
 hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                             const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
                             uint16_t* h, hipStream_t s) {
-  const int NB = (f + 255) / 256;
-  hipLaunchKernelGGL((skinny_kernel<1>), dim3((unsigned)(n * NB)), dim3(256), 0, s, x, perm_token,
+  constexpr int NCOL = SkinnyShape<1>::kCols;
+  const int NB = (f + NCOL - 1) / NCOL;
+  hipLaunchKernelGGL((skinny_kernel<1>), dim3((unsigned)(n * NB)), dim3(SkinnyShape<1>::kWaves * 64), 0, s, x, perm_token,
                      W1, W3, offsets, n, d, f, 1, (int)T, TK, h, (float*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_skinny_down(const uint16_t* h, const uint16_t* W2, const int* offsets, int64_t TK,
                               int n, int f, int d, int splits, float* o, hipStream_t s) {
-  const int NB = (d + 255) / 256;
-  hipLaunchKernelGGL((skinny_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(256), 0, s, h,
+  constexpr int NCOL = SkinnyShape<2>::kCols;
+  const int NB = (d + NCOL - 1) / NCOL;
+  hipLaunchKernelGGL((skinny_kernel<2>), dim3((unsigned)(n * NB * splits)), dim3(SkinnyShape<2>::kWaves * 64), 0, s, h,
                      (const int*)nullptr, W2, (const uint16_t*)nullptr, offsets, n, f, d, splits,
                      (int)TK, TK, (uint16_t*)nullptr, o);
   return hipGetLastError();
