@@ -60,6 +60,7 @@ def test_forward_tiny_fp32():
     (700, 256, 384, 8, 2),    # tiled path, one row tile per expert
     (4096, 128, 128, 64, 2),  # tiled path, many experts
     (40, 256, 320, 8, 2),     # weight-streaming path, column tail
+    (40, 128, 1152, 8, 2),    # weight-streaming path, 3 up-projection column blocks, the last one 128 wide
     (512, 128, 128, 64, 2),   # weight-streaming path, many experts
     (300, 128, 192, 4, 4),    # K = n: dense softmax mixture
     (300, 128, 192, 6, 1),    # K = 1
