@@ -40,11 +40,18 @@ Readings where the pages leave a step open (each also listed in the design notes
     C assignments in token order, dropped ones add nothing and the kept
     weights are not renormalised.
 
-Pins (tests/test_oracle_pins.py) tie every function to something other than
+Pins (tests/test_oracle_pins.py) tie each function to something other than
 itself: the walk-through's printed weights, brute force over all expert
 subsets, the K = n / K = 1 / n = K = 1 special cases, the parameter arithmetic
-printed in Part 4 of the explainer, closed forms of the sigmoid, and
-metamorphic invariants.  No function here is "parity unpinned".
+printed in Part 4 of the explainer, closed forms of the sigmoid, hand-worked
+rows for the top-K margins and for the expert-choice readings, and metamorphic
+invariants.  Two limits of those pins:
+  * expert_swiglu computes a reading (the pages name SwiGLU without defining
+    it and print no expert output); its pins fix that reading (explicit loops,
+    closed forms, the gate/up asymmetry), not a number from the pages;
+  * the expert-choice, capacity and 4-bit functions implement readings of
+    passages that give no worked numbers; their pins are hand-worked examples,
+    brute force and limits that reduce to the top-K layer.
 """
 from __future__ import annotations
 

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import config_inputs, log, sample_rows, upload
+from gpu_util import config_inputs, log, upload
 from parity import BF16_MAX_REL, BF16_MEAN_REL, assert_rows_close, check_routing
 from synth import make_inputs
 
@@ -123,10 +123,7 @@ def test_forward_capacity_skewed_full_size():
     y = y.cpu().numpy()
     del dev
     sub, ref, cap = _check_dispatch(inp, rc, cf)
-    rs = sample_rows(inp.T, 128)
-    # include some tokens that lost an assignment
-    lost = np.nonzero(~ref["kept"].all(axis=1))[0]
-    rs = np.unique(np.concatenate([rs, lost[:: max(1, lost.size // 32)]]))
+    rs = np.arange(inp.T)  # every row, including every token that lost an assignment
     yref = oracle.forward_kept(inp.f64("x")[rs], inp.f64("Wg"), lambda e: inp.expert_f64("W1", e),
                                lambda e: inp.expert_f64("W3", e), lambda e: inp.expert_f64("W2", e),
                                sub[rs], ref["kept"][rs])

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import config_inputs, log, sample_rows, upload
+from gpu_util import config_inputs, log, upload
 from parity import (BF16_MAX_REL, BF16_MEAN_REL, F32_MAX_REL, F32_MEAN_REL, assert_rows_close,
                     check_routing)
 from synth import bf16_bits_from_f32, bf16_bits_to_f32, make_inputs
@@ -150,9 +150,10 @@ def test_invalid_call_enqueues_nothing():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,rows", [("mixtral_decode", 32), ("mixtral_prefill", 128),
-                                       ("mixtral_skewed", 128), ("many_experts", 256)])
-def test_forward_full_configs(name, rows):
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "mixtral_skewed", "many_experts"])
+def test_forward_full_configs(name):
+    """Every row and every element of y at full size (the fp64 oracle needs a few
+    seconds per configuration on a many-core host)."""
     import torch
     moe = _moe()
     inp = config_inputs(name)
@@ -166,14 +167,12 @@ def test_forward_full_configs(name, rows):
     del dev
     r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
     sub = check_routing(r, rt, inp.K)
-    rs = sample_rows(inp.T, rows)
     ref = oracle.forward_with_selection(
-        inp.f64("x")[rs], inp.f64("Wg"),
+        inp.f64("x"), inp.f64("Wg"),
         lambda e: inp.expert_f64("W1", e), lambda e: inp.expert_f64("W3", e),
-        lambda e: inp.expert_f64("W2", e), sub[rs])
-    rel = assert_rows_close(y[rs], ref, BF16_MAX_REL, BF16_MEAN_REL)
-    assert np.isfinite(y).all()
-    log(f"  {name}: rows={len(rs)} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} "
+        lambda e: inp.expert_f64("W2", e), sub)
+    rel = assert_rows_close(y, ref, BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  {name}: rows={inp.T} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} "
         f"near-ties={(r['margin'] <= 1e-3).sum()}")
 
 

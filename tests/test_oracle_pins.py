@@ -628,3 +628,102 @@ def test_expert_choice_dispatch_layout():
         assert (np.diff(toks) > 0).all()
         np.testing.assert_array_equal(slot[toks, e], e * C + np.arange(C))
     assert ((slot >= 0) == chosen).all()
+
+
+# --------------------------------------- near-tie margins (acceptance rule)
+# The acceptance rule compares the top-K set exactly where the gap between the
+# K-th and (K+1)-th scores exceeds 1e-3, and the slot order exactly where every
+# gap between consecutive kept scores does (Part 3 of the explainer, step 2:
+# keep the highest scores, the larger listed first).  Hand-worked rows with
+# known gaps fix both margins.
+
+# scores 5, 1.0005, 1.0, 0.2 placed out of order: sorted order is e2, e3, e0, e1
+_MARGIN_ROW = np.array([[1.0, 0.2, 5.0, 1.0005]])
+
+
+@pytest.mark.parametrize("K,sel,margin,slot_margin", [
+    (1, [2], 5.0 - 1.0005, math.inf),
+    (2, [2, 3], 1.0005 - 1.0, 5.0 - 1.0005),
+    (3, [2, 3, 0], 1.0 - 0.2, 1.0005 - 1.0),
+    (4, [2, 3, 0, 1], math.inf, 1.0005 - 1.0),
+])
+def test_topk_margins_hand_worked(K, sel, margin, slot_margin):
+    s, m, sm = oracle.topk_select(_MARGIN_ROW, K)
+    assert list(s[0]) == sel
+    assert m[0] == margin            # exact: the same two fp64 subtractions
+    assert sm[0] == slot_margin
+
+
+def test_topk_margins_ties_and_rows():
+    # an exact tie at the K-th place gives margin 0; a tie inside the kept slots
+    # gives slot margin 0; rows are independent
+    L = np.array([[3.0, 1.0, 1.0, 0.0],      # K=2: 1.0 vs 1.0 tie at 2nd/3rd -> margin 0
+                  [2.0, 2.0, -1.0, -4.0],    # K=2: kept slots tie -> slot margin 0, margin 3
+                  [-1.0, -2.5, -0.5, -3.0]])
+    s, m, sm = oracle.topk_select(L, 2)
+    np.testing.assert_array_equal(s, [[0, 1], [0, 1], [2, 0]])
+    np.testing.assert_array_equal(m, [0.0, 3.0, 1.5])
+    np.testing.assert_array_equal(sm, [2.0, 0.0, 0.5])
+
+
+# ------------------------------- expert-choice readings, pinned by hand
+# "How Experts Are Chosen (Routing Methods)" names expert-based routing without
+# details; the readings (probability score, unnormalised weights, ceil in the
+# capacity) are pinned here against hand-computed values.
+
+def _two_token_router():
+    # x = the logits themselves (W_g = I): token 0 scores (3, 5), token 1 (1, -1)
+    x = np.array([[3.0, 5.0], [1.0, -1.0]])
+    return x, np.eye(2)
+
+
+def test_expert_choice_ranks_by_probability_not_logit():
+    # expert 0: token 0 has the larger logit (3 > 1) but the smaller probability
+    # (sigmoid(-2) = 0.119 < sigmoid(2) = 0.881), so with C = 1 expert 0 takes
+    # token 1; expert 1 takes token 0 either way
+    x, Wg = _two_token_router()
+    C = oracle.expert_choice_capacity(2, 2, 1.0)
+    assert C == 1
+    chosen, S, margin = oracle.expert_choice_select(oracle.router_logits(x, Wg), C)
+    np.testing.assert_array_equal(chosen, [[False, True], [True, False]])
+    sig2 = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(S, [[1 - sig2, sig2], [sig2, 1 - sig2]], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(margin, [2 * sig2 - 1, 2 * sig2 - 1], rtol=0, atol=1e-15)
+
+
+def test_expert_choice_weights_are_not_renormalised():
+    # each token is chosen by one expert only; its output is that expert's output
+    # times the router probability sigmoid(2) = 0.8808, not times 1
+    x, Wg = _two_token_router()
+    rng = np.random.default_rng(5)
+    W1, W3 = rng.standard_normal((2, 2, 3)), rng.standard_normal((2, 2, 3))
+    W2 = rng.standard_normal((2, 3, 2))
+    chosen = np.array([[False, True], [True, False]])
+    y = oracle.forward_expert_choice(x, Wg, W1, W3, W2, chosen)
+    sig2 = 1.0 / (1.0 + math.exp(-2.0))
+    e1_t0 = oracle.expert_swiglu(x[0:1], W1[1], W3[1], W2[1])[0]
+    e0_t1 = oracle.expert_swiglu(x[1:2], W1[0], W3[0], W2[0])[0]
+    np.testing.assert_allclose(y[0], sig2 * e1_t0, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(y[1], sig2 * e0_t1, rtol=1e-14, atol=0)
+    assert np.abs(y[0] - e1_t0).max() > 0.05 * np.abs(e1_t0).max()
+
+
+@pytest.mark.parametrize("T,n,cf,C", [
+    (10, 4, 1.0, 3),      # 2.5 -> 3 (floor would give 2)
+    (7, 3, 1.0, 3),       # 2.33 -> 3
+    (9, 4, 2.0, 5),       # 4.5 -> 5
+    (100, 8, 0.01, 1),    # 0.125 -> 1
+    (3, 2, 5.0, 3),       # 7.5 -> 8, at most T
+    (8192, 8, 2.0, 2048),
+])
+def test_expert_choice_capacity_rounds_up(T, n, cf, C):
+    assert oracle.expert_choice_capacity(T, n, cf) == C
+
+
+def test_expert_choice_capacity_ceil_changes_selection():
+    # T = 10, n = 4, cf = 1: each expert takes 3 tokens (not 2)
+    rng = np.random.default_rng(17)
+    logits = rng.standard_normal((10, 4))
+    C = oracle.expert_choice_capacity(10, 4, 1.0)
+    chosen, _, _ = oracle.expert_choice_select(logits, C)
+    np.testing.assert_array_equal(chosen.sum(axis=0), [3, 3, 3, 3])
