@@ -30,11 +30,16 @@
  *   - Limits: 1 <= K <= n <= 256, K <= 8, T*K < 2^31.  bf16 entry points need
  *     d % 64 == 0, f % 64 == 0 and 16-byte aligned tensors (MOE_ERR_UNSUPPORTED).
  *   - The library owns a per-device workspace (routing arrays, the
- *     intermediate h and o buffers and partial sums of split tiles, at most
- *     moe_workspace_bytes() bytes).  It is
- *     allocated on the first call on a device and grown on demand (the growing
- *     call synchronises the device); moe_release() frees it.  Calls that share
- *     a device's workspace must not run concurrently on different streams.
+ *     intermediate h and o buffers and partial sums of split tiles;
+ *     moe_workspace_bytes() gives what one call needs).  It is allocated on the
+ *     first call on a device and grown on demand, at least doubling; an
+ *     outgrown buffer is not freed but kept until moe_release(), so work
+ *     already enqueued and HIP graphs captured over earlier calls keep valid
+ *     addresses.  moe_release() frees every buffer: a graph captured over any
+ *     call must not be replayed after it.  Capture a call only after a call
+ *     of the same or a larger shape has run uncaptured (a growing call
+ *     allocates).  Calls that share a device's workspace must not run
+ *     concurrently on different streams.
  *   - Results are deterministic: no float atomics; every output element has a
  *     single writer and a fixed summation order.
  */

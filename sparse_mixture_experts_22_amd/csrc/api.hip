@@ -10,6 +10,7 @@
 // grouped GEMM and the weight-streaming kernels, made from the shape alone.
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include <algorithm>
 #include <cmath>
@@ -31,6 +32,9 @@ struct DeviceWorkspace {
   void* ptr = nullptr;
   size_t bytes = 0;
   int cus_per_xcd = 0;  // compute units per XCD, queried on first use
+  // Outgrown workspaces: a HIP graph captured over an earlier call still
+  // addresses them, so they stay allocated until moe_release.
+  std::vector<void*> retired;
 };
 std::mutex g_ws_mutex;
 DeviceWorkspace g_ws[kMaxDevices];
@@ -123,22 +127,19 @@ moe_status_t get_workspace(size_t bytes, char** out) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   DeviceWorkspace& ws = g_ws[dev];
   if (ws.bytes < bytes) {
-    if (ws.ptr != nullptr) {
-      e = hipDeviceSynchronize();  // earlier work may still use the old buffer
-      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-      e = hipFree(ws.ptr);
-      ws.ptr = nullptr;
-      ws.bytes = 0;
-      if (e != hipSuccess) return hip_fail(e, "hipFree");
-    }
+    // Grow at least 2x, so the outgrown buffers kept alive (retired) total
+    // less than the live one.  Nothing is freed here: work already enqueued,
+    // or a graph captured over an earlier call, may still use the old buffer.
+    const size_t want = std::max(bytes, 2 * ws.bytes);
     void* p = nullptr;
-    e = hipMalloc(&p, bytes);
+    e = hipMalloc(&p, want);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return fail(MOE_ERR_NO_MEMORY, std::string("hipMalloc of workspace failed: ") + hipGetErrorString(e));
     }
+    if (ws.ptr != nullptr) ws.retired.push_back(ws.ptr);
     ws.ptr = p;
-    ws.bytes = bytes;
+    ws.bytes = want;
   }
   *out = static_cast<char*>(ws.ptr);
   return MOE_OK;
@@ -491,6 +492,9 @@ moe_status_t moe_release(void) {
     if (ws.ptr == nullptr) continue;
     hipError_t e = hipSetDevice(dev);
     if (e == hipSuccess) e = hipDeviceSynchronize();
+    for (void* old : ws.retired)
+      if (e == hipSuccess) e = hipFree(old);
+    ws.retired.clear();
     if (e == hipSuccess) e = hipFree(ws.ptr);
     ws.ptr = nullptr;
     ws.bytes = 0;

@@ -58,3 +58,49 @@ def test_forward_graph_replays_match_eager(T, d, f, n, K):
         torch.cuda.synchronize()
         assert torch.equal(y_static, ref), f"replay {rep} differs"
     assert np.isfinite(y_static.cpu().numpy()).all()
+
+
+def test_graph_replays_after_the_workspace_grows():
+    # a graph captured over a small call keeps addressing the workspace it was
+    # captured with; a later, larger call grows the workspace, and the outgrown
+    # buffer must stay valid for the graph's replays (it is freed only by
+    # moe_release, which this test does not call)
+    import torch
+    moe = _moe()
+    T, d, f, n, K = 32, 256, 384, 8, 2
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=77)
+    dev = upload(inp)
+    w = (dev["Wg"], dev["W1"], dev["W3"], dev["W2"])
+    torch.cuda.synchronize()
+    moe.release()  # start from no workspace, so the calls below size it from small to large
+    x_static = dev["x"].clone()
+    y_static = torch.empty((T, d), dtype=torch.float32, device=x_static.device)
+    ref = moe.forward(dev["x"], *w, K).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(x_static, *w, K, y=y_static)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        moe.forward(x_static, *w, K, y=y_static)
+    # a much larger call: needs more workspace than any call since the release
+    Tb = 4 * 1024 * 1024 // (K * (2 * f + 4 * d)) * 64   # a few hundred MiB of intermediates
+    need = moe.workspace_bytes(Tb, d, f, n, K)
+    log(f"growth call: T={Tb} workspace {need / 2**20:.0f} MiB")
+    xb = torch.randn((Tb, d), device=x_static.device).to(torch.bfloat16)
+    yb = moe.forward(xb, *w, K)
+    torch.cuda.synchronize()
+    assert torch.isfinite(yb).all()
+    del yb, xb
+    torch.cuda.empty_cache()
+    # torch may now hand out memory; the graph must still use its own workspace
+    filler = torch.full((64 << 20,), 3.0, device=x_static.device)
+    for rep in range(3):
+        y_static.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static, ref), f"replay {rep} after growth differs"
+    del filler

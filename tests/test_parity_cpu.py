@@ -109,3 +109,17 @@ def test_fp32_bounds_are_tighter():
     assert_rows_close(got, ref, BF16_MAX_REL, BF16_MEAN_REL)
     with pytest.raises(AssertionError):
         assert_rows_close(got, ref, F32_MAX_REL, F32_MEAN_REL)
+
+
+def test_rows_below_fp32_range_are_compared_absolutely():
+    # a row whose only kept expert has a gate weight of e^-104 (about 7e-46, below
+    # fp32's range) is 0 on the GPU; that is fp32's resolution, not an error
+    ref = _rows(T=4, d=64)
+    ref[2] *= np.exp(-104.0)
+    got = ref.copy()
+    got[2] = 0.0
+    assert_rows_close(got, ref, BF16_MAX_REL, BF16_MEAN_REL)
+    # a row of ordinary size that comes back as zeros still fails
+    got[1] = 0.0
+    with pytest.raises(AssertionError):
+        assert_rows_close(got, ref, BF16_MAX_REL, BF16_MEAN_REL)
