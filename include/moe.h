@@ -92,6 +92,35 @@ moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, c
                                 int32_t K, float* y, moe_stream_t stream, void* const* stage_events);
 
 /*
+ * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, validation and routing; it calls no
+ * hipMalloc/hipFree and no allocating library routine.  Its intermediates live
+ * in a fixed scratch array of MOE_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.
+ *   - A shape whose intermediates exceed that size returns MOE_ERR_UNSUPPORTED
+ *     before anything is enqueued; moe_noalloc_scratch_bytes() gives the need
+ *     (Mixtral decode batches, T = 32, d = 4096, f = 14336, n = 8, K = 2, need
+ *     about 4 MiB; the weight-streaming path covers T*K <= 24*n).
+ *   - Weight-streaming shapes (T*K <= 24*n) give results bitwise equal to
+ *     moe_forward.  On the tiled path every down-projection tile runs whole
+ *     (moe_forward may split the last tiles over the reduction), so results
+ *     agree to fp32 summation order.
+ *   - Every call on a device shares that device's scratch, which keeps the last
+ *     call's contents (each call writes everything it reads, nothing needs to
+ *     start at zero).  Calls that overlap on one device race: serialise them
+ *     on one stream.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+moe_status_t moe_forward_noalloc(const void* x, const void* Wg, const void* W1, const void* W3,
+                                 const void* W2, int64_t T, int64_t d, int64_t f, int32_t n,
+                                 int32_t K, float* y, moe_stream_t stream);
+
+/* Scratch bytes moe_forward_noalloc needs for this shape (0 on invalid shapes). */
+size_t moe_noalloc_scratch_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K);
+
+/*
  * moe_forward_f32 -- the same layer with every input in fp32 (the hidden
  * activation stays fp32).  No alignment or divisibility requirement.
  */

@@ -12,7 +12,8 @@ _LIB = None
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP",
           4: "MOE_ERR_NO_MEMORY"}
 
-EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_f32", "moe_route", "moe_route_f32",
+EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
+           "moe_forward_f32", "moe_route", "moe_route_f32",
            "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
            "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4",
            "moe_expert_choice_capacity", "moe_route_expert_choice", "moe_forward_expert_choice",
@@ -52,6 +53,10 @@ def lib() -> ctypes.CDLL:
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
     L.moe_forward_traced.restype = ctypes.c_int
+    L.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    L.moe_forward_noalloc.restype = ctypes.c_int
+    L.moe_noalloc_scratch_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.moe_forward_f32.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
     L.moe_forward_f32.restype = ctypes.c_int
     L.moe_route.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -166,6 +171,23 @@ def forward_traced(x, Wg, W1, W3, W2, K, stage_events, y=None, stream=None):
     arr = (ctypes.c_void_p * 6)(*stage_events)
     return _forward(lib().moe_forward_traced, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream,
                     extra=(ctypes.cast(arr, ctypes.c_void_p),))
+
+
+def forward_noalloc(x, Wg, W1, W3, W2, K, y, stream=None):
+    """moe_forward_noalloc: as forward(), with the intermediates in the library's
+    fixed scratch (no device allocation by the library).  The caller passes y."""
+    import torch
+    if y is None:
+        raise ValueError("forward_noalloc needs a caller-allocated y")
+    return _forward(lib().moe_forward_noalloc, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream)
+
+
+def noalloc_scratch_bytes(T, d, f, n, K) -> int:
+    """moe_noalloc_scratch_bytes: scratch a moe_forward_noalloc call of this shape needs."""
+    return int(lib().moe_noalloc_scratch_bytes(T, d, f, n, K))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 def forward_f32(x, Wg, W1, W3, W2, K, y=None, stream=None):

@@ -35,9 +35,20 @@ struct DeviceWorkspace {
   // Outgrown workspaces: a HIP graph captured over an earlier call still
   // addresses them, so they stay allocated until moe_release.
   std::vector<void*> retired;
+  char* scratch = nullptr;  // this device's address of `scratch` (below)
 };
 std::mutex g_ws_mutex;
 DeviceWorkspace g_ws[kMaxDevices];
+
+}  // namespace
+
+// Fixed scratch of moe_forward_noalloc: one copy per device, held until the
+// process ends.  Host code never passes this name to a kernel (on the host it
+// is only a stand-in symbol): it takes the device address from
+// hipGetSymbolAddress once per device and passes that.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -145,6 +156,25 @@ moe_status_t get_workspace(size_t bytes, char** out) {
   return MOE_OK;
 }
 
+// Device address of the current device's fixed scratch, looked up once per
+// device (with that device current) and kept.
+moe_status_t get_scratch(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  DeviceWorkspace& ws = g_ws[dev];
+  if (ws.scratch == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    ws.scratch = static_cast<char*>(p);
+  }
+  *out = ws.scratch;
+  return MOE_OK;
+}
+
 // Compute units per XCD of the current device (the tile scheduler assumes 8
 // XCDs, the layout of the CDNA4 parts), queried once per device.
 moe_status_t cus_per_xcd(int* out) {
@@ -240,9 +270,11 @@ moe_status_t check_forward_ptrs(int64_t T, const void* x, const void* Wg, const 
 
 namespace {
 
+// `fixed`: run in the fixed scratch instead of the growable workspace (no
+// allocation; the tiled path then runs every down-projection tile whole).
 moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,
                           int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
-                          hipStream_t stream, void* const* ev, int cap = INT32_MAX) {
+                          hipStream_t stream, void* const* ev, int cap = INT32_MAX, bool fixed = false) {
   g_last_error.clear();
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
@@ -257,9 +289,17 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   int cus = 0;
   st = cus_per_xcd(&cus);
   if (st != MOE_OK) return st;
-  const Plan p = make_plan(T, d, f, n, K, Path::kBf16, cus);
+  const Plan p = make_plan(T, d, f, n, K, Path::kBf16, fixed ? 0 : cus);
   char* ws = nullptr;
-  st = get_workspace(p.total, &ws);
+  if (fixed) {
+    if (p.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_UNSUPPORTED, "this shape needs " + std::to_string(p.total) +
+                                           " bytes of scratch; the fixed scratch holds " +
+                                           std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES));
+    st = get_scratch(&ws);
+  } else {
+    st = get_workspace(p.total, &ws);
+  }
   if (st != MOE_OK) return st;
   auto mark = [&](int i) -> hipError_t {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream) : hipSuccess;
@@ -411,6 +451,19 @@ moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const vo
                          moe_stream_t stream) {
   return forward_bf16(x, Wg, W1, W3, W2, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream),
                       nullptr);
+}
+
+moe_status_t moe_forward_noalloc(const void* x, const void* Wg, const void* W1, const void* W3,
+                                 const void* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
+                                 float* y, moe_stream_t stream) {
+  return forward_bf16(x, Wg, W1, W3, W2, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream), nullptr,
+                      INT32_MAX, true);
+}
+
+size_t moe_noalloc_scratch_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K) {
+  if (T < 0 || d < 1 || f < 1 || n < 1 || n > moe::kMaxN || K < 1 || K > n || K > moe::kMaxK) return 0;
+  if (T * (int64_t)K > INT32_MAX || d > INT32_MAX || f > INT32_MAX) return 0;
+  return make_plan(T, d, f, n, K, Path::kBf16, 0).total;
 }
 
 moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, const void* W3,
