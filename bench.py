@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-One step = one call of moe_forward (router, top-K + softmax, dispatch, gate/up
-projection with SwiGLU, down projection, combine) on a resident batch.  The
-default workload is the Mixtral-shape prefill layer (T=8192, d=4096, f=14336,
-n=8, K=2, bf16); the decode batch (T=32) is measured in the same run and
-reported under "decode".  Inputs are seeded synthetic draws (synth/), weights
-random-init with the Mixtral layer's shapes.  Two weight copies alternate
-between steps so repeated reads cannot be served from the 256 MB last-level
-cache.
+One step = one call of the whole layer (router, top-K + softmax, dispatch,
+gate/up projection with SwiGLU, down projection, combine) on a resident batch.
+The headline is moe_forward_packed: the expert weights packed once into MFMA
+fragment order (moe_pack_up / moe_pack_down, outside the timed region, as a
+deployment does at weight-load time); moe_forward on the caller's layout is
+timed on the same inputs and reported under "caller_layout".  The default
+workload is the Mixtral-shape prefill layer (T=8192, d=4096, f=14336, n=8,
+K=2, bf16); the decode batch (T=32), the skewed-routing and the many-experts
+workloads are measured in the same run.  Inputs are seeded synthetic draws
+(synth/), weights random-init with the Mixtral layer's shapes.  Two weight
+copies alternate between steps so repeated reads cannot be served from the
+256 MB last-level cache.
 
 Per-kernel durations come from HIP events the library records between its
-stages on the launch stream (moe_forward_traced), over the timed steps.
-The CPU baseline times the fp64 oracle on a bounded sample of the workload.
+stages on the launch stream (moe_forward_traced / moe_forward_packed_traced),
+over the timed steps.  The CPU baseline times the fp64 oracle on a bounded
+sample of each workload.
 
 Prints one JSON line.
 """
@@ -41,6 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip timing the router statistics and the capacity-limited forward")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the skewed-routing and many-experts workloads")
+    ap.add_argument("--packed-only", action="store_true",
+                    help="time only moe_forward_packed (not moe_forward on the caller's layout)")
     ap.add_argument("--cpu-sample", type=int, default=8192, help="tokens in the oracle's timed sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device-to-device copy (reference for traffic counters)")
@@ -131,7 +140,49 @@ def time_extras(moe, x, wg, wsets, K, y, stream, reps):
     }
 
 
-def time_workload(name, steps, warmup, with_extras=False):
+def _stage_events(stream):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record(stream)  # creates the underlying hipEvent_t
+    return evs
+
+
+def _time_layer(step, traced_step, steps, warmup, stream):
+    """Mean ms per step over `steps` plain calls (two events around the loop), then
+    the same calls with the library's stage events (per-stage durations)."""
+    import numpy as np
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    events = [_stage_events(stream) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        traced_step(i, [e.cuda_event for e in events[i]])
+    torch.cuda.synchronize()
+    stage_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(5)] for ev in events])
+    traced_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
+    return dict(ms_per_step=total_ms / steps, wall_s=wall, stage_ms=stage_ms.mean(axis=0),
+                stage_ms_min=stage_ms.min(axis=0),
+                traced_step_ms={"median": round(float(np.median(traced_ms)), 4),
+                                "min": round(float(traced_ms.min()), 4), "max": round(float(traced_ms.max()), 4)})
+
+
+def time_workload(name, steps, warmup, with_extras=False, layouts=("packed", "caller")):
+    """One workload on resident inputs: moe_forward_packed on weights packed once
+    (moe_pack_up / moe_pack_down, outside the timed region) and moe_forward on the
+    caller's [n][d][f] / [n][f][d] layout.  Two weight copies alternate between steps."""
     import numpy as np
     import torch
 
@@ -148,89 +199,113 @@ def time_workload(name, steps, warmup, with_extras=False):
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    out = dict(name=name, T=T, d=d, f=f, n=n, K=K)
+    if "caller" in layouts:
+        def step(i):
+            w1, w3, w2 = wsets[i % 2]
+            moe.forward(x, wg, w1, w3, w2, K, y=y)
 
-    def make_events():
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        for e in evs:
-            e.record(stream)  # creates the underlying hipEvent_t
-        return evs
+        def traced(i, evs):
+            w1, w3, w2 = wsets[i % 2]
+            moe.forward_traced(x, wg, w1, w3, w2, K, evs, y=y)
 
-    for i in range(warmup):
-        w1, w3, w2 = wsets[i % 2]
-        moe.forward(x, wg, w1, w3, w2, K, y=y)
+        out["caller"] = _time_layer(step, traced, steps, warmup, stream)
+        assert torch.isfinite(y).all().item()
+        if with_extras:
+            out["extras"] = time_extras(moe, x, wg, wsets, K, y, stream, max(3, steps // 4))
+    if "packed" in layouts:
+        psets = [(moe.pack_up(w1, w3), moe.pack_down(w2)) for (w1, w3, w2) in wsets]
+        torch.cuda.synchronize()
+
+        def pstep(i):
+            p13, p2 = psets[i % 2]
+            moe.forward_packed(x, wg, p13, p2, f, K, y=y)
+
+        def ptraced(i, evs):
+            p13, p2 = psets[i % 2]
+            moe.forward_packed_traced(x, wg, p13, p2, f, K, evs, y=y)
+
+        out["packed"] = _time_layer(pstep, ptraced, steps, warmup, stream)
+        assert torch.isfinite(y).all().item()
+        del psets
+    rt = moe.route(x, wg, K, outputs=("counts", "topk_idx"))
     torch.cuda.synchronize()
-    # timed region 1: plain calls, two events around the whole loop
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        w1, w3, w2 = wsets[i % 2]
-        moe.forward(x, wg, w1, w3, w2, K, y=y)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    # timed region 2: the same calls with the library recording HIP events on
-    # its stream between stages (per-kernel durations; each event adds a few us)
-    events = [make_events() for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        w1, w3, w2 = wsets[i % 2]
-        moe.forward_traced(x, wg, w1, w3, w2, K, [e.cuda_event for e in events[i]], y=y)
-    torch.cuda.synchronize()
-    stage_ms = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(5)] for ev in events])
-    traced_ms = np.array([ev[0].elapsed_time(ev[5]) for ev in events])
-    rt = moe.route(x, wg, K, outputs=("counts",))
-    torch.cuda.synchronize()
-    counts = rt["counts"].cpu().numpy()
-    assert torch.isfinite(y).all().item()
-    extras = time_extras(moe, x, wg, wsets, K, y, stream, max(3, steps // 4)) if with_extras else None
-    return dict(name=name, T=T, d=d, f=f, n=n, K=K, ms_per_step=total_ms / steps, wall_s=wall,
-                stage_ms=stage_ms.mean(axis=0), stage_ms_min=stage_ms.min(axis=0), counts=counts,
-                traced_step_ms={"median": round(float(np.median(traced_ms)), 4),
-                                "min": round(float(traced_ms.min()), 4), "max": round(float(traced_ms.max()), 4)},
-                extras=extras)
+    out["counts"] = rt["counts"].cpu().numpy()
+    top1 = rt["topk_idx"][:, 0].cpu().numpy()
+    out["top1_share"] = np.bincount(top1, minlength=n) / float(T)
+    del x, wg, wsets, y
+    torch.cuda.empty_cache()
+    return out
 
 
-def prefill_record(r):
+def layer_flops(r):
+    return 2.0 * r["T"] * r["d"] * r["n"] + 6.0 * r["T"] * r["K"] * r["d"] * r["f"]
+
+
+def mfma_record(r, layout, kernel, traffic_kernel=None):
+    """Roofline of the up projection (the dominant kernel: 2/3 of the FLOPs) and
+    the layer and per-GEMM fractions of the bf16 MFMA peak for one layout."""
+    t = r[layout]
     T, d, f, n, K = r["T"], r["d"], r["f"], r["n"], r["K"]
     up_flops = 4.0 * T * K * d * f           # a = xW1 and b = xW3 on the T*K assignments
-    layer_flops = 2.0 * T * d * n + 6.0 * T * K * d * f
-    up_ms = float(r["stage_ms"][2])
+    down_flops = 2.0 * T * K * f * d
+    up_ms, down_ms = float(t["stage_ms"][2]), float(t["stage_ms"][3])
     achieved = up_flops / (up_ms * 1e-3) / 1e12
+    lt = layer_flops(r) / (t["ms_per_step"] * 1e-3) / 1e12
     return {
-        "roofline": {"kernel": "grouped_gemm_kernel<1> (gate/up projection + SwiGLU)", "bound": "mfma",
-                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("grouped_gemm_kernel<1>") if r["name"] == "mixtral_prefill" else None,
+        "roofline": {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(traffic_kernel) if traffic_kernel else None,
                      "flops_per_launch": up_flops, "avg_launch_ms": round(up_ms, 4)},
-        "layer_tflops": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12, 1),
-        "layer_frac_of_mfma_peak": round(layer_flops / (r["ms_per_step"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "tokens_per_s": round(T / (t["ms_per_step"] * 1e-3), 1),
+        "layer_tflops": round(lt, 1),
+        "layer_frac_of_mfma_peak": round(lt / PEAK_BF16_TFLOPS, 4),
+        "up_proj_frac_of_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "down_proj_frac_of_mfma_peak": round(down_flops / (down_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, t["stage_ms"])},
+        "traced_step_ms": t["traced_step_ms"],
     }
 
 
-def decode_record(r):
+def workload_record(r):
+    """Both layouts of a prefill-size workload, with the routing's per-expert loads."""
+    rec = {"workload": r["name"], "T": r["T"], "d": r["d"], "f": r["f"], "n": r["n"], "K": r["K"],
+           "flops_per_step": layer_flops(r)}
+    if "packed" in r:
+        rec["packed"] = mfma_record(r, "packed", "packed_gemm_kernel<1> (gate/up projection + SwiGLU)",
+                                    "packed_gemm_kernel<1>" if r["name"] == "mixtral_prefill" else None)
+    if "caller" in r:
+        rec["caller_layout"] = mfma_record(r, "caller", "grouped_gemm_kernel<1> (gate/up projection + SwiGLU)",
+                                           "grouped_gemm_kernel<1>" if r["name"] == "mixtral_prefill" else None)
+    rec["expert_counts"] = r["counts"].tolist()
+    rec["top1_share"] = [round(float(v), 4) for v in r["top1_share"]]
+    return rec
+
+
+def decode_record(r, layout):
+    t = r[layout]
     T, d, f, n, K = r["T"], r["d"], r["f"], r["n"], r["K"]
     touched = int((r["counts"] > 0).sum())
     up_bytes = touched * 2.0 * d * f * 2 + T * d * 2 + T * K * f * 2
     layer_bytes = touched * 3.0 * d * f * 2 + d * n * 2 + T * d * 2 + T * d * 4
-    up_ms = float(r["stage_ms"][2])
+    up_ms = float(t["stage_ms"][2])
     achieved = up_bytes / (up_ms * 1e-3) / 1e9
-    layer_gbs = layer_bytes / (r["ms_per_step"] * 1e-3) / 1e9
+    layer_gbs = layer_bytes / (t["ms_per_step"] * 1e-3) / 1e9
+    kernel = "skinny_kernel<1>" if layout == "caller" else "packed_stream_kernel<1>"
     return {
         "workload": "mixtral_decode", "T": T, "d": d, "f": f, "n": n, "K": K,
-        "value": round(T / (r["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
-        "ms_per_step": round(r["ms_per_step"], 4),
-        "roofline": {"kernel": "skinny_kernel<1> (gate/up projection + SwiGLU)", "bound": "hbm",
+        "value": round(T / (t["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "roofline": {"kernel": kernel + " (gate/up projection + SwiGLU)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("skinny_kernel<1>") if r["name"] == "mixtral_decode" else None,
+                     "traffic": measured_traffic(kernel) if r["name"] == "mixtral_decode" else None,
                      "bytes_per_launch": up_bytes, "avg_launch_ms": round(up_ms, 4)},
         "layer_gbs": round(layer_gbs, 1), "layer_frac_of_hbm_peak": round(layer_gbs / PEAK_HBM_GBS, 4),
         "experts_touched": touched,
-        "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, r["stage_ms"])},
-        "traced_step_ms": r["traced_step_ms"],
+        "stages_ms": {s: round(float(v), 4) for s, v in zip(STAGES, t["stage_ms"])},
+        "traced_step_ms": t["traced_step_ms"],
     }
 
 
@@ -285,38 +360,50 @@ def time_decode_q4(steps, warmup):
             "experts_touched": touched}
 
 
-def cpu_baseline(name, sample):
-    """The fp64 oracle as it stands, on the first `sample` tokens of the workload."""
+def cpu_baseline(names, sample):
+    """The fp64 oracle as it stands, per workload on its first `sample` tokens
+    (all of them where the workload is no larger), on this host's cores."""
     import numpy as np
 
     import oracle
     from synth import make_config_inputs
 
-    blas = "unknown"
+    blas, threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        pools = threadpool_info()
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
         threads = max([int(i.get("num_threads", 1)) for i in pools] or [1])
-        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools if i.get("user_api") == "blas")
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        pass
+    usable = len(os.sched_getaffinity(0))
     host_cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
             host_cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
     except (OSError, StopIteration):
         pass
-    inp = make_config_inputs(name)
-    x = inp.f64("x")[:sample]
-    t0 = time.perf_counter()
-    y = oracle.forward(x, inp.f64("Wg"), lambda e: inp.expert_f64("W1", e),
-                       lambda e: inp.expert_f64("W3", e), lambda e: inp.expert_f64("W2", e), inp.K)
-    el = time.perf_counter() - t0
-    assert np.isfinite(y).all()
-    return {"value": round(sample / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample} of the {inp.T} tokens of {name}: fp64 routing and every "
-                      f"touched expert (weights widened per expert), {el:.1f} s",
-            "host_cpu": host_cpu, "blas": blas}
+    per = {}
+    for name in names:
+        inp = make_config_inputs(name)
+        ns = min(sample, inp.T)
+        x = inp.f64("x")[:ns]
+        t0 = time.perf_counter()
+        y = oracle.forward(x, inp.f64("Wg"), lambda e: inp.expert_f64("W1", e),
+                           lambda e: inp.expert_f64("W3", e), lambda e: inp.expert_f64("W2", e), inp.K)
+        el = time.perf_counter() - t0
+        assert np.isfinite(y).all()
+        per[name] = {"tokens_per_s": round(ns / el, 2), "seconds": round(el, 2), "tokens": ns,
+                     "of_tokens": inp.T}
+        log(f"[bench] oracle {name}: {ns} tokens in {el:.1f}s")
+        del inp, x, y
+    head = names[0]
+    return {"value": per[head]["tokens_per_s"], "unit": "tokens/s", "cores": threads or usable, "kind": "oracle",
+            "sample": f"first {per[head]['tokens']} of the {per[head]['of_tokens']} tokens of {head}: fp64 routing "
+                      f"and every touched expert (weights widened per expert), {per[head]['seconds']} s",
+            "usable_cores": usable, "blas_threads": threads, "blas": blas,
+            "env": {k: os.environ.get(k) for k in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS")},
+            "host_cpu": host_cpu, "per_config": per}
 
 
 # ---------------------------------------------------------------- profiles
@@ -327,7 +414,9 @@ CALIB_BYTES = 1 << 30  # the --calibrate-copy copy: 1 GiB read, 1 GiB written
 # kernel's name without template arguments: every instance of a template shares them.
 _Q = ["csrc/moe_internal.h", "build.py"]
 KERNEL_SOURCES = {
-    "grouped_gemm_kernel": ["csrc/gemm_prefill.hip"] + _Q,
+    "grouped_gemm_kernel": ["csrc/gemm_prefill.hip", "csrc/tile_sched.h"] + _Q,
+    "packed_gemm_kernel": ["csrc/gemm_packed.hip", "csrc/tile_sched.h"] + _Q,
+    "packed_stream_kernel": ["csrc/gemm_packed.hip", "csrc/tile_sched.h"] + _Q,
     "skinny_kernel": ["csrc/gemm_skinny.hip"] + _Q,
     "skinny_q4_kernel": ["csrc/quant4.hip"] + _Q,
 }
@@ -472,8 +561,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU only; run with --gpus 1",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures one GPU only (every box here has one); "
+                                   "run with --gpus 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -490,43 +579,65 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    main_r = time_workload(args.workload, args.steps, args.warmup, with_extras=not args.no_extras)
-    log(f"[bench] {args.workload}: {main_r['ms_per_step']:.3f} ms/step, stages {main_r['stage_ms']}")
+    layouts = ("packed",) if args.packed_only else ("packed", "caller")
+    main_r = time_workload(args.workload, args.steps, args.warmup, with_extras=not args.no_extras, layouts=layouts)
+    log(f"[bench] {args.workload}: " + ", ".join(
+        f"{lay} {main_r[lay]['ms_per_step']:.3f} ms/step" for lay in layouts))
+    head = main_r["packed"]
     rec = {
         "metric": METRIC,
-        "value": round(main_r["T"] / (main_r["ms_per_step"] * 1e-3), 1),
+        "value": round(main_r["T"] / (head["ms_per_step"] * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "ms_per_step": round(head["ms_per_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic: seeded N(0,1) activations, random-init N(0,1/fan_in) weights",
         "config": {"workload": args.workload, "T": main_r["T"], "d": main_r["d"], "f": main_r["f"],
-                   "n": main_r["n"], "K": main_r["K"], "parallelism": "single GPU"},
+                   "n": main_r["n"], "K": main_r["K"], "parallelism": "single GPU",
+                   "weights": "bf16, packed once into MFMA fragment order (moe_pack_up / moe_pack_down) "
+                              "outside the timed region; each step is one moe_forward_packed call "
+                              "(routing included)"},
     }
     if args.workload == "mixtral_decode":
-        dr = decode_record(main_r)
+        dr = decode_record(main_r, "packed")
         rec["roofline"] = dr["roofline"]
+        rec["stages_ms"] = dr["stages_ms"]
+        if "caller" in main_r:
+            rec["caller_layout"] = decode_record(main_r, "caller")
     else:
-        pr = prefill_record(main_r)
-        rec["roofline"] = pr["roofline"]
-        rec["layer_tflops"] = pr["layer_tflops"]
-        rec["layer_frac_of_mfma_peak"] = pr["layer_frac_of_mfma_peak"]
-    rec["stages_ms"] = {s: round(float(v), 4) for s, v in zip(STAGES, main_r["stage_ms"])}
-    rec["traced_step_ms"] = main_r["traced_step_ms"]
-    if main_r["extras"] is not None:
+        wr = workload_record(main_r)
+        pk = wr["packed"]
+        rec["roofline"] = pk["roofline"]
+        for k in ("layer_tflops", "layer_frac_of_mfma_peak", "up_proj_frac_of_mfma_peak",
+                  "down_proj_frac_of_mfma_peak", "stages_ms", "traced_step_ms"):
+            rec[k] = pk[k]
+        if "caller_layout" in wr:
+            rec["caller_layout"] = wr["caller_layout"]
+        rec["expert_counts"] = wr["expert_counts"]
+    if "extras" in main_r:
         rec["extras"] = main_r["extras"]
-    rec["expert_counts"] = main_r["counts"].tolist()
     if not args.no_decode and args.workload != "mixtral_decode":
-        dr_raw = time_workload("mixtral_decode", max(args.steps, 20), args.warmup)
-        rec["decode"] = decode_record(dr_raw)
-        log(f"[bench] decode: {dr_raw['ms_per_step']:.3f} ms/step, stages {dr_raw['stage_ms']}")
+        dr_raw = time_workload("mixtral_decode", max(args.steps, 20), args.warmup, layouts=layouts)
+        rec["decode"] = decode_record(dr_raw, "packed")
+        if "caller" in dr_raw:
+            rec["decode_caller_layout"] = decode_record(dr_raw, "caller")
+        log("[bench] decode: " + ", ".join(f"{lay} {dr_raw[lay]['ms_per_step']:.3f} ms/step" for lay in layouts))
     if not args.no_decode and not args.no_extras:
         rec["decode_q4"] = time_decode_q4(max(args.steps, 20), args.warmup)
         log(f"[bench] decode (4-bit weights): {rec['decode_q4']['ms_per_step']:.3f} ms/step")
+    if not args.no_configs:
+        for key, name in (("skewed", "mixtral_skewed"), ("many_experts", "many_experts")):
+            if name == args.workload:
+                continue
+            r = time_workload(name, args.steps, args.warmup, layouts=layouts)
+            rec[key] = workload_record(r)
+            log(f"[bench] {name}: " + ", ".join(f"{lay} {r[lay]['ms_per_step']:.3f} ms/step" for lay in layouts))
     if not args.no_cpu_baseline:
-        log("[bench] timing the fp64 oracle on a sample ...")
-        rec["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample)
+        log("[bench] timing the fp64 oracle ...")
+        names = [args.workload] + [w for w in ("mixtral_decode", "mixtral_skewed", "many_experts")
+                                   if w != args.workload and not (args.no_configs and w != "mixtral_decode")]
+        rec["cpu_baseline"] = cpu_baseline(names, args.cpu_sample)
     print(json.dumps(rec), flush=True)
 
 

@@ -92,6 +92,42 @@ moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, c
                                 int32_t K, float* y, moe_stream_t stream, void* const* stage_events);
 
 /*
+ * Packed expert weights: the same bf16 values in the order the matrix cores
+ * consume them, written once (at weight-load time) and then read by
+ * moe_forward_packed on every call.  The layer is the one moe_forward computes
+ * (card 2.1 "Sparse Mixture of Experts" of the "Mixtral of Experts" study
+ * deck): only the storage order of W1, W3 and W2 differs.
+ * Format, for a stack with reduction index k and columns c:
+ *     P[e][pb][kk][j][l][i]   bf16, kk = k / 16, j = 0..1, l = 0..63, i = 0..7
+ *     holds W[e][16 kk + 8 (l / 32) + i][column of (pb, j, l % 32)]
+ *   up pair  (moe_pack_up, from W1 and W3 [n][d][f], 2*n*d*f values):
+ *            pb < f / 32; j = 0 takes W1, j = 1 takes W3, column 32 pb + l % 32
+ *   down     (moe_pack_down, from W2 [n][f][d], n*f*d values):
+ *            pb < d / 64; column 64 pb + 32 j + l % 32
+ * (one 1 KiB unit per (pb, kk, j) is one MFMA operand; a column pair's whole
+ * reduction is one contiguous stream).  Both need d % 256 == 0, f % 128 == 0,
+ * n <= 256 and 16-byte aligned tensors (MOE_ERR_UNSUPPORTED otherwise); the
+ * output buffers are caller-allocated, not overlapping the inputs.
+ *
+ * moe_forward_packed -- moe_forward on packed weights: x[T][d], Wg[d][n] bf16,
+ *   W13p from moe_pack_up, W2p from moe_pack_down, y[T][d] fp32.  Routing,
+ *   SwiGLU, bf16 rounding of h and the combine are those of moe_forward; the
+ *   expert projections multiply in the same order, so y equals moe_forward's
+ *   bit for bit on the tiled path except where the last tiles of the down
+ *   projection are split over the reduction (then to fp32 summation order).
+ * moe_forward_packed_traced -- the same with the six stage events of
+ *   moe_forward_traced.
+ */
+moe_status_t moe_pack_up(const void* W1, const void* W3, int32_t n, int64_t d, int64_t f, void* W13p,
+                         moe_stream_t stream);
+moe_status_t moe_pack_down(const void* W2, int32_t n, int64_t f, int64_t d, void* W2p, moe_stream_t stream);
+moe_status_t moe_forward_packed(const void* x, const void* Wg, const void* W13p, const void* W2p, int64_t T,
+                                int64_t d, int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream);
+moe_status_t moe_forward_packed_traced(const void* x, const void* Wg, const void* W13p, const void* W2p, int64_t T,
+                                       int64_t d, int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream,
+                                       void* const* stage_events);
+
+/*
  * moe_forward_noalloc -- moe_forward for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, validation and routing; it calls no

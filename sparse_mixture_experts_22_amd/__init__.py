@@ -17,6 +17,10 @@ from ._binding import (  # noqa: F401
     forward_f32,
     forward_traced,
     forward_noalloc,
+    forward_packed,
+    forward_packed_traced,
+    pack_down,
+    pack_up,
     noalloc_scratch_bytes,
     NOALLOC_SCRATCH_BYTES,
     last_error,
@@ -34,7 +38,8 @@ from ._binding import (  # noqa: F401
     workspace_bytes,
 )
 
-__all__ = ["forward", "forward_traced", "forward_noalloc", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
+__all__ = ["forward", "forward_traced", "forward_noalloc", "pack_up", "pack_down", "forward_packed",
+           "forward_packed_traced", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
            "expert_capacity", "route_capacity", "forward_capacity",
            "quantize_q4", "forward_q4", "expert_choice_capacity", "route_expert_choice",
            "forward_expert_choice", "workspace_bytes", "release",

@@ -13,6 +13,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "M
           4: "MOE_ERR_NO_MEMORY"}
 
 EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
+           "moe_pack_up", "moe_pack_down", "moe_forward_packed", "moe_forward_packed_traced",
            "moe_forward_f32", "moe_route", "moe_route_f32",
            "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
            "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4",
@@ -53,6 +54,14 @@ def lib() -> ctypes.CDLL:
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
     L.moe_forward_traced.restype = ctypes.c_int
+    L.moe_pack_up.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    L.moe_pack_up.restype = ctypes.c_int
+    L.moe_pack_down.argtypes = [vp, i32, i64, i64, vp, vp]
+    L.moe_pack_down.restype = ctypes.c_int
+    L.moe_forward_packed.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
+    L.moe_forward_packed.restype = ctypes.c_int
+    L.moe_forward_packed_traced.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
+    L.moe_forward_packed_traced.restype = ctypes.c_int
     L.moe_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp]
     L.moe_forward_noalloc.restype = ctypes.c_int
     L.moe_noalloc_scratch_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -180,6 +189,61 @@ def forward_noalloc(x, Wg, W1, W3, W2, K, y, stream=None):
     if y is None:
         raise ValueError("forward_noalloc needs a caller-allocated y")
     return _forward(lib().moe_forward_noalloc, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream)
+
+
+def pack_up(W1, W3, stream=None):
+    """moe_pack_up: W1, W3 bf16 [n][d][f] -> the packed up pair, bf16 [n][2*d*f]."""
+    import torch
+    _expect(W1, torch.bfloat16, "W1", 3)
+    _expect(W3, torch.bfloat16, "W3", 3)
+    if W1.shape != W3.shape:
+        raise ValueError("W1 and W3 must have the same shape")
+    n, d, f = W1.shape
+    out = torch.empty((n, 2 * d * f), dtype=torch.bfloat16, device=W1.device)
+    _check(lib().moe_pack_up(_ptr(W1), _ptr(W3), n, d, f, _ptr(out), _stream(stream)))
+    return out
+
+
+def pack_down(W2, stream=None):
+    """moe_pack_down: W2 bf16 [n][f][d] -> the packed down stack, bf16 [n][f*d]."""
+    import torch
+    _expect(W2, torch.bfloat16, "W2", 3)
+    n, f, d = W2.shape
+    out = torch.empty((n, f * d), dtype=torch.bfloat16, device=W2.device)
+    _check(lib().moe_pack_down(_ptr(W2), n, f, d, _ptr(out), _stream(stream)))
+    return out
+
+
+def _forward_packed(fn, x, Wg, W13p, W2p, f, K, y, stream, extra=()):
+    import torch
+    for t, name, nd in ((x, "x", 2), (Wg, "Wg", 2), (W13p, "W13p", 2), (W2p, "W2p", 2)):
+        _expect(t, torch.bfloat16, name, nd)
+    T, d = x.shape
+    n = Wg.shape[1]
+    if Wg.shape != (d, n) or W13p.shape != (n, 2 * d * f) or W2p.shape != (n, f * d):
+        raise ValueError("shapes must be x[T][d], Wg[d][n], W13p[n][2*d*f], W2p[n][f*d]")
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    else:
+        _expect(y, torch.float32, "y", 2)
+        if tuple(y.shape) != (T, d):
+            raise ValueError("y must be [T][d]")
+    _check(fn(_ptr(x), _ptr(Wg), _ptr(W13p), _ptr(W2p), T, d, int(f), n, int(K), _ptr(y), _stream(stream), *extra))
+    return y
+
+
+def forward_packed(x, Wg, W13p, W2p, f, K, y=None, stream=None):
+    """moe_forward_packed: the layer on weights from pack_up / pack_down (f = FFN size)."""
+    return _forward_packed(lib().moe_forward_packed, x, Wg, W13p, W2p, f, K, y, stream)
+
+
+def forward_packed_traced(x, Wg, W13p, W2p, f, K, stage_events, y=None, stream=None):
+    """moe_forward_packed_traced: forward_packed() recording six hipEvent_t handles between stages."""
+    if len(stage_events) != 6:
+        raise ValueError("need 6 events")
+    arr = (ctypes.c_void_p * 6)(*stage_events)
+    return _forward_packed(lib().moe_forward_packed_traced, x, Wg, W13p, W2p, f, K, y, stream,
+                           extra=(ctypes.cast(arr, ctypes.c_void_p),))
 
 
 def noalloc_scratch_bytes(T, d, f, n, K) -> int:

@@ -53,7 +53,7 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-enum class Path { kRouteOnly, kStats, kBf16, kF32 };
+enum class Path { kRouteOnly, kStats, kBf16, kPacked, kF32 };
 
 struct Plan {
   size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
@@ -87,9 +87,12 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
   p.perm_token = take((size_t)TK * 4);
   p.slot_pos = take((size_t)TK * 4);
   if (path == Path::kStats) p.probsum = take((size_t)nb * n * 4);
-  if (path == Path::kBf16) {
+  if (path == Path::kBf16 || path == Path::kPacked) {
     p.skinny = force_skinny || R <= (int64_t)moe::kSkinnyMaxAvgRows * n;
-    p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
+    if (path == Path::kPacked)  // cus_per_xcd == 0 (a size query): the largest split count
+      p.splits = p.skinny ? (cus_per_xcd > 0 ? moe::packed_stream_splits(n, (int)f, (int)d, cus_per_xcd) : 8) : 1;
+    else
+      p.splits = p.skinny ? moe::kSkinnyDownSplits : 1;
     p.h = take((size_t)R * f * 2);
     p.o = take((size_t)p.splits * R * d * 4);
     if (!p.skinny && cus_per_xcd >= 1 && cus_per_xcd <= 64) p.tail = take(moe::prefill_tail_bytes(cus_per_xcd));
@@ -272,16 +275,21 @@ namespace {
 
 // `fixed`: run in the fixed scratch instead of the growable workspace (no
 // allocation; the tiled path then runs every down-projection tile whole).
+// `packed`: W1 is the packed up pair (moe_pack_up), W3 is unused, W2 the packed
+// down stack (moe_pack_down).
 moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,
                           int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
-                          hipStream_t stream, void* const* ev, int cap = INT32_MAX, bool fixed = false) {
+                          hipStream_t stream, void* const* ev, int cap = INT32_MAX, bool fixed = false,
+                          bool packed = false) {
   g_last_error.clear();
   moe_status_t st = check_shape(T, d, f, n, K, true);
   if (st != MOE_OK) return st;
-  st = check_forward_ptrs(T, x, Wg, W1, W3, W2, y);
+  st = check_forward_ptrs(T, x, Wg, W1, packed ? W1 : W3, W2, y);
   if (st != MOE_OK) return st;
-  st = check_bf16(d, f, true, {x, Wg, W1, W3, W2, y});
+  st = check_bf16(d, f, true, {x, Wg, W1, packed ? W1 : W3, W2, y});
   if (st != MOE_OK) return st;
+  if (packed && (d % 256 != 0 || f % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need d % 256 == 0 and f % 128 == 0");
   if (ev != nullptr)
     for (int i = 0; i < 6; ++i)
       if (ev[i] == nullptr) return fail(MOE_ERR_INVALID_ARG, "stage_events must hold 6 events");
@@ -289,7 +297,8 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   int cus = 0;
   st = cus_per_xcd(&cus);
   if (st != MOE_OK) return st;
-  const Plan p = make_plan(T, d, f, n, K, Path::kBf16, fixed ? 0 : cus);
+  const Plan p = packed ? make_plan(T, d, f, n, K, Path::kPacked, cus)
+                        : make_plan(T, d, f, n, K, Path::kBf16, fixed ? 0 : cus);
   char* ws = nullptr;
   if (fixed) {
     if (p.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
@@ -318,7 +327,20 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   const auto* w1 = static_cast<const uint16_t*>(W1);
   const auto* w3 = static_cast<const uint16_t*>(W3);
   const auto* w2 = static_cast<const uint16_t*>(W2);
-  if (p.skinny) {
+  if (packed && p.skinny) {
+    MOE_LAUNCH(moe::launch_packed_stream_up(xb, T, r.perm_token, w1, r.offsets, TK, n, (int)d, (int)f, h, stream),
+               "up-projection kernel launch");
+    MOE_LAUNCH(mark(3), "hipEventRecord");
+    MOE_LAUNCH(moe::launch_packed_stream_down(h, w2, r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
+               "down-projection kernel launch");
+  } else if (packed) {
+    MOE_LAUNCH(moe::launch_packed_up(xb, T, r.perm_token, w1, r.offsets, TK, n, (int)d, (int)f, cus, h, stream),
+               "up-projection kernel launch");
+    MOE_LAUNCH(mark(3), "hipEventRecord");
+    float* tail = p.tail ? at<float>(ws, p.tail) : nullptr;
+    MOE_LAUNCH(moe::launch_packed_down(h, w2, r.offsets, TK, n, (int)f, (int)d, cus, tail, o, stream),
+               "down-projection kernel launch");
+  } else if (p.skinny) {
     MOE_LAUNCH(moe::launch_skinny_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, h, stream),
                "up-projection kernel launch");
     MOE_LAUNCH(mark(3), "hipEventRecord");
@@ -453,6 +475,52 @@ moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const vo
                       nullptr);
 }
 
+moe_status_t moe_pack_up(const void* W1, const void* W3, int32_t n, int64_t d, int64_t f, void* W13p,
+                         moe_stream_t stream) {
+  g_last_error.clear();
+  if (!W1 || !W3 || !W13p) return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  if (n < 1 || d < 1 || f < 1) return fail(MOE_ERR_INVALID_ARG, "n, d and f must be >= 1");
+  if (n > moe::kMaxN) return fail(MOE_ERR_UNSUPPORTED, "n > 256 experts is not supported");
+  if (d % 256 != 0 || f % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need d % 256 == 0 and f % 128 == 0");
+  if (d > INT32_MAX || f > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "d and f must be < 2^31");
+  if (!aligned16(W1) || !aligned16(W3) || !aligned16(W13p))
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need 16-byte aligned tensors");
+  MOE_LAUNCH(moe::launch_pack(1, static_cast<const uint16_t*>(W1), static_cast<const uint16_t*>(W3), n, (int)d,
+                              (int)f, static_cast<uint16_t*>(W13p), reinterpret_cast<hipStream_t>(stream)),
+             "pack kernel launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_down(const void* W2, int32_t n, int64_t f, int64_t d, void* W2p, moe_stream_t stream) {
+  g_last_error.clear();
+  if (!W2 || !W2p) return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  if (n < 1 || d < 1 || f < 1) return fail(MOE_ERR_INVALID_ARG, "n, d and f must be >= 1");
+  if (n > moe::kMaxN) return fail(MOE_ERR_UNSUPPORTED, "n > 256 experts is not supported");
+  if (d % 256 != 0 || f % 128 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "packed weights need d % 256 == 0 and f % 128 == 0");
+  if (d > INT32_MAX || f > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "d and f must be < 2^31");
+  if (!aligned16(W2) || !aligned16(W2p)) return fail(MOE_ERR_UNSUPPORTED, "packed weights need 16-byte aligned tensors");
+  MOE_LAUNCH(moe::launch_pack(2, static_cast<const uint16_t*>(W2), nullptr, n, (int)f, (int)d,
+                              static_cast<uint16_t*>(W2p), reinterpret_cast<hipStream_t>(stream)),
+             "pack kernel launch");
+  return MOE_OK;
+}
+
+moe_status_t moe_forward_packed(const void* x, const void* Wg, const void* W13p, const void* W2p, int64_t T,
+                                int64_t d, int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream) {
+  return forward_bf16(x, Wg, W13p, nullptr, W2p, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream), nullptr,
+                      INT32_MAX, false, true);
+}
+
+moe_status_t moe_forward_packed_traced(const void* x, const void* Wg, const void* W13p, const void* W2p, int64_t T,
+                                       int64_t d, int64_t f, int32_t n, int32_t K, float* y, moe_stream_t stream,
+                                       void* const* stage_events) {
+  if (stage_events == nullptr) return fail(MOE_ERR_INVALID_ARG, "stage_events must be non-null");
+  return forward_bf16(x, Wg, W13p, nullptr, W2p, T, d, f, n, K, y, reinterpret_cast<hipStream_t>(stream),
+                      stage_events, INT32_MAX, false, true);
+}
+
 moe_status_t moe_forward_noalloc(const void* x, const void* Wg, const void* W1, const void* W3,
                                  const void* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
                                  float* y, moe_stream_t stream) {
@@ -532,7 +600,9 @@ size_t moe_workspace_bytes(int64_t T, int64_t d, int64_t f, int32_t n, int32_t K
   const Plan a = make_plan(T, d, f, n, K, Path::kBf16, 64);
   const Plan b = make_plan(T, d, f, n, K, Path::kBf16, 0, true);
   const Plan c = make_plan(T, d, f, n, K, Path::kF32);
-  return std::max(a.total, std::max(b.total, c.total));
+  const Plan e = make_plan(T, d, f, n, K, Path::kPacked, 64);
+  const Plan g = make_plan(T, d, f, n, K, Path::kPacked, 0);
+  return std::max(std::max(a.total, std::max(b.total, c.total)), std::max(e.total, g.total));
 }
 
 moe_status_t moe_release(void) {

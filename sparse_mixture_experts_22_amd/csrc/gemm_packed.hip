@@ -1,0 +1,434 @@
+// Grouped expert GEMMs on weights stored in MFMA fragment order ("packed"),
+// bf16 MFMA on gfx950.
+//
+// The projections are those of the layer's SwiGLU experts (card 2.1 "Sparse
+// Mixture of Experts" of the "Mixtral of Experts" study deck; three d x f
+// matrices per expert, Part 4 of "Mixture of Experts: Why Mixtral Only Wakes
+// Up Two Specialists"):
+//   up   (MODE 1): h[p] = SiLU(x[perm_token[p]] W1_e) * (x[perm_token[p]] W3_e) -> bf16
+//   down (MODE 2): o[p] = h[p] W2_e -> fp32
+//
+// Packed format.  For v_mfma_f32_32x32x16_bf16, lane l of a B fragment holds
+// the 8 consecutive reduction indices k = 16 kk + 8 (l / 32) + i (i = 0..7) of
+// column l % 32.  A packed stack stores fragments contiguously:
+//     P[e][pb][kk][j][l][i]        (bf16; kk = k / 16, j = 0, 1, l = 0..63)
+// so one fragment is 1 KiB and the whole reduction of a column pair pb is one
+// contiguous stream of 2 KiB per kk.  Up projection (from W1, W3 [n][d][f]):
+// pair pb < f / 32 holds W1 columns 32 pb .. 32 pb + 31 (j = 0) and the same
+// W3 columns (j = 1).  Down projection (from W2 [n][f][d]): pair pb < d / 64
+// holds columns 64 pb + 32 j .. + 31.
+//
+// Kernel.  One 256-thread workgroup (one wave per SIMD) computes a 256-row
+// tile of one expert: 128 h columns (MODE 1; 128 of W1 and the matching 128 of
+// W3) or 256 output columns (MODE 2).  Wave w owns all 256 rows against pair
+// 4 nt + w: 8 row blocks x 2 fragments of 32x32 fp32 accumulators (256
+// registers, kept in AGPRs).  Its weight fragments come from the packed stream
+// straight into a ring of registers, PD k16-steps ahead, so the weights never
+// pass through LDS (half the LDS traffic of staging both operands).  The
+// gathered activation rows go through an LDS ring of PSA super-stages of 64 k
+// (256 rows x 128 bytes), filled by direct-to-LDS loads that each wave waits
+// for itself (s_waitcnt vmcnt, counted by issue order) before a barrier
+// publishes the super-stage; chunk c of row r sits at c ^ ((r >> 1) & 7), so
+// the 16 lanes of a 16-byte fragment read served together hit distinct banks.
+// Results equal the caller-layout kernels' bit for bit where no tile is split:
+// the same MFMA, the same fragment contents and the same k order.
+#include <algorithm>
+
+#include "moe_internal.h"
+#include "tile_sched.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int A_SUPER = BM * 64 * 2;  // 32 KiB: 256 rows x 64 k
+constexpr int PSA = 5;                // activation super-stages in LDS (160 KiB)
+constexpr int PR = 8;                 // register ring of weight k16-steps
+constexpr int PD = 7;                 // weight look-ahead in k16-steps
+static_assert(PD < PR, "a weight load must not target the slot in use");
+constexpr int kDS = 8;                // 1 KiB activation loads per wave per super-stage
+
+// Loads one wave issues, in order: the prologue (super-stages 0 .. PSA-2, kDS
+// loads each; piece 0 of super-stage PSA-1, kDS/4 loads; the weights of steps
+// 0 .. PD-1, 2 loads each), then per k16 step kk: kDS/4 loads of super-stage
+// (kk+1)/4 + PSA - 1 (piece (kk+1) % 4) followed by the 2 weight loads of step
+// kk + PD.  packed_after(st, kk) = loads issued after the last load of
+// super-stage `st` when step `kk` begins.
+constexpr int packed_after(int st, int kk) {
+  const int pro = (PSA - 1) * kDS + kDS / 4 + 2 * PD;
+  int last;
+  if (st <= PSA - 2) {
+    last = (st + 1) * kDS - 1;
+  } else {
+    const int kl = 4 * (st - PSA + 1) + 2;  // step that issues the last piece
+    last = pro + kl * (kDS / 4 + 2) + kDS / 4 - 1;
+  }
+  return pro + kk * (kDS / 4 + 2) - 1 - last;
+}
+// vmcnt bound that guarantees super-stage s+1 has landed at the barrier of
+// step 4s+3, for every s: the smallest count over the first super-stages
+// (prologue) and the steady state (reached by s = PSA - 1).
+constexpr int packed_wait_stage() {
+  int w = 63;
+  for (int s = 0; s < 3 * PSA; ++s) {
+    const int c = packed_after(s + 1, 4 * s + 3);
+    if (c < w) w = c;
+  }
+  return w;
+}
+constexpr int W_STAGE = packed_wait_stage();
+constexpr int W_FIRST = packed_after(0, 0);
+static_assert(W_STAGE >= 0 && W_STAGE <= 63 && W_FIRST <= 63, "vmcnt is a 6-bit counter");
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
+    const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
+    // not __restrict__: loads through a restrict pointer to read-only data may be
+    // moved across the asm statements whose issue order the waits count on
+    const uint16_t* Bp, const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK, int cus,
+    uint16_t* __restrict__ hout, float* __restrict__ oout, float* __restrict__ tail_ws) {
+  __shared__ __attribute__((aligned(1024))) char smem[PSA * A_SUPER];
+  constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
+  const int NT = N / NTW;
+  Tile tc;
+  // pieces of split tiles are whole unrolled loops: PR k16-steps = PR / 2 k-steps of 32
+  if (!decode_tile(offsets, n, NT, Kdim / BK, cus, MODE == 2 && tail_ws != nullptr, PR / 2, tc)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // activation loads: wave w fills blocks 8w .. 8w+7 of each super-stage (8 rows x 128 bytes each)
+  const uint16_t* ld_ptr[kDS];
+#pragma unroll
+  for (int b = 0; b < kDS; ++b) {
+    const int r = (wave * kDS + b) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
+    const int p = min(max(tc.row0 + rr, 0), TK - 1);
+    const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
+    ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
+  }
+  const uint32_t a_ld_base = (uint32_t)(uintptr_t)(lds_void*)smem + wave * (kDS * 1024);
+  // the wave's weight stream, from this workgroup's first k16-step
+  const int KK = Kdim / 16;
+  const int P = (MODE == 1) ? N / 32 : N / 64;
+  const int pb = tc.nt * 4 + wave;
+  const uint16_t* bptr = Bp + ((int64_t)(tc.e * P + pb) * KK + tc.k0 * 2) * 1024 + lane * 8;
+
+  const int nk16 = (tc.k1 - tc.k0) * 2;  // a multiple of PR
+  const int nss = nk16 / 4;
+  // Loads past the end re-load the last k-slice (into slots nobody reads
+  // again), so every wave issues the same sequence and the counts hold.
+  auto issue_a = [&](int stage, int b0, int nb) {
+    const uint32_t dst = a_ld_base + (stage % PSA) * A_SUPER;
+    const int64_t koff = (int64_t)(tc.k0 / 2 + min(stage, nss - 1)) * 64;
+#pragma unroll
+    for (int b = 0; b < nb; ++b) load_lds16(ld_ptr[b0 + b] + koff, dst + (b0 + b) * 1024);
+  };
+  auto load_b = [&](int kk, bf16x8_t (&dst)[2]) {
+    const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)min(kk, nk16 - 1) * 1024);
+    dst[0] = src[0];
+    dst[1] = src[64];
+  };
+
+  f32x16_t acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // fragment i of sub-step q (k 16 q .. +15 of a super-stage): row 32 i + l % 32, chunk 2 q + l / 32
+  const int m = lane & 31;
+  const int kg = lane >> 5;
+  int a_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a_off[q] = m * 128 + (((2 * q + kg) ^ ((m >> 1) & 7)) * 16);
+
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+#pragma unroll
+  for (int st = 0; st < PSA - 1; ++st) issue_a(st, 0, kDS);
+  issue_a(PSA - 1, 0, kDS / 4);
+  bf16x8_t br[PR][2];
+#pragma unroll
+  for (int t = 0; t < PD; ++t) load_b(t, br[t]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST, 15));  // super-stage 0 landed
+  fence();
+  __builtin_amdgcn_s_barrier();
+  fence();
+  bf16x8_t a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
+
+  // Step kk: 16 MFMAs on the fragments read during step kk-1; after each row
+  // block's two MFMAs, that block's fragment of step kk+1 is read.  After the
+  // first block come this step's activation loads (a quarter of a super-stage,
+  // into the slot the barrier of step 4s+3 released), after the fourth the
+  // weight loads of step kk + PD.  The last step of each super-stage starts
+  // with the barrier that publishes the next super-stage.
+  for (int base = 0; base < nk16; base += PR) {
+#pragma unroll
+    for (int u = 0; u < PR; ++u) {
+      const int kk = base + u;
+      if ((u & 3) == 3) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 0));  // own loads landed, own reads done
+        fence();
+        __builtin_amdgcn_s_barrier();
+        fence();
+      }
+      const int stn = (kk + 1) >> 2;  // super-stage of step kk+1
+      const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][1], acc[i][1], 0, 0, 0);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
+        if (i == 0) {
+          fence();
+          issue_a(stn + PSA - 1, ((u + 1) & 3) * (kDS / 4), kDS / 4);
+          fence();
+        }
+        if (i == 3) {
+          fence();
+          load_b(kk + PD, br[(u + PD) % PR]);
+          fence();
+        }
+      }
+      fence();  // the next step's fragment reads stay in this step
+    }
+  }
+  // the last (redundant) loads must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
+
+  // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  if (MODE == 1) {
+    // h tile (256 rows x 128 bf16 = 64 KiB) through LDS, stored 16 bytes per lane;
+    // chunk c of row r at c ^ (4 * ((r >> 2) & 1)) keeps the half-waves (rows r, r+4) apart
+    __syncthreads();  // every wave's LDS reads are done
+    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
+    const int cl = wave * 32 + m;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const int ch = (cl >> 3) ^ (4 * ((row >> 2) & 1));
+        hs[row * 128 + ch * 8 + (cl & 7)] = f32_to_bf16_rne(silu_bf16out(acc[i][0][r]) * acc[i][1][r]);
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = q * 256 + tid;  // chunk idx % 16 (8 columns) of row idx / 16
+      const int row = idx >> 4;
+      const int ch = idx & 15;
+      const int col = tc.nt * 128 + ch * 8;
+      if (row < tc.rows && tc.row0 + row < TK)
+        *reinterpret_cast<u32x4_t*>(hout + (int64_t)(tc.row0 + row) * N + col) =
+            *reinterpret_cast<const u32x4_t*>(hs + row * 128 + (ch ^ (4 * ((row >> 2) & 1))) * 8);
+    }
+  } else if (tc.slot >= 0) {
+    // a k-piece: the whole 256 x 256 partial tile goes to its slot
+    float* dst = tail_ws + (int64_t)tc.slot * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+          dst[row * BN + wave * 64 + j * 32 + m] = acc[i][j][r];
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = tc.nt * 256 + wave * 64 + j * 32 + m;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
+          if (row < tc.rows && tc.row0 + row < TK) oout[(int64_t)(tc.row0 + row) * N + c] = acc[i][j][r];
+        }
+      }
+  }
+}
+
+
+// Weight streaming on packed weights, for decode-sized batches (a few rows per
+// expert): every touched expert's packed stream is read once from HBM.  One
+// wave per (expert, pair[, k-split]): it walks the pair's stream 2 KiB per
+// k16-step with a ring of SPR steps of loads in flight, and multiplies a
+// 32-row pass of the expert's rows (gathered x rows, or h rows) with the two
+// fragments.  The activation fragments come straight from global memory (x
+// and h are small and stay in L2).  Every load here is an ordinary compiler-
+// tracked load, so the compiler's own waits are exact.  An expert with more
+// than 32 rows takes further passes over its weights; one with none returns
+// at once, so unselected experts are never read.
+//   MODE 1: h rows of the pass = SiLU(a) * b (the whole reduction per wave).
+//   MODE 2: o[split][row] = the split's partial sum over its k range.
+constexpr int SPR = 4;  // k16-steps of loads in flight per wave
+
+template <int MODE>
+__global__ __launch_bounds__(256) void packed_stream_kernel(
+    const uint16_t* __restrict__ A, const int* __restrict__ perm_token, const uint16_t* __restrict__ Bp,
+    const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK, int splits,
+    uint16_t* __restrict__ hout, float* __restrict__ oout) {
+  const int P = (MODE == 1) ? N / 32 : N / 64;
+  const int groups = P / 4;  // workgroups per expert and split
+  const int wg = blockIdx.x;
+  const int split = wg % splits;
+  const int g = (wg / splits) % groups;
+  const int e = wg / (splits * groups);
+  if (e >= n) return;
+  const int row_beg = offsets[e];
+  const int rows = offsets[e + 1] - row_beg;
+  if (rows <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pb = 4 * g + wave;
+  const int KK = Kdim / 16;
+  const int kb = (int)((int64_t)KK * split / splits);
+  const int ke = (int)((int64_t)KK * (split + 1) / splits);
+  const int nst = ke - kb;
+  const uint16_t* bptr = Bp + ((int64_t)(e * P + pb) * KK + kb) * 1024 + lane * 8;
+  const int m = lane & 31;
+  const int kg = lane >> 5;
+
+  for (int r0 = 0; r0 < rows; r0 += 32) {
+    // this lane's activation row (rows past the expert's last are computed, never stored)
+    const int p = row_beg + min(r0 + m, rows - 1);
+    const int arow = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
+    const uint16_t* aptr = A + (int64_t)arow * Kdim + (int64_t)kb * 16 + kg * 8;
+    f32x16_t acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    bf16x8_t ra[SPR], rb[SPR][2];
+    auto load = [&](int kk, int slot) {
+      const int k = min(kk, nst - 1);
+      ra[slot] = *reinterpret_cast<const bf16x8_t*>(aptr + (int64_t)k * 16);
+      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)k * 1024);
+      rb[slot][0] = src[0];
+      rb[slot][1] = src[64];
+    };
+#pragma unroll
+    for (int t = 0; t < SPR - 1; ++t) load(t, t);
+    for (int base = 0; base < nst; base += SPR) {
+#pragma unroll
+      for (int u = 0; u < SPR; ++u) {
+        load(base + u + SPR - 1, (u + SPR - 1) % SPR);
+        if (base + u < nst) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][0], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][1], acc[1], 0, 0, 0);
+        }
+      }
+    }
+    // 32x32 D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 8 * (r >> 2) + 4 * kg + (r & 3);
+      if (row >= rows) continue;
+      const int64_t prow = row_beg + row;
+      if (MODE == 1) {
+        hout[prow * N + 32 * pb + m] = f32_to_bf16_rne(silu_bf16out(acc[0][r]) * acc[1][r]);
+      } else {
+        float* dst = oout + ((int64_t)split * TK + prow) * N + 64 * pb + m;
+        dst[0] = acc[0][r];
+        dst[32] = acc[1][r];
+      }
+    }
+  }
+}
+
+// Repacks bf16 W[n][R][C] into the fragment order above (MODE 1: with the
+// matching W3 as fragment j = 1).  One thread per 16-byte fragment lane
+// out[e][pb][kk][j][l][0..7]; its 8 values are one column's 8 consecutive rows.
+template <int MODE>
+__global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, const uint16_t* __restrict__ W3,
+                                                   int n, int R, int C, uint16_t* __restrict__ out) {
+  const int P = (MODE == 1) ? C / 32 : C / 64;
+  const int KK = R / 16;
+  const int64_t total = (int64_t)n * P * KK * 2 * 64;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(g & 63);
+    const int j = (int)((g >> 6) & 1);
+    int64_t t = g >> 7;
+    const int kk = (int)(t % KK);
+    t /= KK;
+    const int pb = (int)(t % P);
+    const int e = (int)(t / P);
+    const uint16_t* src = (MODE == 1 && j == 1) ? W3 : W;
+    const int col = (MODE == 1) ? 32 * pb + (l & 31) : 64 * pb + 32 * j + (l & 31);
+    const uint16_t* s = src + ((int64_t)e * R + 16 * kk + 8 * (l >> 5)) * C + col;
+    u32x4_t w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)s[(int64_t)(2 * q) * C] | ((uint32_t)s[(int64_t)(2 * q + 1) * C] << 16);
+    *reinterpret_cast<u32x4_t*>(out + g * 8) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_packed_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
+                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, uint16_t* h,
+                            hipStream_t s) {
+  const int NT = f / 128;
+  hipLaunchKernelGGL((packed_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(256), 0, s, x,
+                     perm_token, W13p, offsets, n, d, f, (int)T, (int)TK, cus_per_xcd, h, (float*)nullptr,
+                     (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n, int f,
+                              int d, int cus_per_xcd, float* tail_ws, float* o, hipStream_t s) {
+  const int NT = d / 256;
+  hipLaunchKernelGGL((packed_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(256), 0, s, h,
+                     (const int*)nullptr, W2p, offsets, n, f, d, (int)TK, (int)TK, cus_per_xcd, (uint16_t*)nullptr,
+                     o, tail_ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || tail_ws == nullptr || cus_per_xcd < 2) return e;  // fewer CUs never split
+  return launch_tail_reduce(offsets, n, d, f / BK, cus_per_xcd, PR / 2, tail_ws, o, s);
+}
+
+
+int packed_stream_splits(int n, int f, int d, int cus) {
+  // enough (expert, pair, split) waves to fill every CU about 14-16 deep
+  const int waves = n * (d / 64);
+  const int want = (16 * 8 * cus + waves - 1) / waves;
+  return std::max(1, std::min(std::min(want, 8), f / 128));
+}
+
+hipError_t launch_packed_stream_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
+                                   const int* offsets, int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s) {
+  const int groups = (f / 32) / 4;
+  hipLaunchKernelGGL((packed_stream_kernel<1>), dim3(n * groups), dim3(256), 0, s, x, perm_token, W13p, offsets, n,
+                     d, f, (int)T, (int)TK, 1, h, (float*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_stream_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n,
+                                     int f, int d, int splits, float* o, hipStream_t s) {
+  const int groups = (d / 64) / 4;
+  hipLaunchKernelGGL((packed_stream_kernel<2>), dim3(n * groups * splits), dim3(256), 0, s, h, (const int*)nullptr,
+                     W2p, offsets, n, f, d, (int)TK, (int)TK, splits, (uint16_t*)nullptr, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, int R, int C, uint16_t* out,
+                       hipStream_t s) {
+  if (mode == 1)
+    hipLaunchKernelGGL((pack_kernel<1>), dim3(4096), dim3(256), 0, s, W, W3, n, R, C, out);
+  else
+    hipLaunchKernelGGL((pack_kernel<2>), dim3(4096), dim3(256), 0, s, W, W3, n, R, C, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

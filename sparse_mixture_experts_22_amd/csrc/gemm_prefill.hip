@@ -46,165 +46,13 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "tile_sched.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int BM = kPrefillBM;  // 256 rows
-constexpr int BN = 256;         // LDS B-tile columns
-constexpr int BK = 32;
-#ifndef MOE_NGROUP
-#define MOE_NGROUP 4
-#endif
-constexpr int NGROUP = MOE_NGROUP;  // column tiles per scheduling group
-
-constexpr int kXcds = 8;          // the hardware hands workgroup i to XCD (i mod 8)
-constexpr int kMaxTailSplit = 8;  // k-pieces per leftover tile
-
-struct Tile {
-  int e, m, nt, row0, rows;
-  int k0, k1;  // k-steps [k0, k1) of this workgroup's share of the tile
-  int slot;    // >= 0: a k-piece of a split tile, partial sums go to this slot
-};
-
-// Row tiles per expert, gathered by each wave in parallel: lane l holds
-// experts 4l .. 4l+3 (n <= 256), `pre` counts the row tiles of the experts
-// before 4l and `total` those of all experts.  Serial loops over the experts
-// here cost several microseconds per workgroup at n = 64, on the critical path
-// between one tile and the next on a CU.
-static_assert(kMaxN <= 256, "expert_tiles covers 4 experts per lane");
-struct ExpertTiles {
-  int mt[4];
-  int pre, total;
-};
-
-__device__ ExpertTiles expert_tiles(const int* __restrict__ offsets, int n) {
-  const int lane = threadIdx.x & 63;
-  ExpertTiles t;
-  int s = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = 4 * lane + j;
-    const int c = e < n ? offsets[e + 1] - offsets[e] : 0;
-    t.mt[j] = (c + BM - 1) / BM;
-    s += t.mt[j];
-  }
-  int incl = s;  // inclusive scan over the lanes
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  t.pre = incl - s;
-  t.total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-  return t;
-}
-
-// Position L of the tile list -> expert, row tile, column tile.  The list is
-// expert-major, then groups of NGROUP column tiles, then row tiles; expert e
-// owns positions [NT * P(e), NT * P(e+1)) with P the running sum of row tiles.
-__device__ bool tile_at(const int* __restrict__ offsets, const ExpertTiles& et, int NT, int L, Tile& tc) {
-  int hit = -1, base = 0, mt = 0;
-  int p = et.pre;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (et.mt[j] > 0 && L >= NT * p && L < NT * (p + et.mt[j])) {
-      hit = j;
-      base = p;
-      mt = et.mt[j];
-    }
-    p += et.mt[j];
-  }
-  const unsigned long long owner = __ballot(hit >= 0);  // at most one lane
-  if (owner == 0) return false;
-  const int src = __ffsll(owner) - 1;
-  const int e = __builtin_amdgcn_readfirstlane(4 * src + __shfl(hit, src));
-  mt = __builtin_amdgcn_readfirstlane(__shfl(mt, src));
-  L -= NT * __builtin_amdgcn_readfirstlane(__shfl(base, src));
-  const int ng = NT / NGROUP;
-  const int gsz = mt * NGROUP;
-  const int grp = L / gsz;
-  int m, nt;
-  if (grp < ng) {
-    const int rem = L - grp * gsz;
-    m = rem / NGROUP;
-    nt = grp * NGROUP + rem % NGROUP;
-  } else {
-    const int rem = L - ng * gsz;
-    const int gt = NT - ng * NGROUP;
-    m = rem / gt;
-    nt = ng * NGROUP + rem % gt;
-  }
-  tc.e = e;
-  tc.m = m;
-  tc.nt = nt;
-  tc.row0 = offsets[e] + m * BM;
-  const int left = offsets[e + 1] - tc.row0;
-  tc.rows = left < BM ? left : BM;
-  return true;
-}
-
-// Work of one XCD: the contiguous tiles [beg, beg + cnt) of the list.  `q`
-// tiles fill whole waves of the XCD's `cus` compute units; when the `r`
-// leftover tiles would leave more than half of the last wave idle (and the
-// kernel may split), each is cut into `s` k-pieces of `chunk` k-steps, so
-// the last wave is r * s <= cus shorter workgroups.
-struct XcdPlan {
-  int beg, cnt, q, r, s, chunk;
-};
-
-__device__ XcdPlan xcd_plan(int total, int x, int cus, int nk, bool may_split) {
-  XcdPlan t;
-  const int per = (total + kXcds - 1) / kXcds;
-  t.beg = x * per;
-  t.cnt = max(0, min(per, total - t.beg));
-  t.q = t.cnt / cus * cus;
-  t.r = t.cnt - t.q;
-  t.s = 1;
-  t.chunk = nk;
-  if (may_split && t.r > 0 && 2 * t.r <= cus) {
-    const int s0 = min(min(cus / t.r, kMaxTailSplit), nk / 2);
-    if (s0 >= 2) {
-      t.chunk = 2 * ((nk / 2 + s0 - 1) / s0);  // whole 64-k super-stages
-      t.s = (nk + t.chunk - 1) / t.chunk;
-    }
-  }
-  return t;
-}
-
-// Maps this workgroup to its tile (or k-piece of a tile); false if it has none.
-// Every wave computes the same answer from offsets[0..n].
-__device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int nk, int cus,
-                            bool may_split, Tile& tc) {
-  const ExpertTiles et = expert_tiles(offsets, n);
-  const int total = et.total * NT;
-  const int x = blockIdx.x % kXcds;
-  const int i = blockIdx.x / kXcds;
-  const XcdPlan t = xcd_plan(total, x, cus, nk, may_split);
-  tc.k0 = 0;
-  tc.k1 = nk;
-  tc.slot = -1;
-  int L;
-  if (t.s == 1) {
-    if (i >= t.cnt) return false;
-    L = t.beg + i;
-  } else if (i < t.q) {
-    L = t.beg + i;
-  } else {
-    const int u = i - t.q;
-    if (u >= t.r * t.s) return false;
-    L = t.beg + t.q + u % t.r;
-    const int piece = u / t.r;
-    tc.k0 = piece * t.chunk;
-    tc.k1 = min(nk, tc.k0 + t.chunk);
-    tc.slot = x * cus + u;
-  }
-  return tile_at(offsets, et, NT, L, tc);
-}
-
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
 // LDS rings.  The activation operand A moves in "super-stages" of 64 k
@@ -229,10 +77,6 @@ constexpr int B_LOADS = 4;  // 1 KiB loads per B-loader wave per stage
 // the main loop spreads a step's refill over the 4 row blocks of a burst:
 // one B load, or two A loads, per block
 static_assert(B_LOADS == 4 && A_LOADS == 8, "refill spread assumes 4 B and 8 A loads per wave");
-// s_waitcnt immediate: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-constexpr int waitcnt_imm(int vm, int lgkm) {
-  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
-}
 // Publishing k-step kt+1: the wave's own loads of the stage holding it must
 // have landed while the later stages may stay in flight, and its LDS reads of
 // step kt must have returned (the slot of step kt is refilled after the barrier).
@@ -242,15 +86,11 @@ constexpr int WAIT_LDS_ONLY = waitcnt_imm(63, 0);                 // kt+1 in the
 // before the loop every stage is in flight and the first one must have landed
 constexpr int WAIT_FIRST_B = waitcnt_imm(B_LOADS * (SB - 1), 15);
 constexpr int WAIT_FIRST_A = waitcnt_imm(A_LOADS * (SA - 1), 15);
-constexpr int WAITCNT_ALL = waitcnt_imm(0, 15);
 static_assert(B_LOADS * (SB - 1) < 64 && A_LOADS * (SA - 1) < 64, "vmcnt is a 6-bit counter");
 
 constexpr int A_SUPER = BM * 64 * 2;  // 32 KiB
 constexpr int B_STAGE = BK * BN * 2;  // 16 KiB
 
-__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds_addr) : "memory");
-}
 
 // A B fragment is two transposing LDS reads (k 0..3 and 4..7 of the lane's column).
 __device__ __forceinline__ i16x4_t read_b_half(const char* p) {
@@ -277,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
   const int NT = (N + NTW - 1) / NTW;
   Tile tc;
   // only the down projection (plain fp32 output) splits leftover tiles over k
-  if (!decode_tile(offsets, n, NT, Kdim / BK, cus, MODE == 2 && tail_ws != nullptr, tc)) return;
+  if (!decode_tile(offsets, n, NT, Kdim / BK, cus, MODE == 2 && tail_ws != nullptr, 2, tc)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -557,7 +397,8 @@ __global__ __launch_bounds__(512, 1) void grouped_gemm_kernel(
 // of XCD b / (16 * tmax) (tmax = cus / 2 bounds the leftover tiles of an XCD
 // that are split); it recomputes the XCD's plan exactly as the GEMM did.
 __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict__ offsets, int n, int N,
-                                                          int nk, int cus, const float* __restrict__ tail_ws,
+                                                          int nk, int cus, int gran,
+                                                          const float* __restrict__ tail_ws,
                                                           float* __restrict__ o) {
   const int NT = (N + 255) / 256;
   const int tmax = cus / 2;
@@ -565,7 +406,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict_
   const int t = (blockIdx.x / 16) % tmax;
   const int rblk = blockIdx.x % 16;
   const ExpertTiles et = expert_tiles(offsets, n);
-  const XcdPlan pl = xcd_plan(et.total * NT, x, cus, nk, true);
+  const XcdPlan pl = xcd_plan(et.total * NT, x, cus, nk, true, gran);
   if (pl.s == 1 || t >= pl.r) return;
   Tile tc;
   if (!tile_at(offsets, et, NT, pl.beg + pl.q + t, tc)) return;
@@ -601,13 +442,6 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const int* __restrict_
   }
 }
 
-// Grid: per XCD at most ceil(tiles / 8) tiles plus one extra wave of pieces.
-inline unsigned prefill_grid(int64_t TK, int n, int NT, int cus) {
-  const int64_t tiles_ub = ((TK + BM - 1) / BM + n) * (int64_t)NT;  // sum_e ceil(c_e/BM) bound
-  const int64_t per = (tiles_ub + kXcds - 1) / kXcds;
-  return (unsigned)((per + cus) * kXcds);
-}
-
 }  // namespace
 
 size_t prefill_tail_bytes(int cus_per_xcd) { return (size_t)kXcds * cus_per_xcd * BM * BN * sizeof(float); }
@@ -631,9 +465,14 @@ hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int*
                      (int)TK, cus_per_xcd, (uint16_t*)nullptr, o, tail_ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tail_ws == nullptr || cus_per_xcd < 2) return e;  // fewer CUs never split
+  return launch_tail_reduce(offsets, n, d, f / BK, cus_per_xcd, 2, tail_ws, o, s);
+}
+
+hipError_t launch_tail_reduce(const int* offsets, int n, int N, int nk, int cus_per_xcd, int gran,
+                              const float* tail_ws, float* o, hipStream_t s) {
   // split leftover tiles per XCD are at most cus / 2; 16 workgroups of 16 rows per tile
-  hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds * (cus_per_xcd / 2) * 16), dim3(256), 0, s, offsets, n, d,
-                     f / BK, cus_per_xcd, tail_ws, o);
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(kXcds * (cus_per_xcd / 2) * 16), dim3(256), 0, s, offsets, n, N,
+                     nk, cus_per_xcd, gran, tail_ws, o);
   return hipGetLastError();
 }
 

@@ -94,6 +94,28 @@ hipError_t launch_prefill_down(const uint16_t* h, const uint16_t* W2, const int*
                                int n, int f, int d, int cus_per_xcd, float* tail_ws, float* o,
                                hipStream_t s);
 size_t prefill_tail_bytes(int cus_per_xcd);
+// Sums the k-pieces of the split leftover tiles of a tiled down projection
+// (N output columns, nk k-steps of 32, pieces multiples of `gran` k-steps) into o.
+hipError_t launch_tail_reduce(const int* offsets, int n, int N, int nk, int cus_per_xcd, int gran,
+                              const float* tail_ws, float* o, hipStream_t s);
+// Packed weights (fragment order, see gemm_packed.hip): W13p from W1, W3
+// [n][d][f] (d % 128 == 0, f % 128 == 0); W2p from W2 [n][f][d] (f % 128 == 0,
+// d % 256 == 0).  mode 1 packs (W, W3) as the up pair, mode 2 packs W alone.
+hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, int R, int C, uint16_t* out,
+                       hipStream_t s);
+hipError_t launch_packed_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
+                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, uint16_t* h,
+                            hipStream_t s);
+hipError_t launch_packed_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n, int f,
+                              int d, int cus_per_xcd, float* tail_ws, float* o, hipStream_t s);
+// Weight streaming on packed weights (decode-sized batches): the up projection
+// streams each touched expert's pairs once; the down projection splits the
+// reduction over f into `splits` parts (o[split][p][:] partial sums).
+int packed_stream_splits(int n, int f, int d, int cus_per_xcd);
+hipError_t launch_packed_stream_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
+                                   const int* offsets, int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s);
+hipError_t launch_packed_stream_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n,
+                                     int f, int d, int splits, float* o, hipStream_t s);
 hipError_t launch_skinny_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W1,
                             const uint16_t* W3, const int* offsets, int64_t TK, int n, int d, int f,
                             uint16_t* h, hipStream_t s);

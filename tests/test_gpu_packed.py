@@ -1,0 +1,161 @@
+"""Packed expert weights (moe_pack_up / moe_pack_down / moe_forward_packed) on
+the GPU: the packed layout against its definition, the layer against the fp64
+oracle (every row, also at the full Mixtral-shape configurations) and against
+moe_forward on the caller's layout (same products, so fp32 summation order at
+most)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import config_inputs, log, upload
+from parity import BF16_MAX_REL, BF16_MEAN_REL, F32_MAX_REL, F32_MEAN_REL, assert_rows_close, check_routing
+from synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _moe():
+    import sparse_mixture_experts_22_amd as moe
+    return moe
+
+
+def _expected_pack(Ws, pair_cols):
+    """The packed order written out on the host from its definition:
+    P[e][pb][kk][j][l][i] = W_j'[e][16 kk + 8 (l // 32) + i][col(pb, j, l % 32)]."""
+    W0 = Ws[0]
+    n, R, C = W0.shape
+    P = C // pair_cols
+    out = np.empty((n, P, R // 16, 2, 64, 8), dtype=W0.dtype)
+    l = np.arange(64)
+    i = np.arange(8)
+    for j in range(2):
+        src = Ws[j] if len(Ws) == 2 else W0
+        for pb in range(P):
+            col = (32 * pb if len(Ws) == 2 else 64 * pb + 32 * j) + (l % 32)        # [64]
+            for kk in range(R // 16):
+                k = 16 * kk + 8 * (l // 32)[:, None] + i[None, :]                  # [64][8]
+                out[:, pb, kk, j] = src[:, k, col[:, None]]
+    return out.reshape(n, -1)
+
+
+def test_pack_layout_matches_definition():
+    import torch
+    moe = _moe()
+    inp = make_inputs(4, 256, 256, 3, 2, dtype="bf16", seed=61)
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    torch.cuda.synchronize()
+    got13 = p13.cpu().view(torch.int16).numpy().view(np.uint16)
+    got2 = p2.cpu().view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got13, _expected_pack((inp.W1, inp.W3), 32))
+    np.testing.assert_array_equal(got2, _expected_pack((inp.W2,), 64))
+
+
+def _run_both(inp):
+    import torch
+    moe = _moe()
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    yp = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, inp.K)
+    y = moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], inp.K)
+    rt = moe.route(dev["x"], dev["Wg"], inp.K)
+    torch.cuda.synchronize()
+    return yp.cpu().numpy(), y.cpu().numpy(), {k: v.cpu().numpy() for k, v in rt.items()}
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (2000, 256, 384, 4, 2),   # tiled: several row tiles per expert, ragged last tile
+    (700, 512, 256, 8, 2),    # tiled: one row tile per expert
+    (4096, 256, 128, 64, 2),  # tiled: many experts
+    (3000, 256, 128, 256, 8), # tiled: maximum n and K
+    (40, 256, 384, 8, 2),     # weight streaming
+    (96, 512, 640, 8, 2),     # weight streaming, up to 24 rows per expert on average
+    (300, 256, 128, 256, 8),  # weight streaming, maximum n and K
+    (1, 256, 128, 8, 2),      # single token
+    (300, 256, 256, 4, 4),    # K = n: dense softmax mixture
+])
+def test_forward_packed_shapes(T, d, f, n, K):
+    log(f"forward_packed: T={T} d={d} f={f} n={n} K={K}")
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=7100 + T + n)
+    yp, y, rt = _run_both(inp)
+    assert_rows_close(yp, y, F32_MAX_REL, F32_MEAN_REL, what="packed vs caller layout")
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), K)
+    sub = check_routing(r, rt, K)
+    ref = oracle.forward_with_selection(inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"), inp.f64("W2"),
+                                        sub)
+    rel = assert_rows_close(yp, ref, BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  max_rel={rel.max():.3e} mean_rel={rel.mean():.3e} bitwise_equal_to_forward={np.array_equal(yp, y)}")
+
+
+def test_forward_packed_is_deterministic_and_skips_unselected_experts():
+    import torch
+    from synth import bf16_bits_from_f32
+    moe = _moe()
+    inp = make_inputs(1500, 256, 256, 8, 2, dtype="bf16", seed=12)
+    one = bf16_bits_from_f32(np.array([1.0], dtype=np.float32))[0]
+    inp.x[:, 0] = one
+    col = np.zeros(8, dtype=np.float32)
+    col[4:] = -200.0
+    inp.Wg[0, :] = bf16_bits_from_f32(col)          # experts 4..7 never win
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    a = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, 2).clone()
+    b = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, 2).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    nan = torch.tensor([0x7FC0], dtype=torch.int16).view(torch.bfloat16).to(p13.device)
+    p13[4:] = nan                                      # the unselected experts' packed weights
+    p2[4:] = nan
+    c = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)
+
+
+def test_packed_invalid_shapes_and_empty_batch():
+    import torch
+    moe = _moe()
+    W = torch.zeros((2, 128, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoEError):
+        moe.pack_up(W, W)                               # d % 256 != 0
+    W = torch.zeros((2, 256, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoEError):
+        moe.pack_up(W, W)                               # f % 128 != 0
+    inp = make_inputs(4, 256, 128, 8, 2, dtype="bf16", seed=3)
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    y = moe.forward_packed(dev["x"][:0], dev["Wg"], p13, p2, 128, 2)
+    assert tuple(y.shape) == (0, 256)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral_decode", "mixtral_prefill", "mixtral_skewed", "many_experts"])
+def test_forward_packed_full_configs(name):
+    """Every row and element of y at full size, on packed weights."""
+    import torch
+    moe = _moe()
+    inp = config_inputs(name)
+    log(f"packed full config {name}: T={inp.T} d={inp.d} f={inp.f} n={inp.n} K={inp.K}")
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    del dev["W1"], dev["W3"], dev["W2"]
+    y = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, inp.K)
+    rt = moe.route(dev["x"], dev["Wg"], inp.K)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    rt = {k: v.cpu().numpy() for k, v in rt.items()}
+    del dev, p13, p2
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), inp.K)
+    sub = check_routing(r, rt, inp.K)
+    ref = oracle.forward_with_selection(
+        inp.f64("x"), inp.f64("Wg"),
+        lambda e: inp.expert_f64("W1", e), lambda e: inp.expert_f64("W3", e),
+        lambda e: inp.expert_f64("W2", e), sub)
+    rel = assert_rows_close(y, ref, BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  {name}: rows={inp.T} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
