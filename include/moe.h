@@ -98,14 +98,15 @@ moe_status_t moe_forward_traced(const void* x, const void* Wg, const void* W1, c
  * (card 2.1 "Sparse Mixture of Experts" of the "Mixtral of Experts" study
  * deck): only the storage order of W1, W3 and W2 differs.
  * Format, for a stack with reduction index k and columns c:
- *     P[e][pb][kk][j][l][i]   bf16, kk = k / 16, j = 0..1, l = 0..63, i = 0..7
- *     holds W[e][16 kk + 8 (l / 32) + i][column of (pb, j, l % 32)]
+ *     P[e][g][kk][w][j][l][i]  bf16, kk = k / 16, w = 0..3, j = 0..1, l = 0..63,
+ *     i = 0..7, holds W[e][16 kk + 8 (l / 32) + i][column of (pb, j, l % 32)]
+ *     with the column pair pb = 4 g + w
  *   up pair  (moe_pack_up, from W1 and W3 [n][d][f], 2*n*d*f values):
  *            pb < f / 32; j = 0 takes W1, j = 1 takes W3, column 32 pb + l % 32
  *   down     (moe_pack_down, from W2 [n][f][d], n*f*d values):
  *            pb < d / 64; column 64 pb + 32 j + l % 32
- * (one 1 KiB unit per (pb, kk, j) is one MFMA operand; a column pair's whole
- * reduction is one contiguous stream).  Both need d % 256 == 0, f % 128 == 0,
+ * (one 1 KiB unit per (pb, kk, j) is one MFMA operand; four adjacent pairs'
+ * whole reduction is one contiguous stream of 8 KiB per kk).  Both need d % 256 == 0, f % 128 == 0,
  * n <= 256 and 16-byte aligned tensors (MOE_ERR_UNSUPPORTED otherwise); the
  * output buffers are caller-allocated, not overlapping the inputs.
  *

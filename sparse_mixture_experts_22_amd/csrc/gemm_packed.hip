@@ -10,13 +10,14 @@
 //
 // Packed format.  For v_mfma_f32_32x32x16_bf16, lane l of a B fragment holds
 // the 8 consecutive reduction indices k = 16 kk + 8 (l / 32) + i (i = 0..7) of
-// column l % 32.  A packed stack stores fragments contiguously:
-//     P[e][pb][kk][j][l][i]        (bf16; kk = k / 16, j = 0, 1, l = 0..63)
-// so one fragment is 1 KiB and the whole reduction of a column pair pb is one
-// contiguous stream of 2 KiB per kk.  Up projection (from W1, W3 [n][d][f]):
-// pair pb < f / 32 holds W1 columns 32 pb .. 32 pb + 31 (j = 0) and the same
-// W3 columns (j = 1).  Down projection (from W2 [n][f][d]): pair pb < d / 64
-// holds columns 64 pb + 32 j .. + 31.
+// column l % 32.  A packed stack stores fragments contiguously, four column
+// pairs (one group, the columns of one tile) side by side:
+//     P[e][g][kk][w][j][l][i]      (bf16; kk = k / 16, w = 0..3, j = 0, 1, l = 0..63)
+// so one fragment is 1 KiB, pair pb = 4 g + w, and a group's whole reduction
+// is one contiguous stream of 8 KiB per kk.  Up projection (from W1, W3
+// [n][d][f]): pair pb < f / 32 holds W1 columns 32 pb .. 32 pb + 31 (j = 0)
+// and the same W3 columns (j = 1).  Down projection (from W2 [n][f][d]): pair
+// pb < d / 64 holds columns 64 pb + 32 j .. + 31.
 //
 // Kernel.  One 256-thread workgroup (one wave per SIMD) computes a 256-row
 // tile of one expert: 128 h columns (MODE 1; 128 of W1 and the matching 128 of
@@ -56,7 +57,7 @@ constexpr int kDS = 8;                // 1 KiB activation loads per wave per sup
 // super-stage `st` when step `kk` begins.
 constexpr int packed_after(int st, int kk) {
   const int pro = (PSA - 1) * kDS + kDS / 4 + 2 * PD;
-  int last;
+  int last = 0;
   if (st <= PSA - 2) {
     last = (st + 1) * kDS - 1;
   } else {
@@ -110,11 +111,10 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
   }
   const uint32_t a_ld_base = (uint32_t)(uintptr_t)(lds_void*)smem + wave * (kDS * 1024);
-  // the wave's weight stream, from this workgroup's first k16-step
+  // the wave's weight stream (pair 4 nt + wave of group nt), from this workgroup's first k16-step
   const int KK = Kdim / 16;
-  const int P = (MODE == 1) ? N / 32 : N / 64;
-  const int pb = tc.nt * 4 + wave;
-  const uint16_t* bptr = Bp + ((int64_t)(tc.e * P + pb) * KK + tc.k0 * 2) * 1024 + lane * 8;
+  const int G = (MODE == 1) ? N / 128 : N / 256;
+  const uint16_t* bptr = Bp + (((int64_t)(tc.e * G + tc.nt) * KK + tc.k0 * 2) * 4 + wave) * 1024 + lane * 8;
 
   const int nk16 = (tc.k1 - tc.k0) * 2;  // a multiple of PR
   const int nss = nk16 / 4;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     for (int b = 0; b < nb; ++b) load_lds16(ld_ptr[b0 + b] + koff, dst + (b0 + b) * 1024);
   };
   auto load_b = [&](int kk, bf16x8_t (&dst)[2]) {
-    const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)min(kk, nk16 - 1) * 1024);
+    const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)min(kk, nk16 - 1) * 4096);
     dst[0] = src[0];
     dst[1] = src[64];
   };
@@ -262,61 +262,71 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
 
 // Weight streaming on packed weights, for decode-sized batches (a few rows per
 // expert): every touched expert's packed stream is read once from HBM.  One
-// wave per (expert, pair[, k-split]): it walks the pair's stream 2 KiB per
-// k16-step with a ring of SPR steps of loads in flight, and multiplies a
-// 32-row pass of the expert's rows (gathered x rows, or h rows) with the two
-// fragments.  The activation fragments come straight from global memory (x
-// and h are small and stay in L2).  Every load here is an ordinary compiler-
-// tracked load, so the compiler's own waits are exact.  An expert with more
-// than 32 rows takes further passes over its weights; one with none returns
-// at once, so unselected experts are never read.
+// wave (one workgroup) per (expert, two adjacent column pairs[, k-split]): it
+// walks 4 KiB of weights per k16-step, SPR steps of loads in flight, and
+// multiplies a 32-row pass of the expert's rows (gathered x rows, or h rows)
+// with the four fragments.  The activation fragment comes straight from global
+// memory (x and h are small and stay in L2); two pairs per wave keep those
+// reads at a quarter of the weight bytes (one pair per wave made them half,
+// and the up projection ran 6% slower; four pairs per wave left too few waves
+// in flight).  Every load here is an ordinary compiler-tracked load, so the
+// compiler's own waits are exact.  An expert with more than 32 rows takes
+// further passes over its weights; one with none returns at once, so
+// unselected experts are never read.
 //   MODE 1: h rows of the pass = SiLU(a) * b (the whole reduction per wave).
 //   MODE 2: o[split][row] = the split's partial sum over its k range.
-constexpr int SPR = 4;  // k16-steps of loads in flight per wave
+constexpr int SPR = 5;  // k16-steps of loads in flight per wave
+constexpr int SQ = 2;  // column pairs per wave: 4 KiB of weights per 1 KiB activation fragment per k16-step
 
 template <int MODE>
-__global__ __launch_bounds__(256) void packed_stream_kernel(
+__global__ __launch_bounds__(64) void packed_stream_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token, const uint16_t* __restrict__ Bp,
     const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK, int splits,
     uint16_t* __restrict__ hout, float* __restrict__ oout) {
   const int P = (MODE == 1) ? N / 32 : N / 64;
-  const int groups = P / 4;  // workgroups per expert and split
+  const int units = P / SQ;  // waves per expert and split
   const int wg = blockIdx.x;
   const int split = wg % splits;
-  const int g = (wg / splits) % groups;
-  const int e = wg / (splits * groups);
+  const int u0 = (wg / splits) % units;
+  const int e = wg / (splits * units);
   if (e >= n) return;
   const int row_beg = offsets[e];
   const int rows = offsets[e + 1] - row_beg;
   if (rows <= 0) return;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pb = 4 * g + wave;
+  const int pb0 = u0 * SQ;          // first pair; pairs pb0 .. pb0 + SQ - 1 lie in group pb0 / 4
+  const int g = pb0 / 4;
+  const int w0 = pb0 % 4;
   const int KK = Kdim / 16;
   const int kb = (int)((int64_t)KK * split / splits);
   const int ke = (int)((int64_t)KK * (split + 1) / splits);
   const int nst = ke - kb;
-  const uint16_t* bptr = Bp + ((int64_t)(e * P + pb) * KK + kb) * 1024 + lane * 8;
+  const int G = P / 4;
+  const uint16_t* bptr = Bp + (((int64_t)(e * G + g) * KK + kb) * 4 + w0) * 1024 + lane * 8;
   const int m = lane & 31;
   const int kg = lane >> 5;
 
   for (int r0 = 0; r0 < rows; r0 += 32) {
-    // this lane's activation row (rows past the expert's last are computed, never stored)
     const int p = row_beg + min(r0 + m, rows - 1);
     const int arow = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
     const uint16_t* aptr = A + (int64_t)arow * Kdim + (int64_t)kb * 16 + kg * 8;
-    f32x16_t acc[2];
+    f32x16_t acc[SQ][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < SQ; ++q)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-    bf16x8_t ra[SPR], rb[SPR][2];
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][j][r] = 0.0f;
+    bf16x8_t ra[SPR], rb[SPR][SQ][2];
     auto load = [&](int kk, int slot) {
       const int k = min(kk, nst - 1);
       ra[slot] = *reinterpret_cast<const bf16x8_t*>(aptr + (int64_t)k * 16);
-      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)k * 1024);
-      rb[slot][0] = src[0];
-      rb[slot][1] = src[64];
+      const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)k * 4096);
+#pragma unroll
+      for (int q = 0; q < SQ; ++q) {
+        rb[slot][q][0] = src[q * 128];
+        rb[slot][q][1] = src[q * 128 + 64];
+      }
     };
 #pragma unroll
     for (int t = 0; t < SPR - 1; ++t) load(t, t);
@@ -325,23 +335,29 @@ __global__ __launch_bounds__(256) void packed_stream_kernel(
       for (int u = 0; u < SPR; ++u) {
         load(base + u + SPR - 1, (u + SPR - 1) % SPR);
         if (base + u < nst) {
-          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][0], acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][1], acc[1], 0, 0, 0);
+#pragma unroll
+          for (int q = 0; q < SQ; ++q) {
+            acc[q][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][q][0], acc[q][0], 0, 0, 0);
+            acc[q][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[u], rb[u][q][1], acc[q][1], 0, 0, 0);
+          }
         }
       }
     }
-    // 32x32 D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = r0 + 8 * (r >> 2) + 4 * kg + (r & 3);
       if (row >= rows) continue;
       const int64_t prow = row_beg + row;
-      if (MODE == 1) {
-        hout[prow * N + 32 * pb + m] = f32_to_bf16_rne(silu_bf16out(acc[0][r]) * acc[1][r]);
-      } else {
-        float* dst = oout + ((int64_t)split * TK + prow) * N + 64 * pb + m;
-        dst[0] = acc[0][r];
-        dst[32] = acc[1][r];
+#pragma unroll
+      for (int q = 0; q < SQ; ++q) {
+        const int pb = pb0 + q;
+        if (MODE == 1) {
+          hout[prow * N + 32 * pb + m] = f32_to_bf16_rne(silu_bf16out(acc[q][0][r]) * acc[q][1][r]);
+        } else {
+          float* dst = oout + ((int64_t)split * TK + prow) * N + 64 * pb + m;
+          dst[0] = acc[q][0][r];
+          dst[32] = acc[q][1][r];
+        }
       }
     }
   }
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(256) void packed_stream_kernel(
 
 // Repacks bf16 W[n][R][C] into the fragment order above (MODE 1: with the
 // matching W3 as fragment j = 1).  One thread per 16-byte fragment lane
-// out[e][pb][kk][j][l][0..7]; its 8 values are one column's 8 consecutive rows.
+// out[e][g][kk][w][j][l][0..7]; its 8 values are one column's 8 consecutive rows.
 template <int MODE>
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ W, const uint16_t* __restrict__ W3,
                                                    int n, int R, int C, uint16_t* __restrict__ out) {
@@ -360,11 +376,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
        g += (int64_t)gridDim.x * blockDim.x) {
     const int l = (int)(g & 63);
     const int j = (int)((g >> 6) & 1);
-    int64_t t = g >> 7;
+    const int wp = (int)((g >> 7) & 3);
+    int64_t t = g >> 9;
     const int kk = (int)(t % KK);
     t /= KK;
-    const int pb = (int)(t % P);
-    const int e = (int)(t / P);
+    const int grp = (int)(t % (P / 4));
+    const int e = (int)(t / (P / 4));
+    const int pb = 4 * grp + wp;
     const uint16_t* src = (MODE == 1 && j == 1) ? W3 : W;
     const int col = (MODE == 1) ? 32 * pb + (l & 31) : 64 * pb + 32 * j + (l & 31);
     const uint16_t* s = src + ((int64_t)e * R + 16 * kk + 8 * (l >> 5)) * C + col;
@@ -399,25 +417,26 @@ hipError_t launch_packed_down(const uint16_t* h, const uint16_t* W2p, const int*
 }
 
 
-int packed_stream_splits(int n, int f, int d, int cus) {
-  // enough (expert, pair, split) waves to fill every CU about 14-16 deep
-  const int waves = n * (d / 64);
-  const int want = (16 * 8 * cus + waves - 1) / waves;
+int packed_stream_splits(int n, int f, int d, int cus_per_xcd) {
+  // about 3 down-projection waves per compute unit (measured best at the
+  // Mixtral decode shape: 3 splits of f; 2 and 4 were slower)
+  const int waves = n * (d / 64) / SQ;
+  const int want = (3 * 8 * cus_per_xcd + waves / 2) / waves;
   return std::max(1, std::min(std::min(want, 8), f / 128));
 }
 
 hipError_t launch_packed_stream_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
                                    const int* offsets, int64_t TK, int n, int d, int f, uint16_t* h, hipStream_t s) {
-  const int groups = (f / 32) / 4;
-  hipLaunchKernelGGL((packed_stream_kernel<1>), dim3(n * groups), dim3(256), 0, s, x, perm_token, W13p, offsets, n,
-                     d, f, (int)T, (int)TK, 1, h, (float*)nullptr);
+  const int units = (f / 32) / SQ;
+  hipLaunchKernelGGL((packed_stream_kernel<1>), dim3(n * units), dim3(64), 0, s, x, perm_token, W13p, offsets, n, d,
+                     f, (int)T, (int)TK, 1, h, (float*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_packed_stream_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n,
                                      int f, int d, int splits, float* o, hipStream_t s) {
-  const int groups = (d / 64) / 4;
-  hipLaunchKernelGGL((packed_stream_kernel<2>), dim3(n * groups * splits), dim3(256), 0, s, h, (const int*)nullptr,
+  const int units = (d / 64) / SQ;
+  hipLaunchKernelGGL((packed_stream_kernel<2>), dim3(n * units * splits), dim3(64), 0, s, h, (const int*)nullptr,
                      W2p, offsets, n, f, d, (int)TK, (int)TK, splits, (uint16_t*)nullptr, o);
   return hipGetLastError();
 }

@@ -21,11 +21,11 @@ def _moe():
 
 def _expected_pack(Ws, pair_cols):
     """The packed order written out on the host from its definition:
-    P[e][pb][kk][j][l][i] = W_j'[e][16 kk + 8 (l // 32) + i][col(pb, j, l % 32)]."""
+    P[e][g][kk][w][j][l][i] = W_j'[e][16 kk + 8 (l // 32) + i][col(4 g + w, j, l % 32)]."""
     W0 = Ws[0]
     n, R, C = W0.shape
     P = C // pair_cols
-    out = np.empty((n, P, R // 16, 2, 64, 8), dtype=W0.dtype)
+    out = np.empty((n, P // 4, R // 16, 4, 2, 64, 8), dtype=W0.dtype)
     l = np.arange(64)
     i = np.arange(8)
     for j in range(2):
@@ -34,7 +34,7 @@ def _expected_pack(Ws, pair_cols):
             col = (32 * pb if len(Ws) == 2 else 64 * pb + 32 * j) + (l % 32)        # [64]
             for kk in range(R // 16):
                 k = 16 * kk + 8 * (l // 32)[:, None] + i[None, :]                  # [64][8]
-                out[:, pb, kk, j] = src[:, k, col[:, None]]
+                out[:, pb // 4, kk, pb % 4, j] = src[:, k, col[:, None]]
     return out.reshape(n, -1)
 
 
