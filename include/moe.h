@@ -58,7 +58,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1, /* null pointer, K < 1, K > n, n < 1, d/f < 1, T < 0 */
   MOE_ERR_UNSUPPORTED = 2, /* valid but outside this library's limits (see above) */
   MOE_ERR_HIP = 3,         /* a HIP call or kernel launch failed */
-  MOE_ERR_NO_MEMORY = 4    /* workspace allocation failed */
+  MOE_ERR_NO_MEMORY = 4,   /* workspace allocation failed */
+  MOE_ERR_VALIDATION = 5   /* a dispatch check failed (moe_check_dispatch, MOE_VALIDATE=1) */
 } moe_status_t;
 
 /* Opaque HIP stream handle (hipStream_t). */
@@ -311,6 +312,27 @@ moe_status_t moe_forward_q4(const void* x, const void* Wg, const void* W1q, cons
                             const void* W3q, const void* W3s, const void* W2q, const void* W2s,
                             int64_t T, int64_t d, int64_t f, int32_t n, int32_t K, float* y,
                             moe_stream_t stream);
+
+/*
+ * moe_check_dispatch -- checks routing arrays on the device against the
+ * definition of the dispatch (moe_route above): counts[e] = offsets[e+1] -
+ * offsets[e] <= capacity, offsets[0] = 0, offsets[n] = T*K without a capacity;
+ * every expert index in [0, n) and distinct within its token; every kept
+ * assignment (t, k) at a position slot_pos[t][k] inside its expert's segment
+ * with perm_token[slot_pos[t][k]] = t; every position owned by exactly such an
+ * assignment; tokens ascending within each segment.  capacity = 0: dropless
+ * (slot_pos = -1 is then an error); capacity > 0: moe_route_capacity's arrays,
+ * where -1 marks a dropped assignment.  All arrays are device int32 in the
+ * layouts of moe_route.  The call waits for the verdict on `stream` (it
+ * synchronises that stream): MOE_OK, or MOE_ERR_VALIDATION with the failed
+ * properties and the first offending index in moe_last_error().
+ * With MOE_VALIDATE=1 in the environment, moe_route, moe_route_capacity and
+ * every bf16 forward entry point run the same check after routing (and so
+ * synchronise their stream; not for use under graph capture).
+ */
+moe_status_t moe_check_dispatch(const int32_t* topk_idx, const int32_t* counts, const int32_t* offsets,
+                                const int32_t* perm_token, const int32_t* slot_pos, int64_t T, int32_t n, int32_t K,
+                                int64_t capacity, moe_stream_t stream);
 
 /* Bytes of library workspace a call of this shape needs on any supported
  * device, for every entry point that takes (T, d, f, n, K) (an upper bound:

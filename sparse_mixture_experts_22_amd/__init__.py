@@ -8,6 +8,7 @@ built, every call raises; there is no CPU fallback.
 from ._binding import (  # noqa: F401
     MoEError,
     STATUS,
+    check_dispatch,
     expert_capacity,
     expert_choice_capacity,
     forward,
@@ -40,7 +41,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["forward", "forward_traced", "forward_noalloc", "pack_up", "pack_down", "forward_packed",
            "forward_packed_traced", "noalloc_scratch_bytes", "NOALLOC_SCRATCH_BYTES", "forward_f32", "route", "route_f32", "route_stats", "route_stats_f32",
-           "expert_capacity", "route_capacity", "forward_capacity",
+           "expert_capacity", "route_capacity", "forward_capacity", "check_dispatch",
            "quantize_q4", "forward_q4", "expert_choice_capacity", "route_expert_choice",
            "forward_expert_choice", "workspace_bytes", "release",
            "last_error", "version", "lib", "lib_path", "MoEError", "STATUS"]

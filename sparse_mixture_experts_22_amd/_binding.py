@@ -10,7 +10,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED", 3: "MOE_ERR_HIP",
-          4: "MOE_ERR_NO_MEMORY"}
+          4: "MOE_ERR_NO_MEMORY", 5: "MOE_ERR_VALIDATION"}
 
 EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_noalloc", "moe_noalloc_scratch_bytes",
            "moe_pack_up", "moe_pack_down", "moe_forward_packed", "moe_forward_packed_traced",
@@ -18,7 +18,7 @@ EXPORTS = ["moe_forward", "moe_forward_traced", "moe_forward_noalloc", "moe_noal
            "moe_route_stats", "moe_route_stats_f32", "moe_expert_capacity", "moe_route_capacity",
            "moe_forward_capacity", "moe_quantize_q4", "moe_forward_q4",
            "moe_expert_choice_capacity", "moe_route_expert_choice", "moe_forward_expert_choice",
-           "moe_workspace_bytes",
+           "moe_check_dispatch", "moe_workspace_bytes",
            "moe_release", "moe_status_string", "moe_last_error", "moe_version"]
 
 
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.moe_forward.restype = ctypes.c_int
     L.moe_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp]
     L.moe_forward_traced.restype = ctypes.c_int
+    L.moe_check_dispatch.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, vp]
+    L.moe_check_dispatch.restype = ctypes.c_int
     L.moe_pack_up.argtypes = [vp, vp, i32, i64, i64, vp, vp]
     L.moe_pack_up.restype = ctypes.c_int
     L.moe_pack_down.argtypes = [vp, i32, i64, i64, vp, vp]
@@ -189,6 +191,15 @@ def forward_noalloc(x, Wg, W1, W3, W2, K, y, stream=None):
     if y is None:
         raise ValueError("forward_noalloc needs a caller-allocated y")
     return _forward(lib().moe_forward_noalloc, torch.bfloat16, x, Wg, W1, W3, W2, K, y, stream)
+
+
+def check_dispatch(routing, T, n, K, capacity=0, stream=None):
+    """moe_check_dispatch on a dict with the moe_route arrays (topk_idx, counts,
+    offsets, perm_token, slot_pos; device int32).  Raises MoEError on a violation."""
+    r = routing
+    _check(lib().moe_check_dispatch(_ptr(r["topk_idx"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+                                    _ptr(r["perm_token"]), _ptr(r["slot_pos"]), T, n, K, int(capacity),
+                                    _stream(stream)))
 
 
 def pack_up(W1, W3, stream=None):

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["route.hip", "gemm_prefill.hip", "gemm_packed.hip", "gemm_skinny.hip", "quant4.hip", "misc.hip",
-           "api.hip"]
+           "validate.hip", "api.hip"]
 ARCH = "gfx950"
 
 

@@ -14,6 +14,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <utility>
 
 #include "moe.h"
 #include "moe_internal.h"
@@ -58,7 +60,7 @@ enum class Path { kRouteOnly, kStats, kBf16, kPacked, kF32 };
 struct Plan {
   size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
          perm_token = 0, slot_pos = 0;
-  size_t h = 0, o = 0, tail = 0, probsum = 0, total = 0;
+  size_t h = 0, o = 0, tail = 0, probsum = 0, verr = 0, total = 0;
   bool skinny = false;
   int splits = 1;
 };
@@ -86,6 +88,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
   p.offsets = take((size_t)(n + 1) * 4);
   p.perm_token = take((size_t)TK * 4);
   p.slot_pos = take((size_t)TK * 4);
+  p.verr = take(8);
   if (path == Path::kStats) p.probsum = take((size_t)nb * n * 4);
   if (path == Path::kBf16 || path == Path::kPacked) {
     p.skinny = force_skinny || R <= (int64_t)moe::kSkinnyMaxAvgRows * n;
@@ -130,6 +133,32 @@ moe_status_t check_bf16(int64_t d, int64_t f, bool need_f, std::initializer_list
 
 moe_status_t hip_fail(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// MOE_VALIDATE=1 in the environment: every routing is followed by the
+// dispatch checks on the device, and the call waits for their verdict.
+bool validate_enabled() {
+  const char* v = std::getenv("MOE_VALIDATE");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+moe_status_t validation_verdict(const int* topk_idx, const int* counts, const int* offsets, const int* perm_token,
+                                const int* slot_pos, int64_t T, int n, int K, int cap, int* err, hipStream_t stream) {
+  hipError_t e = moe::launch_validate(topk_idx, counts, offsets, perm_token, slot_pos, T, n, K, cap, err, stream);
+  if (e != hipSuccess) return hip_fail(e, "validation kernel launch");
+  int host[2] = {0, 0};
+  e = hipMemcpyAsync(host, err, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "validation read-back");
+  if (host[0] == 0) return MOE_OK;
+  std::string what;
+  const std::pair<int, const char*> names[] = {
+      {moe::kValidateOffsets, "counts/offsets"}, {moe::kValidateTotal, "total assignments"},
+      {moe::kValidateIndex, "expert index"}, {moe::kValidateSlot, "slot_pos segment"},
+      {moe::kValidatePerm, "perm_token/slot_pos back-pointer"}, {moe::kValidateOrder, "token order in a segment"}};
+  for (const auto& nm : names)
+    if (host[0] & nm.first) what += std::string(what.empty() ? "" : ", ") + nm.second;
+  return fail(MOE_ERR_VALIDATION, "dispatch check failed (" + what + "), first at index " + std::to_string(host[1]));
 }
 
 // Returns the current device's workspace, grown to at least `bytes`.
@@ -258,6 +287,9 @@ moe_status_t route_impl(const void* x, const void* Wg, int64_t T, int64_t d, int
     MOE_LAUNCH(moe::launch_route_f32(static_cast<const float*>(x), static_cast<const float*>(Wg), T, d, n,
                                      K, r, stream),
                "routing kernel launch");
+  if (validate_enabled())
+    return validation_verdict(r.topk_idx, r.counts, r.offsets, r.perm_token, r.slot_pos, T, n, K, cap,
+                              at<int>(ws, p.verr), stream);
   return MOE_OK;
 }
 
@@ -323,6 +355,11 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   MOE_LAUNCH(moe::launch_route_bf16(xb, static_cast<const uint16_t*>(Wg), T, d, n, K, r, stream,
                                     ev ? static_cast<hipEvent_t>(ev[1]) : nullptr, cap),
              "routing kernel launch");
+  if (validate_enabled()) {
+    st = validation_verdict(r.topk_idx, r.counts, r.offsets, r.perm_token, r.slot_pos, T, n, K, cap,
+                            at<int>(ws, p.verr), stream);
+    if (st != MOE_OK) return st;
+  }
   MOE_LAUNCH(mark(2), "hipEventRecord");
   const auto* w1 = static_cast<const uint16_t*>(W1);
   const auto* w3 = static_cast<const uint16_t*>(W3);
@@ -521,6 +558,23 @@ moe_status_t moe_forward_packed_traced(const void* x, const void* Wg, const void
                       stage_events, INT32_MAX, false, true);
 }
 
+moe_status_t moe_check_dispatch(const int32_t* topk_idx, const int32_t* counts, const int32_t* offsets,
+                                const int32_t* perm_token, const int32_t* slot_pos, int64_t T, int32_t n, int32_t K,
+                                int64_t capacity, moe_stream_t stream) {
+  g_last_error.clear();
+  moe_status_t st = check_shape(T, 1, 1, n, K, false);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || (T > 0 && (!topk_idx || !perm_token || !slot_pos)))
+    return fail(MOE_ERR_INVALID_ARG, "null routing array");
+  if (capacity < 0 || capacity > INT32_MAX) return fail(MOE_ERR_INVALID_ARG, "capacity must be in [0, 2^31)");
+  char* ws = nullptr;
+  st = get_workspace(256, &ws);
+  if (st != MOE_OK) return st;
+  return validation_verdict(topk_idx, counts, offsets, perm_token, slot_pos, T, n, K,
+                            capacity == 0 ? INT32_MAX : (int)capacity, reinterpret_cast<int*>(ws),
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
 moe_status_t moe_forward_noalloc(const void* x, const void* Wg, const void* W1, const void* W3,
                                  const void* W2, int64_t T, int64_t d, int64_t f, int32_t n, int32_t K,
                                  float* y, moe_stream_t stream) {
@@ -637,6 +691,7 @@ const char* moe_status_string(moe_status_t s) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
     case MOE_ERR_HIP: return "MOE_ERR_HIP";
     case MOE_ERR_NO_MEMORY: return "MOE_ERR_NO_MEMORY";
+    case MOE_ERR_VALIDATION: return "MOE_ERR_VALIDATION";
   }
   return "MOE_ERR_UNKNOWN";
 }

@@ -139,6 +139,18 @@ hipError_t launch_q4_up(const uint16_t* x, int64_t T, const int* perm_token, con
 hipError_t launch_q4_down(const uint16_t* h, const uint8_t* Q2, const uint16_t* S2, const int* offsets,
                           int64_t TK, int n, int f, int d, int splits, int cus, float* o, hipStream_t s);
 
+// ------------------------------------------------------------ validation
+// Dispatch invariants, as bit flags in err[0] (err[1]: smallest offending index).
+constexpr int kValidateOffsets = 1;  // offsets[0] != 0, a count negative, above the capacity or != its segment
+constexpr int kValidateTotal = 2;    // offsets[n] != T*K (dropless) or outside [0, T*K]
+constexpr int kValidateIndex = 4;    // an expert index out of range or repeated within a token
+constexpr int kValidateSlot = 8;     // slot_pos outside its expert's segment (or -1 without a capacity)
+constexpr int kValidatePerm = 16;    // perm_token and slot_pos do not point at each other
+constexpr int kValidateOrder = 32;   // tokens not ascending within an expert's segment
+// Clears err and checks the arrays; err is 2 ints of device memory.  cap = INT32_MAX: dropless.
+hipError_t launch_validate(const int* topk_idx, const int* counts, const int* offsets, const int* perm_token,
+                           const int* slot_pos, int64_t T, int n, int K, int cap, int* err, hipStream_t s);
+
 // ----------------------------------------------------------------- combine
 // y[t][:] = sum_k topk_w[t][k] * (sum_s o[s][slot_pos[t][k]][:]), k and s ascending.
 hipError_t launch_combine(const float* o, int splits, int64_t TK, const float* topk_w,

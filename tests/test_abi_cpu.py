@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     _, L = _lib()
     for code, name in [(0, b"MOE_OK"), (1, b"MOE_ERR_INVALID_ARG"), (2, b"MOE_ERR_UNSUPPORTED"),
-                       (3, b"MOE_ERR_HIP"), (4, b"MOE_ERR_NO_MEMORY")]:
+                       (3, b"MOE_ERR_HIP"), (4, b"MOE_ERR_NO_MEMORY"), (5, b"MOE_ERR_VALIDATION")]:
         assert L.moe_status_string(code) == name
 
 
