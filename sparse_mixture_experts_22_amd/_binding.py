@@ -30,7 +30,9 @@ class MoEError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libmoe.so")
+    """The in-tree libmoe.so, or the build named by MOE_LIBRARY (for instance the
+    host-sanitized build that tests/test_abi_sanitized.py makes)."""
+    return os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 
 def lib() -> ctypes.CDLL:

@@ -40,9 +40,20 @@ def compile_flags() -> list:
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (the C-ABI
+# layer and every launcher; device code is compiled as usual).  Each sanitizer
+# flag applies to the host compilation only.
+SANITIZE_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_BUILD = os.path.join(BUILD, "sanitized")
+SAN_LIB = os.path.join(SAN_BUILD, "libmoe_sanitized.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = SAN_BUILD if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    flags = compile_flags() + (SANITIZE_FLAGS if sanitize else [])
+    cmd = [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
@@ -63,6 +74,38 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized build links (a process
+    that did not start with it must preload it)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cands = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not cands:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return cands[-1]
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """libmoe_sanitized.so: the same sources with host-side ASan + UBSan.  The
+    objects are linked by the host compiler driver (they carry their device
+    code already)."""
+    os.makedirs(SAN_BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, sanitize=True), SOURCES))
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    clangxx = os.path.join(rocm, "llvm", "bin", "clang++")
+    host_link = [clangxx, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", "-o", SAN_LIB,
+                 *objs, "-L" + os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    res = subprocess.run(host_link, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
 
 
 if __name__ == "__main__":
