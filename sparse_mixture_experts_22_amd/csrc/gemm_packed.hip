@@ -23,7 +23,9 @@
 // tile of one expert: 128 h columns (MODE 1; 128 of W1 and the matching 128 of
 // W3) or 256 output columns (MODE 2).  Wave w owns all 256 rows against pair
 // 4 nt + w: 8 row blocks x 2 fragments of 32x32 fp32 accumulators (256
-// registers, kept in AGPRs).  Its weight fragments come from the packed stream
+// registers, kept in AGPRs; the MFMA takes the weights as its row operand, so
+// each lane ends with 4 consecutive columns of a row and stores 8 or 16 bytes
+// at a time without staging).  Its weight fragments come from the packed stream
 // straight into a ring of registers, PD k16-steps ahead, so the weights never
 // pass through LDS (half the LDS traffic of staging both operands).  The
 // gathered activation rows go through an LDS ring of PSA super-stages of 64 k
@@ -186,8 +188,10 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][1], acc[i][1], 0, 0, 0);
+        // the transposed product (weights as the row operand): a lane's accumulators hold
+        // 4 consecutive output columns of one row, so the epilogue stores 8 or 16 bytes at once
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][0], a[i], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][1], a[i], acc[i][1], 0, 0, 0);
         a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
         if (i == 0) {
           fence();
@@ -206,31 +210,30 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   // the last (redundant) loads must land before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
 
-  // 32x32 MFMA D layout: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // 32x32 MFMA D layout: register r of lane l is D row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32;
+  // with the transposed product, register 4 q + c of fragment (i, j) is tile row 32 i + l % 32
+  // and column 8 q + 4 (l / 32) + c of the pair's fragment j.
   if (MODE == 1) {
-    // h tile (256 rows x 128 bf16 = 64 KiB) through LDS, stored 16 bytes per lane;
-    // chunk c of row r at c ^ (4 * ((r >> 2) & 1)) keeps the half-waves (rows r, r+4) apart
-    __syncthreads();  // every wave's LDS reads are done
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
-    const int cl = wave * 32 + m;
+    // h: four consecutive bf16 (8 bytes) per (row block, q); the 4 waves' 32-column blocks and
+    // the q groups complete each row's 256 bytes in L2
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int row = i * 32 + m;
+      if (row >= tc.rows || tc.row0 + row >= TK) continue;
+      uint16_t* hrow = hout + (int64_t)(tc.row0 + row) * N + tc.nt * 128 + wave * 32 + 4 * kg;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-        const int ch = (cl >> 3) ^ (4 * ((row >> 2) & 1));
-        hs[row * 128 + ch * 8 + (cl & 7)] = f32_to_bf16_rne(silu_bf16out(acc[i][0][r]) * acc[i][1][r]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int r0 = 4 * q + 2 * h2;
+          const uint32_t lo = f32_to_bf16_rne(silu_bf16out(acc[i][0][r0]) * acc[i][1][r0]);
+          const uint32_t hi = f32_to_bf16_rne(silu_bf16out(acc[i][0][r0 + 1]) * acc[i][1][r0 + 1]);
+          w2[h2] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x2_t*>(hrow + 8 * q) = u32x2_t{w2[0], w2[1]};
       }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int idx = q * 256 + tid;  // chunk idx % 16 (8 columns) of row idx / 16
-      const int row = idx >> 4;
-      const int ch = idx & 15;
-      const int col = tc.nt * 128 + ch * 8;
-      if (row < tc.rows && tc.row0 + row < TK)
-        *reinterpret_cast<u32x4_t*>(hout + (int64_t)(tc.row0 + row) * N + col) =
-            *reinterpret_cast<const u32x4_t*>(hs + row * 128 + (ch ^ (4 * ((row >> 2) & 1))) * 8);
     }
   } else if (tc.slot >= 0) {
     // a k-piece: the whole 256 x 256 partial tile goes to its slot
@@ -240,25 +243,24 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-          dst[row * BN + wave * 64 + j * 32 + m] = acc[i][j][r];
-        }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(dst + (i * 32 + m) * BN + wave * 64 + j * 32 + 8 * q + 4 * kg) =
+              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i) {
+      const int row = i * 32 + m;
+      if (row >= tc.rows || tc.row0 + row >= TK) continue;
+      float* orow = oout + (int64_t)(tc.row0 + row) * N + tc.nt * 256 + wave * 64 + 4 * kg;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int c = tc.nt * 256 + wave * 64 + j * 32 + m;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * kg + (r & 3);
-          if (row < tc.rows && tc.row0 + row < TK) oout[(int64_t)(tc.row0 + row) * N + c] = acc[i][j][r];
-        }
-      }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t*>(orow + j * 32 + 8 * q) =
+              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    }
   }
 }
-
 
 // Weight streaming on packed weights, for decode-sized batches (a few rows per
 // expert): every touched expert's packed stream is read once from HBM.  One
