@@ -60,7 +60,7 @@ enum class Path { kRouteOnly, kStats, kBf16, kPacked, kF32 };
 struct Plan {
   size_t topk_idx = 0, topk_w = 0, hist = 0, bases = 0, wgT = 0, counts = 0, offsets = 0,
          perm_token = 0, slot_pos = 0;
-  size_t h = 0, o = 0, tail = 0, probsum = 0, verr = 0, total = 0;
+  size_t h = 0, o = 0, tail = 0, probsum = 0, verr = 0, sched = 0, total = 0;
   bool skinny = false;
   int splits = 1;
 };
@@ -99,6 +99,7 @@ Plan make_plan(int64_t T, int64_t d, int64_t f, int n, int K, Path path, int cus
     p.h = take((size_t)R * f * 2);
     p.o = take((size_t)p.splits * R * d * 4);
     if (!p.skinny && cus_per_xcd >= 1 && cus_per_xcd <= 64) p.tail = take(moe::prefill_tail_bytes(cus_per_xcd));
+    if (path == Path::kPacked && !p.skinny) p.sched = take((size_t)moe::kPackedSchedWords * 4);
   } else if (path == Path::kF32) {
     p.h = take((size_t)TK * f * 4);
     p.o = take((size_t)TK * d * 4);
@@ -345,8 +346,14 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
   auto mark = [&](int i) -> hipError_t {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), stream) : hipSuccess;
   };
-  const moe::RouteBuffers r =
-      route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  moe::RouteBuffers r = route_buffers(ws, p, RouteOut{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr});
+  int* sched = nullptr;
+  if (packed && !p.skinny) {
+    if (cus < 1 || cus > 64) return fail(MOE_ERR_UNSUPPORTED, "packed tiled path needs 1..64 compute units per XCD");
+    sched = at<int>(ws, p.sched);
+    r.zero = sched;  // the router clears the work counters of the two projections
+    r.n_zero = moe::kPackedCounterWords;
+  }
   uint16_t* h = at<uint16_t>(ws, p.h);
   float* o = at<float>(ws, p.o);
   const auto* xb = static_cast<const uint16_t*>(x);
@@ -371,11 +378,11 @@ moe_status_t forward_bf16(const void* x, const void* Wg, const void* W1, const v
     MOE_LAUNCH(moe::launch_packed_stream_down(h, w2, r.offsets, TK, n, (int)f, (int)d, p.splits, o, stream),
                "down-projection kernel launch");
   } else if (packed) {
-    MOE_LAUNCH(moe::launch_packed_up(xb, T, r.perm_token, w1, r.offsets, TK, n, (int)d, (int)f, cus, h, stream),
+    MOE_LAUNCH(moe::launch_packed_up(xb, T, r.perm_token, w1, r.offsets, TK, n, (int)d, (int)f, cus, sched, h, stream),
                "up-projection kernel launch");
     MOE_LAUNCH(mark(3), "hipEventRecord");
     float* tail = p.tail ? at<float>(ws, p.tail) : nullptr;
-    MOE_LAUNCH(moe::launch_packed_down(h, w2, r.offsets, TK, n, (int)f, (int)d, cus, tail, o, stream),
+    MOE_LAUNCH(moe::launch_packed_down(h, w2, r.offsets, TK, n, (int)f, (int)d, cus, sched, tail, o, stream),
                "down-projection kernel launch");
   } else if (p.skinny) {
     MOE_LAUNCH(moe::launch_skinny_up(xb, T, r.perm_token, w1, w3, r.offsets, TK, n, (int)d, (int)f, h, stream),

@@ -19,13 +19,11 @@
 // and the same W3 columns (j = 1).  Down projection (from W2 [n][f][d]): pair
 // pb < d / 64 holds columns 64 pb + 32 j .. + 31.
 //
-// Kernel.  One 256-thread workgroup (one wave per SIMD) computes a 256-row
-// tile of one expert: 128 h columns (MODE 1; 128 of W1 and the matching 128 of
-// W3) or 256 output columns (MODE 2).  Wave w owns all 256 rows against pair
+// Kernel.  A 256-thread workgroup (one wave per SIMD) computes 256-row tiles
+// of one expert: 128 h columns (MODE 1; 128 of W1 and the matching 128 of W3)
+// or 256 output columns (MODE 2).  Wave w owns all 256 rows against pair
 // 4 nt + w: 8 row blocks x 2 fragments of 32x32 fp32 accumulators (256
-// registers, kept in AGPRs; the MFMA takes the weights as its row operand, so
-// each lane ends with 4 consecutive columns of a row and stores 8 or 16 bytes
-// at a time without staging).  Its weight fragments come from the packed stream
+// registers, kept in AGPRs).  Its weight fragments come from the packed stream
 // straight into a ring of registers, PD k16-steps ahead, so the weights never
 // pass through LDS (half the LDS traffic of staging both operands).  The
 // gathered activation rows go through an LDS ring of PSA super-stages of 64 k
@@ -33,8 +31,15 @@
 // for itself (s_waitcnt vmcnt, counted by issue order) before a barrier
 // publishes the super-stage; chunk c of row r sits at c ^ ((r >> 1) & 7), so
 // the 16 lanes of a 16-byte fragment read served together hit distinct banks.
-// Results equal the caller-layout kernels' bit for bit where no tile is split:
-// the same MFMA, the same fragment contents and the same k order.
+// MODE 1 takes the weights as the MFMA's row operand (each lane ends with 4
+// consecutive h columns of a row: 8-byte stores, and the SiLU pairs stay in
+// one lane); MODE 2 takes the activations (each store instruction writes whole
+// 128-byte pieces of two o rows).
+//
+// One workgroup per compute unit, each looping over a work list of tiles (see
+// below), so a tile's first loads fly while the previous tile's results are
+// written.  Results equal the caller-layout kernels' bit for bit where no tile
+// is split: the same MFMA, the same fragment contents and the same k order.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -83,48 +88,146 @@ constexpr int W_STAGE = packed_wait_stage();
 constexpr int W_FIRST = packed_after(0, 0);
 static_assert(W_STAGE >= 0 && W_STAGE <= 63 && W_FIRST <= 63, "vmcnt is a 6-bit counter");
 
+// Work-list words (int32) of one launch: taken[kXcds] counts the positions
+// handed out beyond the first `cus` of each XCD's share (zero at launch), and
+// kHandoffWords hold two words per workgroup (at most 8 x 64 workgroups).
+constexpr int kHandoffWords = 2 * kXcds * 64;
+static_assert(kPackedCounterWords == 2 * kXcds && kPackedSchedWords == kPackedCounterWords + 2 * kHandoffWords,
+              "work-list words of the two projections");
+
+// An accumulator register read where it is used (the compiler would copy all
+// 256 accumulators to VGPRs at once ahead of the SwiGLU epilogue).
+__device__ __forceinline__ float agpr(float v) {
+  float r;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
     // not __restrict__: loads through a restrict pointer to read-only data may be
     // moved across the asm statements whose issue order the waits count on
     const uint16_t* Bp, const int* __restrict__ offsets, int n, int Kdim, int N, int a_rows, int TK, int cus,
-    uint16_t* __restrict__ hout, float* __restrict__ oout, float* __restrict__ tail_ws) {
+    uint16_t* __restrict__ hout, float* __restrict__ oout, float* __restrict__ tail_ws, int* taken, int* handoffs) {
   __shared__ __attribute__((aligned(1024))) char smem[PSA * A_SUPER];
   constexpr int NTW = (MODE == 1) ? 128 : 256;  // output columns per tile
   const int NT = N / NTW;
-  Tile tc;
+  const int nk = Kdim / BK;
   // pieces of split tiles are whole unrolled loops: PR k16-steps = PR / 2 k-steps of 32
-  if (!decode_tile(offsets, n, NT, Kdim / BK, cus, MODE == 2 && tail_ws != nullptr, PR / 2, tc)) return;
+  const bool may_split = MODE == 2 && tail_ws != nullptr;
+  const ExpertTiles et = expert_tiles(offsets, n);
+  const int total = et.total * NT;
+  const int x = blockIdx.x % kXcds;
+  int* const handoff = handoffs + 2 * blockIdx.x;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  // Work list.  Position pos of XCD xq's share is coded pos * kXcds + xq (-1:
+  // none).  Workgroup (x, i) starts at position i of its XCD's share; later
+  // positions are handed out in order by an atomic counter per XCD, and a
+  // workgroup whose own share is used up takes positions of the other XCDs.
+  // Wave 0 asks for the position after next while a tile runs and hands the
+  // answer to the other waves through a word in global memory (the LDS is all
+  // taken by the activation ring), read after the next end-of-tile barrier.
+  const int len_l = lane < kXcds ? queue_len(xcd_plan(total, lane, cus, nk, may_split, PR / 2)) : 0;
+  auto share_len = [&](int xq) { return __builtin_amdgcn_readlane(len_l, xq); };
+  auto tile_of = [&](int c, Tile& t) -> bool {
+    const int xq = c % kXcds;
+    return queue_tile(offsets, et, NT, nk, cus, xq, xcd_plan(total, xq, cus, nk, may_split, PR / 2), c / kXcds, t);
+  };
+  const bool own_dynamic = share_len(x) > cus;
+  // wave 0 only: a request on the own counter (the answer, in lane 0, is read later)
+  auto request = [&]() -> int {
+    int v = INT32_MAX;
+    if (own_dynamic && lane == 0) {
+      // an index the compiler cannot prove uniform: it would otherwise turn the
+      // add into a wave-wide one whose result is needed (and waited for) at once
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      v = atomicAdd(&taken[x + z], 1);
+    }
+    return v;
+  };
+  // wave 0 only: the position a request gave, or one taken from another XCD's share
+  auto settle = [&](int req) -> int {
+    const int raw = __builtin_amdgcn_readfirstlane(req);
+    if (raw != INT32_MAX && cus + raw < share_len(x)) return (cus + raw) * kXcds + x;
+    for (int k = 1; k < kXcds; ++k) {
+      const int xq = (x + k) % kXcds;
+      const int len = share_len(xq);
+      if (len <= cus) continue;
+      int v = 0;
+      if (lane == 0) v = atomicAdd(&taken[xq], 1);
+      const int pos = cus + __builtin_amdgcn_readfirstlane(v);
+      if (pos < len) return pos * kXcds + xq;
+    }
+    return -1;
+  };
+
+  auto fence = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int cur;
+  const int i0 = blockIdx.x / kXcds;
+  if (i0 < share_len(x)) {
+    cur = i0 * kXcds + x;
+  } else {
+    int c = -1;
+    if (wave == 0) {
+      c = settle(request());
+      if (lane == 0) __hip_atomic_store(&handoff[0], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
+    fence();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    if (wave != 0) c = __hip_atomic_load(&handoff[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cur = __builtin_amdgcn_readfirstlane(c);
+  }
+  Tile tc;
+  if (cur < 0 || !tile_of(cur, tc)) return;
+
   // activation loads: wave w fills blocks 8w .. 8w+7 of each super-stage (8 rows x 128 bytes each)
   const uint16_t* ld_ptr[kDS];
-#pragma unroll
-  for (int b = 0; b < kDS; ++b) {
-    const int r = (wave * kDS + b) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const int rr = r < tc.rows ? r : tc.rows - 1;  // padded rows: computed, never stored
-    const int p = min(max(tc.row0 + rr, 0), TK - 1);
-    const int row = (MODE == 1) ? min(max(perm_token[p], 0), a_rows - 1) : p;
-    ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
-  }
   const uint32_t a_ld_base = (uint32_t)(uintptr_t)(lds_void*)smem + wave * (kDS * 1024);
-  // the wave's weight stream (pair 4 nt + wave of group nt), from this workgroup's first k16-step
   const int KK = Kdim / 16;
   const int G = (MODE == 1) ? N / 128 : N / 256;
-  const uint16_t* bptr = Bp + (((int64_t)(tc.e * G + tc.nt) * KK + tc.k0 * 2) * 4 + wave) * 1024 + lane * 8;
-
-  const int nk16 = (tc.k1 - tc.k0) * 2;  // a multiple of PR
-  const int nss = nk16 / 4;
+  const uint16_t* bptr;
+  int nk16, nss, kbase;
+  // source rows of the wave's activation loads (MODE 1: gathered through perm_token)
+  auto rows_of = [&](const Tile& t, int (&src)[kDS]) {
+#pragma unroll
+    for (int b = 0; b < kDS; ++b) {
+      const int r = (wave * kDS + b) * 8 + (lane >> 3);
+      const int rr = r < t.rows ? r : t.rows - 1;  // padded rows repeat the last row
+      const int p = min(max(t.row0 + rr, 0), TK - 1);
+      src[b] = (MODE == 1) ? perm_token[p] : p;
+    }
+  };
+  auto setup = [&](const Tile& t, const int (&src)[kDS]) {
+#pragma unroll
+    for (int b = 0; b < kDS; ++b) {
+      const int r = (wave * kDS + b) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      const int row = (MODE == 1) ? min(max(src[b], 0), a_rows - 1) : src[b];
+      ld_ptr[b] = A + (int64_t)row * Kdim + c * 8;
+    }
+    // the wave's weight stream (pair 4 nt + wave of group nt), from the tile's first k16-step
+    bptr = Bp + (((int64_t)(t.e * G + t.nt) * KK + t.k0 * 2) * 4 + wave) * 1024 + lane * 8;
+    nk16 = (t.k1 - t.k0) * 2;  // a multiple of PR
+    nss = nk16 / 4;
+    kbase = t.k0 / 2;
+  };
   // Loads past the end re-load the last k-slice (into slots nobody reads
   // again), so every wave issues the same sequence and the counts hold.
   auto issue_a = [&](int stage, int b0, int nb) {
     const uint32_t dst = a_ld_base + (stage % PSA) * A_SUPER;
-    const int64_t koff = (int64_t)(tc.k0 / 2 + min(stage, nss - 1)) * 64;
+    const int64_t koff = (int64_t)(kbase + min(stage, nss - 1)) * 64;
 #pragma unroll
     for (int b = 0; b < nb; ++b) load_lds16(ld_ptr[b0 + b] + koff, dst + (b0 + b) * 1024);
   };
@@ -133,14 +236,14 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     dst[0] = src[0];
     dst[1] = src[64];
   };
-
-  f32x16_t acc[8][2];
+  bf16x8_t br[PR][2];
+  auto prologue = [&] {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int st = 0; st < PSA - 1; ++st) issue_a(st, 0, kDS);
+    issue_a(PSA - 1, 0, kDS / 4);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int t = 0; t < PD; ++t) load_b(t, br[t]);
+  };
 
   // fragment i of sub-step q (k 16 q .. +15 of a super-stage): row 32 i + l % 32, chunk 2 q + l / 32
   const int m = lane & 31;
@@ -149,116 +252,180 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) a_off[q] = m * 128 + (((2 * q + kg) ^ ((m >> 1) & 7)) * 16);
 
-  auto fence = [] {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-#pragma unroll
-  for (int st = 0; st < PSA - 1; ++st) issue_a(st, 0, kDS);
-  issue_a(PSA - 1, 0, kDS / 4);
-  bf16x8_t br[PR][2];
-#pragma unroll
-  for (int t = 0; t < PD; ++t) load_b(t, br[t]);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST, 15));  // super-stage 0 landed
-  fence();
-  __builtin_amdgcn_s_barrier();
-  fence();
-  bf16x8_t a[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
-
-  // Step kk: 16 MFMAs on the fragments read during step kk-1; after each row
-  // block's two MFMAs, that block's fragment of step kk+1 is read.  After the
-  // first block come this step's activation loads (a quarter of a super-stage,
-  // into the slot the barrier of step 4s+3 released), after the fourth the
-  // weight loads of step kk + PD.  The last step of each super-stage starts
-  // with the barrier that publishes the next super-stage.
-  for (int base = 0; base < nk16; base += PR) {
-#pragma unroll
-    for (int u = 0; u < PR; ++u) {
-      const int kk = base + u;
-      if ((u & 3) == 3) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 0));  // own loads landed, own reads done
-        fence();
-        __builtin_amdgcn_s_barrier();
-        fence();
-      }
-      const int stn = (kk + 1) >> 2;  // super-stage of step kk+1
-      const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
+  f32x16_t acc[8][2];
+  // Writes row blocks [ib, ie) of a finished tile.  32x32 MFMA D layout: register r of lane l is
+  // D row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  A padded row (past the tile's rows) was
+  // computed from the tile's last row, so its values equal that row's: it is stored there again,
+  // and every wave issues the same number of stores whatever the tile (the waits count on it).
+  auto epilogue = [&](const Tile& t, int ib, int ie) {
+    if (MODE == 1) {
+      // weights as the row operand: register 4 q + c of fragment (i, j) is tile row 32 i + l % 32,
+      // column 8 q + 4 (l / 32) + c of the pair's fragment j.  h: four consecutive bf16 (8 bytes)
+      // per (row block, q); the 4 waves' 32-column blocks and the q groups complete each row's
+      // 256 bytes in L2
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // the transposed product (weights as the row operand): a lane's accumulators hold
-        // 4 consecutive output columns of one row, so the epilogue stores 8 or 16 bytes at once
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][0], a[i], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][1], a[i], acc[i][1], 0, 0, 0);
-        a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
-        if (i == 0) {
-          fence();
-          issue_a(stn + PSA - 1, ((u + 1) & 3) * (kDS / 4), kDS / 4);
-          fence();
+        if (i < ib || i >= ie) continue;
+        const int row = min(i * 32 + m, t.rows - 1);
+        uint16_t* hrow = hout + (int64_t)(t.row0 + row) * N + t.nt * 128 + wave * 32 + 4 * kg;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w2[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int r0 = 4 * q + 2 * h2;
+            const f32x2_t v = {silu_bf16out(agpr(acc[i][0][r0])) * agpr(acc[i][1][r0]),
+                               silu_bf16out(agpr(acc[i][0][r0 + 1])) * agpr(acc[i][1][r0 + 1])};
+            w2[h2] = bf16x2_rne(v);
+          }
+          *reinterpret_cast<u32x2_t*>(hrow + 8 * q) = u32x2_t{w2[0], w2[1]};
         }
-        if (i == 3) {
-          fence();
-          load_b(kk + PD, br[(u + PD) % PR]);
-          fence();
+        fence();  // one row block's values live at a time
+      }
+    } else {
+      // o rows, or for a k-piece the whole 256 x 256 partial tile in its slot (one code
+      // path, so the store count is the same either way).  Activations as the row operand:
+      // register r of fragment (i, j) is tile row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4,
+      // column 32 j + l % 32 of the wave's 64, so each store covers two whole 128-byte row
+      // pieces (first writes that cover only parts of lines were found much slower).
+      const bool piece = t.slot >= 0;
+      float* const base = piece ? tail_ws + (int64_t)t.slot * (BM * BN) : oout + (int64_t)t.row0 * N + t.nt * 256;
+      const int64_t ld = piece ? BN : N;
+      const int last = piece ? BM - 1 : t.rows - 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < ib || i >= ie) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float* orow = base + (int64_t)min(i * 32 + 8 * (r / 4) + 4 * kg + (r % 4), last) * ld + wave * 64 + m;
+          orow[0] = acc[i][0][r];
+          orow[32] = acc[i][1][r];
         }
       }
-      fence();  // the next step's fragment reads stay in this step
     }
-  }
-  // the last (redundant) loads must land before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(WAITCNT_ALL);
+  };
 
-  // 32x32 MFMA D layout: register r of lane l is D row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32;
-  // with the transposed product, register 4 q + c of fragment (i, j) is tile row 32 i + l % 32
-  // and column 8 q + 4 (l / 32) + c of the pair's fragment j.
-  if (MODE == 1) {
-    // h: four consecutive bf16 (8 bytes) per (row block, q); the 4 waves' 32-column blocks and
-    // the q groups complete each row's 256 bytes in L2
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = i * 32 + m;
-      if (row >= tc.rows || tc.row0 + row >= TK) continue;
-      uint16_t* hrow = hout + (int64_t)(tc.row0 + row) * N + tc.nt * 128 + wave * 32 + 4 * kg;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t w2[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int r0 = 4 * q + 2 * h2;
-          const uint32_t lo = f32_to_bf16_rne(silu_bf16out(acc[i][0][r0]) * acc[i][1][r0]);
-          const uint32_t hi = f32_to_bf16_rne(silu_bf16out(acc[i][0][r0 + 1]) * acc[i][1][r0 + 1]);
-          w2[h2] = lo | (hi << 16);
-        }
-        *reinterpret_cast<u32x2_t*>(hrow + 8 * q) = u32x2_t{w2[0], w2[1]};
-      }
-    }
-  } else if (tc.slot >= 0) {
-    // a k-piece: the whole 256 x 256 partial tile goes to its slot
-    float* dst = tail_ws + (int64_t)tc.slot * (BM * BN);
+  {
+    int src[kDS];
+    rows_of(tc, src);
+    setup(tc, src);
+  }
+  prologue();
+  // wave 0: the position after cur (waited for here, once), handed over now;
+  // the request for the one after that stays in flight during the tile
+  int next = -1, pending = INT32_MAX;
+  int par = 1;
+  if (wave == 0) {
+    next = settle(request());
+    if (lane == 0) __hip_atomic_store(&handoff[par], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (next >= 0) pending = request();
+  }
+
+  // Super-stage 0 of a tile has landed once at most W_FIRST of the loads issued
+  // after it are outstanding, plus whatever was issued after those loads (all
+  // vector memory operations of a wave complete in issue order): after a
+  // previous tile, the stores of its last four row blocks.
+  constexpr int S_LATE = (MODE == 1) ? 4 * 4 : 4 * 32;
+  constexpr int W_FIRST_LATE = (W_FIRST + S_LATE < 63) ? W_FIRST + S_LATE : 63;
+  bool late_stores = false;
+  for (;;) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4_t*>(dst + (i * 32 + m) * BN + wave * 64 + j * 32 + 8 * q + 4 * kg) =
-              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-  } else {
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    if (late_stores)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST_LATE, 15));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST, 15));
+    fence();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    bf16x8_t a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = i * 32 + m;
-      if (row >= tc.rows || tc.row0 + row >= TK) continue;
-      float* orow = oout + (int64_t)(tc.row0 + row) * N + tc.nt * 256 + wave * 64 + 4 * kg;
+    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
+
+    // Step kk: 16 MFMAs on the fragments read during step kk-1; after each row
+    // block's two MFMAs, that block's fragment of step kk+1 is read.  After the
+    // first block come this step's activation loads (a quarter of a super-stage,
+    // into the slot the barrier of step 4s+3 released), after the fourth the
+    // weight loads of step kk + PD.  The last step of each super-stage starts
+    // with the barrier that publishes the next super-stage.
+    for (int base = 0; base < nk16; base += PR) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int u = 0; u < PR; ++u) {
+        const int kk = base + u;
+        if ((u & 3) == 3) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 0));  // own loads landed, own reads done
+          fence();
+          __builtin_amdgcn_s_barrier();
+          fence();
+        }
+        const int stn = (kk + 1) >> 2;  // super-stage of step kk+1
+        const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<f32x4_t*>(orow + j * 32 + 8 * q) =
-              f32x4_t{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        for (int i = 0; i < 8; ++i) {
+          if (MODE == 1) {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][0], a[i], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][1], a[i], acc[i][1], 0, 0, 0);
+          } else {
+            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][0], acc[i][0], 0, 0, 0);
+            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][1], acc[i][1], 0, 0, 0);
+          }
+          a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
+          if (i == 0) {
+            fence();
+            issue_a(stn + PSA - 1, ((u + 1) & 3) * (kDS / 4), kDS / 4);
+            fence();
+          }
+          if (i == 3) {
+            fence();
+            load_b(kk + PD, br[(u + PD) % PR]);
+            fence();
+          }
+        }
+        fence();  // the next step's fragment reads stay in this step
+      }
     }
+    // Every wave's loads have landed (the last, redundant ones included) and its
+    // LDS reads are done: after the barrier the ring may take the next tile.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    fence();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    // The transition to the next tile is interleaved with this tile's epilogue:
+    // row blocks 0-1 are written while the hand-over word comes in, 2-3 while
+    // the next tile's gathered row indices come in, 4-7 while its first
+    // super-stages and weight steps load.
+    // (wave 0 reads back its own word: its store completed before the barrier)
+    int c = __hip_atomic_load(&handoff[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const Tile told = tc;
+    epilogue(told, 0, 2);
+    fence();
+    c = __builtin_amdgcn_readfirstlane(c);
+    const bool more = c >= 0 && tile_of(c, tc);
+    int src[kDS];
+    if (more) rows_of(tc, src);
+    fence();
+    epilogue(told, 2, 4);
+    fence();
+    if (more) {
+      setup(tc, src);
+      prologue();
+      par ^= 1;
+      if (wave == 0) {
+        next = settle(pending);
+        if (lane == 0) __hip_atomic_store(&handoff[par], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pending = next >= 0 ? request() : INT32_MAX;
+      }
+    }
+    fence();
+    epilogue(told, 4, 8);
+    late_stores = true;
+    if (!more) break;
+    fence();
   }
 }
 
@@ -398,26 +565,25 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_packed_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
-                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, uint16_t* h,
-                            hipStream_t s) {
-  const int NT = f / 128;
-  hipLaunchKernelGGL((packed_gemm_kernel<1>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(256), 0, s, x,
-                     perm_token, W13p, offsets, n, d, f, (int)T, (int)TK, cus_per_xcd, h, (float*)nullptr,
-                     (float*)nullptr);
+                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, int* sched,
+                            uint16_t* h, hipStream_t s) {
+  if (cus_per_xcd < 1 || cus_per_xcd > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((packed_gemm_kernel<1>), dim3(kXcds * cus_per_xcd), dim3(256), 0, s, x, perm_token, W13p,
+                     offsets, n, d, f, (int)T, (int)TK, cus_per_xcd, h, (float*)nullptr, (float*)nullptr, sched,
+                     sched + kPackedCounterWords);
   return hipGetLastError();
 }
 
 hipError_t launch_packed_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n, int f,
-                              int d, int cus_per_xcd, float* tail_ws, float* o, hipStream_t s) {
-  const int NT = d / 256;
-  hipLaunchKernelGGL((packed_gemm_kernel<2>), dim3(prefill_grid(TK, n, NT, cus_per_xcd)), dim3(256), 0, s, h,
-                     (const int*)nullptr, W2p, offsets, n, f, d, (int)TK, (int)TK, cus_per_xcd, (uint16_t*)nullptr,
-                     o, tail_ws);
+                              int d, int cus_per_xcd, int* sched, float* tail_ws, float* o, hipStream_t s) {
+  if (cus_per_xcd < 1 || cus_per_xcd > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((packed_gemm_kernel<2>), dim3(kXcds * cus_per_xcd), dim3(256), 0, s, h, (const int*)nullptr,
+                     W2p, offsets, n, f, d, (int)TK, (int)TK, cus_per_xcd, (uint16_t*)nullptr, o, tail_ws,
+                     sched + kXcds, sched + kPackedCounterWords + kHandoffWords);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tail_ws == nullptr || cus_per_xcd < 2) return e;  // fewer CUs never split
   return launch_tail_reduce(offsets, n, d, f / BK, cus_per_xcd, PR / 2, tail_ws, o, s);
 }
-
 
 int packed_stream_splits(int n, int f, int d, int cus_per_xcd) {
   // about 3 down-projection waves per compute unit (measured best at the

@@ -36,6 +36,8 @@ struct RouteBuffers {
   int* perm_token;  // [T*K]
   int* slot_pos;    // [T][K]
   uint16_t* wgT;    // [n_pad][d] transposed router (bf16 path)
+  int* zero = nullptr;  // words the router sets to zero (the packed GEMMs' work counters)
+  int n_zero = 0;
 };
 
 // Rows of an expert handled by one prefill tile.
@@ -103,11 +105,17 @@ hipError_t launch_tail_reduce(const int* offsets, int n, int N, int nk, int cus_
 // d % 256 == 0).  mode 1 packs (W, W3) as the up pair, mode 2 packs W alone.
 hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, int R, int C, uint16_t* out,
                        hipStream_t s);
+// The tiled packed projections run one workgroup per compute unit, each taking
+// tiles from a work list until it is empty (1 <= cus_per_xcd <= 64).  `sched`:
+// kPackedSchedWords int32 of device memory whose first kPackedCounterWords
+// words are zero at the up projection's launch (the router clears them).
+constexpr int kPackedCounterWords = 16;
+constexpr int kPackedSchedWords = kPackedCounterWords + 2 * 2 * 8 * 64;
 hipError_t launch_packed_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
-                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, uint16_t* h,
-                            hipStream_t s);
+                            const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, int* sched,
+                            uint16_t* h, hipStream_t s);
 hipError_t launch_packed_down(const uint16_t* h, const uint16_t* W2p, const int* offsets, int64_t TK, int n, int f,
-                              int d, int cus_per_xcd, float* tail_ws, float* o, hipStream_t s);
+                              int d, int cus_per_xcd, int* sched, float* tail_ws, float* o, hipStream_t s);
 // Weight streaming on packed weights (decode-sized batches): the up projection
 // streams each touched expert's pairs once; the down projection splits the
 // reduction over f into `splits` parts (o[split][p][:] partial sums).
@@ -161,6 +169,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   uint32_t b = __float_as_uint(v);
   b += 0x7FFFu + ((b >> 16) & 1u);
   return (uint16_t)(b >> 16);
+}
+
+// The same rounding for two values at once (the hardware's packed conversion,
+// round to nearest even; its low half is v[0]).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(f32x2_t v) {
+  const bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return *reinterpret_cast<const uint32_t*>(&b);
 }
 
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }

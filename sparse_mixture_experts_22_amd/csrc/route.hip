@@ -244,7 +244,10 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ WgT, int64_t T, int d, int n, int K,
     int* __restrict__ topk_idx, float* __restrict__ topk_w, int* __restrict__ hist, int fused,
     int* __restrict__ counts, int* __restrict__ offsets, int* __restrict__ perm_token,
-    int* __restrict__ slot_pos, float* __restrict__ probsum, int cap, float* __restrict__ ec_probs) {
+    int* __restrict__ slot_pos, float* __restrict__ probsum, int cap, float* __restrict__ ec_probs,
+    int* __restrict__ zero, int n_zero) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   constexpr int BT = 16 * TT;
   constexpr int NP = 16 * NE;
   constexpr int LDL = NP + 1;
@@ -479,7 +482,7 @@ void launch_router_t(const uint16_t* x, const uint16_t* WgT, int64_t T, int64_t 
   const int64_t nb = (T + BT - 1) / BT;
   hipLaunchKernelGGL((router_bf16_kernel<NE, TT, W, DIRECT>), dim3((unsigned)nb), dim3(W * 64), 0, s, x, WgT,
                      T, (int)d, n, K, rb.topk_idx, rb.topk_w, rb.hist, fused ? 1 : 0, rb.counts,
-                     rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap, ec_probs);
+                     rb.offsets, rb.perm_token, rb.slot_pos, probsum, cap, ec_probs, rb.zero, rb.n_zero);
 }
 
 // Router statistics from the per-block histograms and probability sums

@@ -141,26 +141,24 @@ __device__ XcdPlan xcd_plan(int total, int x, int cus, int nk, bool may_split, i
   return t;
 }
 
-// Maps this workgroup to its tile (or k-piece of a tile); false if it has none.
-// Every wave computes the same answer from offsets[0..n].
-__device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int nk, int cus,
-                            bool may_split, int gran, Tile& tc) {
-  const ExpertTiles et = expert_tiles(offsets, n);
-  const int total = et.total * NT;
-  const int x = blockIdx.x % kXcds;
-  const int i = blockIdx.x / kXcds;
-  const XcdPlan t = xcd_plan(total, x, cus, nk, may_split, gran);
+// Positions in an XCD's share: q whole tiles, then r * s k-pieces when the
+// leftover tiles are split, else all cnt tiles whole.
+__device__ __forceinline__ int queue_len(const XcdPlan& t) { return t.s == 1 ? t.cnt : t.q + t.r * t.s; }
+
+// Position `pos` of XCD x's share (plan t) -> tile or k-piece; false past its end.
+__device__ bool queue_tile(const int* __restrict__ offsets, const ExpertTiles& et, int NT, int nk, int cus, int x,
+                           const XcdPlan& t, int pos, Tile& tc) {
   tc.k0 = 0;
   tc.k1 = nk;
   tc.slot = -1;
   int L;
   if (t.s == 1) {
-    if (i >= t.cnt) return false;
-    L = t.beg + i;
-  } else if (i < t.q) {
-    L = t.beg + i;
+    if (pos >= t.cnt) return false;
+    L = t.beg + pos;
+  } else if (pos < t.q) {
+    L = t.beg + pos;
   } else {
-    const int u = i - t.q;
+    const int u = pos - t.q;
     if (u >= t.r * t.s) return false;
     L = t.beg + t.q + u % t.r;
     const int piece = u / t.r;
@@ -169,6 +167,16 @@ __device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int 
     tc.slot = x * cus + u;
   }
   return tile_at(offsets, et, NT, L, tc);
+}
+
+// Maps this workgroup to its tile (or k-piece of a tile); false if it has none.
+// Every wave computes the same answer from offsets[0..n].
+__device__ bool decode_tile(const int* __restrict__ offsets, int n, int NT, int nk, int cus,
+                            bool may_split, int gran, Tile& tc) {
+  const ExpertTiles et = expert_tiles(offsets, n);
+  const int x = blockIdx.x % kXcds;
+  const XcdPlan t = xcd_plan(et.total * NT, x, cus, nk, may_split, gran);
+  return queue_tile(offsets, et, NT, nk, cus, x, t, blockIdx.x / kXcds, tc);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
