@@ -19,8 +19,13 @@
 //                        LDS in wave order, then top-K + softmax + the block's
 //                        expert histogram.  With a single routing block the
 //                        same kernel also performs the scan and the scatter.
+//   router_wave_kernel   many tokens and n in {32, 64, 128, 256}: one routing
+//                        block per wave with the whole d reduction, W_g shared
+//                        through LDS in its own layout (no transposed copy),
+//                        top-K by wave-wide arg-max rounds.
 //   scan_kernel          one workgroup: per-block bases (offsets[e] plus the
-//                        assignments to e in earlier blocks), counts, offsets.
+//                        assignments to e in earlier blocks), counts, offsets
+//                        (scan4_kernel: the same with 16-byte rows, n % 4 == 0).
 //   scatter_kernel       per block: rank of each assignment among the block's
 //                        tokens that chose the same expert (LDS bitmask +
 //                        popcount), position = base + rank.
@@ -347,6 +352,241 @@ __global__ __launch_bounds__(W * 64) void router_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// bf16 router for many tokens and n % 16 == 0 experts.  Each wave owns one
+// routing block of 16*TT tokens and the whole reduction over d, so its logits
+// stay in registers; the workgroup's 4 waves share W_g, streamed through LDS in
+// chunks of KC rows in its own [d][n] layout (a contiguous copy) and read as
+// MFMA B fragments with transposing LDS reads (ds_read_b64_tr_b16: when lane
+// q + 4j of a 16-lane group points at W[k + j][e0 + 4q ..], lane i of the
+// group receives W[k .. k+3][e0 + i]).  x rows are read once, straight into
+// registers, DA chunks ahead.  Top-K runs across the 16 lanes that hold a
+// token's logits: K rounds of a butterfly arg-max (larger score, then lower
+// expert index; NaN as -inf), the winner's lane retiring it; the softmax over
+// the kept scores is the same expression as topk_softmax.
+template <int NE, int TT>
+__global__ __launch_bounds__(256) void router_wave_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ Wg, int64_t T, int d,
+                                                          int K, int* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w, int* __restrict__ hist,
+                                                          float* __restrict__ probsum, int* __restrict__ zero,
+                                                          int n_zero) {
+  constexpr int n = 16 * NE;
+  constexpr int BTW = 16 * TT;              // tokens per wave (one routing block)
+  constexpr int KC = n <= 64 ? 64 : 32;     // W_g rows per LDS chunk
+  constexpr int NBUF = 3;                   // LDS chunk buffers
+  constexpr int RS = n * 2 + 16;            // LDS row stride (bytes): padded against bank conflicts
+  constexpr int CH = KC * n * 2;            // bytes per chunk in W_g
+  constexpr int PIECES = CH / (16 * 256);   // 16-byte pieces per thread per chunk
+  static_assert(PIECES >= 1 && CH % (16 * 256) == 0, "chunk copy");
+  constexpr int DA = 4;                     // chunks of x and of W_g in flight
+  static_assert(DA % 2 == 0, "fragment buffers alternate by k-step");
+  constexpr int KS = KC / 32;               // MFMA k-steps per chunk
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  __shared__ __attribute__((aligned(16))) char wg_s[NBUF][KC * RS];
+  __shared__ int hist_s[4][n];
+
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int64_t nb = (T + BTW - 1) / BTW;
+  const int64_t blk = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t t0 = blk * BTW;
+
+  const uint16_t* ap[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    int64_t tok = t0 + tt * 16 + r;
+    if (tok >= T) tok = T - 1;  // rows past the end are computed, never stored
+    ap[tt] = x + tok * (int64_t)d + g * 8;
+  }
+  const int nch = d / KC;
+  // Loads past the last chunk re-read it (never used), so every iteration issues the
+  // same loads.  Each iteration issues W_g before x: the wait for a W_g chunk then
+  // covers only x chunks that are already needed (a wave's loads complete in order).
+  const u32x4_t* wsrc = reinterpret_cast<const u32x4_t*>(Wg);
+  u32x4_t rb[DA][PIECES];
+  auto load_b = [&](int c, u32x4_t (&dst)[PIECES]) {
+    const int64_t cc = min(c, nch - 1);
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) dst[i] = wsrc[cc * (CH / 16) + i * 256 + tid];
+  };
+  auto store_b = [&](int c, const u32x4_t (&src)[PIECES]) {
+    char* dst = wg_s[c % NBUF];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int byte = (i * 256 + tid) * 16;  // of the chunk in W_g's layout
+      *reinterpret_cast<u32x4_t*>(dst + (byte / (n * 2)) * RS + byte % (n * 2)) = src[i];
+    }
+  };
+  bf16x8_t ra[DA][TT][KS];
+  auto load_a = [&](int c, bf16x8_t (&dst)[TT][KS]) {
+    const int cc = min(c, nch - 1);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        dst[tt][ks] = *reinterpret_cast<const bf16x8_t*>(ap[tt] + cc * KC + ks * 32);
+  };
+  // B fragments of experts 16 et .. +15 at k-step ks of a chunk: two transposing reads each
+  const int lq = r & 3, lj = r >> 2;
+  bf16x8_t fb[2][NE];
+  auto read_b = [&](int c, int ks, bf16x8_t (&dst)[NE]) {
+    const char* row = wg_s[c % NBUF] + (ks * 32 + 8 * g + lj) * RS + 8 * lq;
+#pragma unroll
+    for (int et = 0; et < NE; ++et) {
+      const char* p0 = row + et * 32;
+      const i16x4_t both[2] = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0)),
+                               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * RS))};
+      dst[et] = *reinterpret_cast<const bf16x8_t*>(both);
+    }
+  };
+
+  f32x4_t acc[TT][NE];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int et = 0; et < NE; ++et) acc[tt][et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int c = 0; c < DA; ++c) {
+    load_b(c, rb[c]);
+    load_a(c, ra[c]);
+  }
+  store_b(0, rb[0]);
+  __syncthreads();
+  read_b(0, 0, fb[0]);
+  // Iteration c: chunk c+1 goes to LDS and is published by the barrier, so the
+  // fragments of the next k-step can always be read while the MFMAs of the
+  // current one run (the buffer written in iteration c last held chunk c-2,
+  // whose reads every wave finished before the barrier of iteration c-1).
+  // nch is a multiple of DA: every iteration issues the same loads, so the
+  // compiler's own waits stay exact around the loop.
+  for (int c0 = 0; c0 < nch; c0 += DA) {
+#pragma unroll
+    for (int u = 0; u < DA; ++u) {
+      const int c = c0 + u;
+      store_b(c + 1, rb[(u + 1) % DA]);  // chunk c+1 (past the end: a copy of the last, unread)
+      __syncthreads();
+      load_b(c + DA, rb[u]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int cur = (u * KS + ks) & 1;  // k-steps alternate fragment buffers (DA is even)
+        // next k-step's fragments (the first of chunk c+1 after the last of chunk c)
+        if (ks + 1 < KS)
+          read_b(c, ks + 1, fb[cur ^ 1]);
+        else
+          read_b(c + 1, 0, fb[cur ^ 1]);
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt)
+            acc[tt][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[u][tt][ks], fb[cur][et], acc[tt][et], 0, 0, 0);
+      }
+      load_a(c + DA, ra[u]);
+    }
+  }
+
+  // top-K per token; lane (r, g) holds experts 16 et + r of tokens 4 g + j of each token tile
+  for (int e = lane; e < n; e += 64) hist_s[wave][e] = 0;
+  float psum[NE];  // router statistics: this lane's sum of its experts' probabilities
+#pragma unroll
+  for (int et = 0; et < NE; ++et) psum[et] = 0.0f;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + tt * 16 + 4 * g + j;
+      uint32_t taken = 0;
+      float sv[kMaxK];
+      int si[kMaxK];
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k) {
+        sv[k] = -INFINITY;
+        si[k] = 0;
+        if (k < K) {
+          float bv = -INFINITY;
+          int bi = INT32_MAX;
+#pragma unroll
+          for (int et = 0; et < NE; ++et) {
+            float v = acc[tt][et][j];
+            if (v != v) v = -INFINITY;
+            const int idx = et * 16 + r;
+            if (!((taken >> et) & 1u) && (v > bv || (v == bv && idx < bi))) {
+              bv = v;
+              bi = idx;
+            }
+          }
+#pragma unroll
+          for (int mk = 1; mk < 16; mk <<= 1) {
+            const float ov = __shfl_xor(bv, mk, 16);
+            const int oi = __shfl_xor(bi, mk, 16);
+            if (ov > bv || (ov == bv && oi < bi)) {
+              bv = ov;
+              bi = oi;
+            }
+          }
+          if ((bi & 15) == r) taken |= 1u << (bi >> 4);
+          sv[k] = bv;
+          si[k] = bi;
+        }
+      }
+      // the softmax over the kept scores, term by term as topk_softmax
+      float w[kMaxK];
+      float sum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMaxK; ++k)
+        if (k < K) {
+          w[k] = expf(sv[k] - sv[0]);
+          sum += w[k];
+        }
+      if (t < T) {
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k)
+          if (k < K && r == k) {
+            topk_idx[t * K + k] = si[k];
+            topk_w[t * K + k] = w[k] / sum;
+            atomicAdd(&hist_s[wave][si[k]], 1);
+          }
+      }
+      if (probsum != nullptr && t < T) {
+        // the token's full n-way softmax: max (NaN ignored) and sum of exponentials over its 16 lanes
+        float mx = -INFINITY;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) mx = fmaxf(mx, acc[tt][et][j]);
+#pragma unroll
+        for (int mk = 1; mk < 16; mk <<= 1) mx = fmaxf(mx, __shfl_xor(mx, mk, 16));
+        float ex[NE], sm = 0.0f;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+          ex[et] = expf(acc[tt][et][j] - mx);
+          sm += ex[et];
+        }
+#pragma unroll
+        for (int mk = 1; mk < 16; mk <<= 1) sm += __shfl_xor(sm, mk, 16);
+#pragma unroll
+        for (int et = 0; et < NE; ++et) psum[et] += ex[et] / sm;
+      }
+    }
+  if (blk < nb)
+    for (int e = lane; e < n; e += 64) hist[blk * n + e] = hist_s[wave][e];
+  if (probsum != nullptr) {
+    // the routing block's sum over its tokens: the lanes of the four token groups, then written by group 0
+#pragma unroll
+    for (int et = 0; et < NE; ++et) {
+      float v = psum[et];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (blk < nb && g == 0) probsum[blk * n + et * 16 + r] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 router: one dot product per (token, expert), sequential in j.
 __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x,
                                                          const float* __restrict__ Wg, int64_t T,
@@ -433,6 +673,89 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ hist
       bases[(int64_t)b * n + e] = run;
       run += hist[(int64_t)b * n + e];
     }
+  }
+}
+
+// The same scan when n % 4 == 0, four experts per thread with 16-byte loads:
+// thread (quad q, part p) holds its part's histogram rows in registers (at
+// most kScanRows per pass; longer parts take more passes), so every load of a
+// pass is in flight at once.  The parts' sums are scanned across the
+// workgroup in LDS (Hillis-Steele over p), the experts' offsets by one thread.
+constexpr int kScanRows = 16;
+
+__global__ __launch_bounds__(1024) void scan4_kernel(const int* __restrict__ hist, int nb, int n, int cap,
+                                                     int* __restrict__ bases, int* __restrict__ counts,
+                                                     int* __restrict__ offsets) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  __shared__ i32x4_t part_s[2][1024];
+  __shared__ int tot_s[kMaxN];
+  __shared__ int off_s[kMaxN + 1];
+  const int tid = threadIdx.x;
+  const int nq = n / 4;
+  const int P = 1024 / nq;  // parts (n <= 256: at least 16)
+  const int q = tid % nq;
+  const int p = tid / nq;
+  const bool active = p < P;
+  const int b0 = active ? (int)((int64_t)p * nb / P) : 0;
+  const int b1 = active ? (int)((int64_t)(p + 1) * nb / P) : 0;
+  const i32x4_t* h4 = reinterpret_cast<const i32x4_t*>(hist);
+  i32x4_t s = {0, 0, 0, 0};
+  for (int c0 = b0; c0 < b1; c0 += kScanRows) {
+    i32x4_t v[kScanRows];
+#pragma unroll
+    for (int j = 0; j < kScanRows; ++j)
+      if (c0 + j < b1) v[j] = h4[(int64_t)(c0 + j) * nq + q];
+#pragma unroll
+    for (int j = 0; j < kScanRows; ++j)
+      if (c0 + j < b1) s += v[j];
+  }
+  // inclusive scan of the parts' sums over p (same q), ping-pong buffers
+  int cur = 0;
+  part_s[0][tid] = s;
+  __syncthreads();
+  for (int d = 1; d < P; d <<= 1) {
+    i32x4_t t = part_s[cur][tid];
+    if (active && p >= d) t += part_s[cur][tid - d * nq];
+    part_s[cur ^ 1][tid] = t;
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (tid < nq) {
+    const i32x4_t t = part_s[cur][(P - 1) * nq + tid];
+    tot_s[4 * tid] = t[0];
+    tot_s[4 * tid + 1] = t[1];
+    tot_s[4 * tid + 2] = t[2];
+    tot_s[4 * tid + 3] = t[3];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < n; ++i) {
+      off_s[i] = run;
+      run += min(tot_s[i], cap);
+    }
+    off_s[n] = run;
+  }
+  __syncthreads();
+  for (int i = tid; i <= n; i += 1024) {
+    offsets[i] = off_s[i];
+    if (i < n) counts[i] = min(tot_s[i], cap);
+  }
+  if (!active) return;
+  // bases of the part's rows: offsets plus everything before (exclusive over parts, then rows)
+  i32x4_t run = i32x4_t{off_s[4 * q], off_s[4 * q + 1], off_s[4 * q + 2], off_s[4 * q + 3]} + part_s[cur][tid] - s;
+  i32x4_t* bases4 = reinterpret_cast<i32x4_t*>(bases);
+  for (int c0 = b0; c0 < b1; c0 += kScanRows) {
+    i32x4_t v[kScanRows];
+#pragma unroll
+    for (int j = 0; j < kScanRows; ++j)
+      if (c0 + j < b1) v[j] = h4[(int64_t)(c0 + j) * nq + q];
+#pragma unroll
+    for (int j = 0; j < kScanRows; ++j)
+      if (c0 + j < b1) {
+        bases4[(int64_t)(c0 + j) * nq + q] = run;
+        run += v[j];
+      }
   }
 }
 
@@ -695,6 +1018,31 @@ __global__ __launch_bounds__(kEcWaves * 64) void expert_choice_kernel(const floa
 
 int route_block_tokens(int n) { return n <= 64 ? 32 : 16; }
 
+// Many tokens (more than one routing block) and n in {32, 64, 128, 256}: the
+// wave-per-routing-block router.  Routing and router statistics take the same
+// kernel, so both see the same selection.
+bool use_wave_router(int64_t T, int64_t d, int n) {
+  return T > route_block_tokens(n) && (n == 32 || n == 64 || n == 128 || n == 256) && d % 256 == 0;
+}
+
+void launch_router_wave(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n, int K,
+                        const RouteBuffers& rb, float* probsum, hipStream_t s) {
+  const int64_t nb = (T + route_block_tokens(n) - 1) / route_block_tokens(n);
+  const dim3 grid((unsigned)((nb + 3) / 4)), block(256);
+  if (n == 32)
+    hipLaunchKernelGGL((router_wave_kernel<2, 2>), grid, block, 0, s, x, Wg, T, (int)d, K, rb.topk_idx, rb.topk_w,
+                       rb.hist, probsum, rb.zero, rb.n_zero);
+  else if (n == 64)
+    hipLaunchKernelGGL((router_wave_kernel<4, 2>), grid, block, 0, s, x, Wg, T, (int)d, K, rb.topk_idx, rb.topk_w,
+                       rb.hist, probsum, rb.zero, rb.n_zero);
+  else if (n == 128)
+    hipLaunchKernelGGL((router_wave_kernel<8, 1>), grid, block, 0, s, x, Wg, T, (int)d, K, rb.topk_idx, rb.topk_w,
+                       rb.hist, probsum, rb.zero, rb.n_zero);
+  else
+    hipLaunchKernelGGL((router_wave_kernel<16, 1>), grid, block, 0, s, x, Wg, T, (int)d, K, rb.topk_idx, rb.topk_w,
+                       rb.hist, probsum, rb.zero, rb.n_zero);
+}
+
 int route_padded_experts(int n) { return (n + 15) / 16 * 16; }
 
 hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
@@ -709,6 +1057,8 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
     // transposed copy first (7 us at the Mixtral shape); the whole dispatch
     // runs in the router when one routing block covers T
     launch_router_t<1, 2, 16, true>(x, Wg, T, d, n, K, rb, fused, nullptr, cap, nullptr, s);
+  } else if (use_wave_router(T, d, n)) {
+    launch_router_wave(x, Wg, T, d, n, K, rb, nullptr, s);
   } else {
     const int NP = route_padded_experts(n);
     hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
@@ -726,12 +1076,17 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
 hipError_t launch_route_stats_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, int64_t d, int n,
                                    int K, float alpha, const RouteBuffers& rb, float* probsum,
                                    float* frac, float* prob, float* aux_loss, hipStream_t s) {
-  const int NP = route_padded_experts(n);
-  hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
-                     dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  launch_router_bf16(x, T, d, n, K, rb, false, probsum, INT32_MAX, s);
+  hipError_t e;
+  if (use_wave_router(T, d, n)) {
+    launch_router_wave(x, Wg, T, d, n, K, rb, probsum, s);
+  } else {
+    const int NP = route_padded_experts(n);
+    hipLaunchKernelGGL(wg_transpose_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((NP + 63) / 64)),
+                       dim3(256), 0, s, Wg, (int)d, n, NP, rb.wgT);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_router_bf16(x, T, d, n, K, rb, false, probsum, INT32_MAX, s);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int BT = route_block_tokens(n);
@@ -784,8 +1139,12 @@ hipError_t launch_route_stats_f32(const float* x, const float* Wg, int64_t T, in
 hipError_t launch_dispatch(int64_t T, int n, int K, const RouteBuffers& rb, hipStream_t s, int cap) {
   const int BT = route_block_tokens(n);
   const int nb = (int)((T + BT - 1) / BT);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, cap, rb.bases, rb.counts,
-                     rb.offsets);
+  if (n % 4 == 0)
+    hipLaunchKernelGGL(scan4_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, cap, rb.bases, rb.counts,
+                       rb.offsets);
+  else
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, rb.hist, nb, n, cap, rb.bases, rb.counts,
+                       rb.offsets);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)nb), dim3(64), 0, s, rb.topk_idx, rb.bases, rb.offsets,

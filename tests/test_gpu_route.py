@@ -66,6 +66,11 @@ def test_route_full_configs(name):
     (200, 64, 256, 8, "bf16"),     # maximum n and K
     (300, 64, 8, 8, "bf16"),       # K = n
     (300, 64, 8, 1, "bf16"),       # K = 1
+    (1000, 256, 32, 2, "bf16"),    # many tokens, n % 16 == 0: a routing block per wave, W_g read in place
+    (777, 512, 64, 2, "bf16"),     # 64 experts, ragged last routing block
+    (300, 256, 128, 4, "bf16"),    # 128 experts: 16-token routing blocks
+    (129, 256, 256, 8, "bf16"),    # 256 experts, K = 8
+    (40, 256, 64, 1, "bf16"),      # two routing blocks, K = 1
     (333, 48, 6, 2, "f32"),
     (129, 64, 256, 8, "f32"),
 ])
@@ -113,6 +118,39 @@ def test_route_ties_below_a_larger_later_logit(dtype, T, K):
         inp.x, inp.Wg = bf16_bits_from_f32(x), bf16_bits_from_f32(wg)
     else:
         inp.x, inp.Wg = x, wg
+    gpu = _gpu_route(inp, K)
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), K)
+    np.testing.assert_array_equal(gpu["topk_idx"], r["sel"])
+    np.testing.assert_allclose(gpu["topk_w"], r["w"], rtol=0, atol=1e-6)
+    for name in ("counts", "offsets", "perm_token", "slot_pos"):
+        np.testing.assert_array_equal(gpu[name].reshape(np.shape(r[name])), r[name])
+
+
+# Exact ties spread over the lanes and expert tiles of the wave-level top-K (64
+# experts, several routing blocks): larger score first, then the lower index.
+_TIE_PATTERNS_64 = [
+    {7: 1.0, 40: 1.0},                      # a tie across expert tiles, then the zeros from 0 up
+    {63: 3.0, 16: 2.0, 32: 2.0, 48: 2.0},   # one winner, then a three-way tie at the tiles' first lanes
+    {},                                     # all equal: the lowest indices
+    {0: 1.0, 15: 1.0, 31: 1.0, 47: 1.0},    # ties at the ends of the 16-lane groups
+    {e: -e / 64.0 for e in range(64)},      # strictly decreasing with the index
+    {e: -2.0 for e in range(8)},            # the first experts below all the others
+]
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 8])
+def test_route_ties_many_experts(K):
+    from synth import bf16_bits_from_f32
+    T, d, n = 200, 256, 64
+    inp = make_inputs(T, d, 64, n, K, dtype="bf16", seed=29, router_only=True)
+    P = len(_TIE_PATTERNS_64)
+    x = np.zeros((T, d), dtype=np.float32)
+    x[np.arange(T), np.arange(T) % P] = 1.0       # token t's logits are pattern t % P, exactly
+    wg = np.zeros((d, n), dtype=np.float32)
+    for i, pat in enumerate(_TIE_PATTERNS_64):
+        for e, v in pat.items():
+            wg[i, e] = v
+    inp.x, inp.Wg = bf16_bits_from_f32(x), bf16_bits_from_f32(wg)
     gpu = _gpu_route(inp, K)
     r = oracle.route(inp.f64("x"), inp.f64("Wg"), K)
     np.testing.assert_array_equal(gpu["topk_idx"], r["sel"])
