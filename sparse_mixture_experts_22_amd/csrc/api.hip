@@ -258,6 +258,7 @@ moe::RouteBuffers route_buffers(char* ws, const Plan& p, const RouteOut& user) {
   r.hist = at<int>(ws, p.hist);
   r.bases = at<int>(ws, p.bases);
   r.wgT = at<uint16_t>(ws, p.wgT);
+  r.split = at<float>(ws, p.wgT);  // the transposed copy is unused where the split router runs
   return r;
 }
 

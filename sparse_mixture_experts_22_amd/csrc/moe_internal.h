@@ -36,6 +36,7 @@ struct RouteBuffers {
   int* perm_token;  // [T*K]
   int* slot_pos;    // [T][K]
   uint16_t* wgT;    // [n_pad][d] transposed router (bf16 path)
+  float* split = nullptr;  // [d / 256][32][16] partial logits of the split single-block router
   int* zero = nullptr;  // words the router sets to zero (the packed GEMMs' work counters)
   int n_zero = 0;
 };

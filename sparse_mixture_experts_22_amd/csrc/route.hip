@@ -23,6 +23,9 @@
 //                        block per wave with the whole d reduction, W_g shared
 //                        through LDS in its own layout (no transposed copy),
 //                        top-K by wave-wide arg-max rounds.
+//   router_split_kernel  one routing block (decode) and n <= 16: the d
+//   + router_finish_kernel reduction split over workgroups, then one workgroup
+//                        adds the partials and runs top-K and the dispatch.
 //   scan_kernel          one workgroup: per-block bases (offsets[e] plus the
 //                        assignments to e in earlier blocks), counts, offsets
 //                        (scan4_kernel: the same with 16-byte rows, n % 4 == 0).
@@ -587,6 +590,92 @@ __global__ __launch_bounds__(256) void router_wave_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------------------
+// One routing block (T <= 32 tokens) and n <= 16 experts: the decode case.  A
+// single workgroup would pull all of x through one compute unit, so the d
+// reduction is split over `nsplit` workgroups first: workgroup b sums its k
+// range (its 4 waves a quarter each, W_g's columns gathered in place) and
+// stores the block's [32][16] partial logits; one workgroup then adds the
+// partials in b order and runs top-K, softmax and the whole dispatch.
+constexpr int kDecodeSplitK = 256;  // k per workgroup of the split
+
+__global__ __launch_bounds__(256) void router_split_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ Wg, int64_t T, int d,
+                                                           int n, float* __restrict__ part,
+                                                           int* __restrict__ zero, int n_zero) {
+  __shared__ float wp_s[4][32 * 16];
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  constexpr int KW = kDecodeSplitK / 4;  // k per wave: 2 MFMA k-steps
+  const int k0 = blockIdx.x * kDecodeSplitK + wave * KW;
+  const bool b_col = r < n;
+  bf16x8_t a[2][KW / 32], b[KW / 32];
+#pragma unroll
+  for (int ks = 0; ks < KW / 32; ++ks) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t tok = min<int64_t>(tt * 16 + r, T - 1);  // rows past T are computed, never used
+      a[tt][ks] = *reinterpret_cast<const bf16x8_t*>(x + tok * d + k0 + ks * 32 + g * 8);
+    }
+    typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+    u16x8_t v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = b_col ? Wg[(int64_t)(k0 + ks * 32 + g * 8 + i) * n + r] : (uint16_t)0;
+    b[ks] = *reinterpret_cast<bf16x8_t*>(&v);
+  }
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < KW / 32; ++ks)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tt][ks], b[ks], acc[tt], 0, 0, 0);
+  // D layout: lane (r, g) holds tokens 16 tt + 4 g + j, expert r
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wp_s[wave][(tt * 16 + 4 * g + j) * 16 + r] = acc[tt][j];
+  __syncthreads();
+  for (int i = tid; i < 32 * 16; i += 256) {
+    float s = wp_s[0][i];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) s += wp_s[w][i];  // fixed wave order
+    part[(int64_t)blockIdx.x * 32 * 16 + i] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_finish_kernel(const float* __restrict__ part, int nsplit, int64_t T,
+                                                            int n, int K, int* __restrict__ topk_idx,
+                                                            float* __restrict__ topk_w, int* __restrict__ counts,
+                                                            int* __restrict__ offsets, int* __restrict__ perm_token,
+                                                            int* __restrict__ slot_pos, int cap) {
+  constexpr int LDL = 17;
+  __shared__ float logits_s[32 * LDL];
+  __shared__ int sel_s[32 * kMaxK];
+  __shared__ uint32_t mask_s[kMaxN];
+  __shared__ int hist_s[kMaxN];
+  for (int i = threadIdx.x; i < 32 * 16; i += 256) {
+    // in split order; each run of 16 partials is loaded at once (a chain of
+    // dependent-looking loads would wait for each in turn)
+    float s = 0.0f;
+    for (int b0 = 0; b0 < nsplit; b0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = b0 + j < nsplit ? part[(int64_t)(b0 + j) * 32 * 16 + i] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (b0 + j < nsplit) s += v[j];
+    }
+    logits_s[(i / 16) * LDL + i % 16] = s;
+  }
+  __syncthreads();
+  route_epilogue(logits_s, LDL, 32, 0, T, n, K, topk_idx, topk_w, nullptr, true, counts, offsets, perm_token,
+                 slot_pos, sel_s, mask_s, hist_s, nullptr, cap, nullptr);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 router: one dot product per (token, expert), sequential in j.
 __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x,
                                                          const float* __restrict__ Wg, int64_t T,
@@ -1052,7 +1141,17 @@ hipError_t launch_route_bf16(const uint16_t* x, const uint16_t* Wg, int64_t T, i
   const int64_t nb = (T + BT - 1) / BT;
   const bool fused = nb == 1;
   hipError_t e;
-  if (n <= 16) {
+  if (n <= 16 && fused && route_block_tokens(n) == 32 && d % kDecodeSplitK == 0 && rb.split != nullptr) {
+    // one routing block: the reduction over d split over workgroups, then one
+    // workgroup for top-K and the dispatch
+    const int nsplit = (int)(d / kDecodeSplitK);
+    hipLaunchKernelGGL(router_split_kernel, dim3((unsigned)nsplit), dim3(256), 0, s, x, Wg, T, (int)d, n, rb.split,
+                       rb.zero, rb.n_zero);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(router_finish_kernel, dim3(1), dim3(256), 0, s, rb.split, nsplit, T, n, K, rb.topk_idx,
+                       rb.topk_w, rb.counts, rb.offsets, rb.perm_token, rb.slot_pos, cap);
+  } else if (n <= 16) {
     // up to 16 experts: gather W_g's columns in place instead of launching a
     // transposed copy first (7 us at the Mixtral shape); the whole dispatch
     // runs in the router when one routing block covers T

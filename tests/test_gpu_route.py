@@ -58,6 +58,10 @@ def test_route_full_configs(name):
     (17, 64, 1, 1, "bf16"),        # one block, one expert
     (32, 2048, 16, 2, "bf16"),     # one block, wide d
     (32, 64, 17, 2, "bf16"),       # one block, n > 16: transposed W_g copy, fused dispatch
+    (32, 256, 8, 2, "bf16"),       # one block, d % 256 == 0: the reduction split over workgroups
+    (7, 512, 5, 3, "bf16"),        # the same, n not a multiple of 8, a partial block
+    (32, 1024, 16, 4, "bf16"),     # the same, 16 experts
+    (1, 256, 1, 1, "bf16"),        # the same, one token, one expert
     (129, 128, 8, 2, "bf16"),      # ragged tail of a 128-token block
     (1000, 192, 8, 2, "bf16"),
     (300, 64, 1, 1, "bf16"),       # one expert
