@@ -60,6 +60,50 @@ def test_forward_graph_replays_match_eager(T, d, f, n, K):
     assert np.isfinite(y_static.cpu().numpy()).all()
 
 
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (32, 256, 384, 8, 2),     # decode form: weight streaming on packed weights
+    (2000, 256, 384, 4, 2),   # prefill form: the work-list GEMMs, whose counters the router clears
+])
+def test_forward_packed_graph_replays_match_eager(T, d, f, n, K):
+    import torch
+    moe = _moe()
+    log(f"graph capture (packed): T={T} d={d} f={f} n={n} K={K}")
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=950 + T)
+    dev = upload(inp)
+    other = upload(make_inputs(T, d, f, n, K, dtype="bf16", seed=951 + T))
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    x_static = dev["x"].clone()
+    y_static = torch.empty((T, d), dtype=torch.float32, device=x_static.device)
+
+    ref_a = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, f, K).clone()
+    ref_b = moe.forward_packed(other["x"], dev["Wg"], p13, p2, f, K).clone()
+    torch.cuda.synchronize()
+    assert not torch.equal(ref_a, ref_b)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward_packed(x_static, dev["Wg"], p13, p2, f, K, y=y_static)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        moe.forward_packed(x_static, dev["Wg"], p13, p2, f, K, y=y_static)
+
+    for rep in range(4):
+        src, ref = (dev["x"], ref_a) if rep % 2 == 0 else (other["x"], ref_b)
+        x_static.copy_(src)
+        y_static.fill_(float("nan"))
+        g.replay()
+        # eager work between replays, including another call that uses (and leaves behind) the work lists
+        scratch = moe.forward_packed(other["x"], dev["Wg"], p13, p2, f, K)
+        _ = (scratch * 2.0).sum()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static, ref), f"replay {rep} differs"
+    assert np.isfinite(y_static.cpu().numpy()).all()
+
+
 def test_graph_replays_after_the_workspace_grows():
     # a graph captured over a small call keeps addressing the workspace it was
     # captured with; a later, larger call grows the workspace, and the outgrown
