@@ -55,20 +55,25 @@ constexpr int PR = 8;                 // register ring of weight k16-steps
 constexpr int PD = 7;                 // weight look-ahead in k16-steps
 static_assert(PD < PR, "a weight load must not target the slot in use");
 constexpr int kDS = 8;                // 1 KiB activation loads per wave per super-stage
+// The barrier that publishes super-stage s + 1 (at step 4 s + 3) releases the slot of
+// super-stage s - 1, whose last fragment reads were consumed by MFMAs several steps
+// earlier, so the barrier need not wait for the wave's LDS reads: loads issued from
+// there on fill super-stage s + PSA - 1 (PSA - LAG super-stages ahead of the one read).
+constexpr int LAG = 2;
 
-// Loads one wave issues, in order: the prologue (super-stages 0 .. PSA-2, kDS
-// loads each; piece 0 of super-stage PSA-1, kDS/4 loads; the weights of steps
+// Loads one wave issues, in order: the prologue (super-stages 0 .. PSA-LAG-1, kDS
+// loads each; piece 0 of super-stage PSA-LAG, kDS/4 loads; the weights of steps
 // 0 .. PD-1, 2 loads each), then per k16 step kk: kDS/4 loads of super-stage
-// (kk+1)/4 + PSA - 1 (piece (kk+1) % 4) followed by the 2 weight loads of step
+// (kk+1)/4 + PSA - LAG (piece (kk+1) % 4) followed by the 2 weight loads of step
 // kk + PD.  packed_after(st, kk) = loads issued after the last load of
 // super-stage `st` when step `kk` begins.
 constexpr int packed_after(int st, int kk) {
-  const int pro = (PSA - 1) * kDS + kDS / 4 + 2 * PD;
+  const int pro = (PSA - LAG) * kDS + kDS / 4 + 2 * PD;
   int last = 0;
-  if (st <= PSA - 2) {
+  if (st <= PSA - LAG - 1) {
     last = (st + 1) * kDS - 1;
   } else {
-    const int kl = 4 * (st - PSA + 1) + 2;  // step that issues the last piece
+    const int kl = 4 * (st - PSA + LAG) + 2;  // step that issues the last piece
     last = pro + kl * (kDS / 4 + 2) + kDS / 4 - 1;
   }
   return pro + kk * (kDS / 4 + 2) - 1 - last;
@@ -239,8 +244,8 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   bf16x8_t br[PR][2];
   auto prologue = [&] {
 #pragma unroll
-    for (int st = 0; st < PSA - 1; ++st) issue_a(st, 0, kDS);
-    issue_a(PSA - 1, 0, kDS / 4);
+    for (int st = 0; st < PSA - LAG; ++st) issue_a(st, 0, kDS);
+    issue_a(PSA - LAG, 0, kDS / 4);
 #pragma unroll
     for (int t = 0; t < PD; ++t) load_b(t, br[t]);
   };
@@ -345,20 +350,23 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     fence();
     bf16x8_t a[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
+    for (int i = 0; i < 8; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
+      fence();  // in block order, as in the loop: the loop's first wait then covers one read, not eight
+    }
 
     // Step kk: 16 MFMAs on the fragments read during step kk-1; after each row
     // block's two MFMAs, that block's fragment of step kk+1 is read.  After the
     // first block come this step's activation loads (a quarter of a super-stage,
-    // into the slot the barrier of step 4s+3 released), after the fourth the
-    // weight loads of step kk + PD.  The last step of each super-stage starts
-    // with the barrier that publishes the next super-stage.
+    // into the slot the last barrier released), after the fourth the weight loads
+    // of step kk + PD.  The last step of each super-stage starts with the barrier
+    // that publishes the next super-stage and releases the slot of the previous one.
     for (int base = 0; base < nk16; base += PR) {
 #pragma unroll
       for (int u = 0; u < PR; ++u) {
         const int kk = base + u;
         if ((u & 3) == 3) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 0));  // own loads landed, own reads done
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 15));  // own loads of super-stage kk/4 + 1 landed
           fence();
           __builtin_amdgcn_s_barrier();
           fence();
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
           a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
           if (i == 0) {
             fence();
-            issue_a(stn + PSA - 1, ((u + 1) & 3) * (kDS / 4), kDS / 4);
+            issue_a(stn + PSA - LAG, ((u + 1) & 3) * (kDS / 4), kDS / 4);
             fence();
           }
           if (i == 3) {
