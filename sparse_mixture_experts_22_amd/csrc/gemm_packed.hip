@@ -31,6 +31,9 @@
 // for itself (s_waitcnt vmcnt, counted by issue order) before a barrier
 // publishes the super-stage; chunk c of row r sits at c ^ ((r >> 1) & 7), so
 // the 16 lanes of a 16-byte fragment read served together hit distinct banks.
+// The last row tile of an expert is usually part padding: when a launch has
+// enough tiles for unequal ones to even out, its padded 32-row blocks are
+// neither multiplied nor stored (a copy of the k-loop per live-block count).
 // MODE 1 takes the weights as the MFMA's row operand (each lane ends with 4
 // consecutive h columns of a row: 8-byte stores, and the SiLU pairs stay in
 // one lane); MODE 2 takes the activations (each store instruction writes whole
@@ -41,6 +44,7 @@
 // written.  Results equal the caller-layout kernels' bit for bit where no tile
 // is split: the same MFMA, the same fragment contents and the same k order.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 #include "tile_sched.h"
@@ -92,6 +96,12 @@ constexpr int packed_wait_stage() {
 constexpr int W_STAGE = packed_wait_stage();
 constexpr int W_FIRST = packed_after(0, 0);
 static_assert(W_STAGE >= 0 && W_STAGE <= 63 && W_FIRST <= 63, "vmcnt is a 6-bit counter");
+// The same bound when the previous tile's epilogue issued the stores of `blocks` row
+// blocks after these loads (4 store instructions per row block in MODE 1, 32 in MODE 2).
+constexpr int packed_w_late(int mode, int blocks) {
+  const int w = W_FIRST + blocks * (mode == 1 ? 4 : 32);
+  return w < 63 ? w : 63;
+}
 
 // Work-list words (int32) of one launch: taken[kXcds] counts the positions
 // handed out beyond the first `cus` of each XCD's share (zero at launch), and
@@ -99,6 +109,9 @@ static_assert(W_STAGE >= 0 && W_STAGE <= 63 && W_FIRST <= 63, "vmcnt is a 6-bit 
 constexpr int kHandoffWords = 2 * kXcds * 64;
 static_assert(kPackedCounterWords == 2 * kXcds && kPackedSchedWords == kPackedCounterWords + 2 * kHandoffWords,
               "work-list words of the two projections");
+
+// 32-row blocks of a tile that hold rows of the expert (the rest are padding)
+__device__ __forceinline__ int live_blocks(const Tile& t) { return (t.rows + 31) >> 5; }
 
 // An accumulator register read where it is used (the compiler would copy all
 // 256 accumulators to VGPRs at once ahead of the SwiGLU epilogue).
@@ -123,6 +136,12 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   const bool may_split = MODE == 2 && tail_ws != nullptr;
   const ExpertTiles et = expert_tiles(offsets, n);
   const int total = et.total * NT;
+  // Padded row blocks are skipped when the launch has at least 8 tiles per compute unit:
+  // tiles of unequal length then even out over the work list.  With only a few long tiles
+  // per unit (the long-reduction down projection) equal tiles keep the per-XCD shares,
+  // which assume equal tiles, finishing together.
+  const bool skip_padding = total >= 8 * kXcds * cus;
+  auto nb_of = [&](const Tile& t) { return skip_padding ? live_blocks(t) : 8; };
   const int x = blockIdx.x % kXcds;
   int* const handoff = handoffs + 2 * blockIdx.x;
 
@@ -271,7 +290,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (i < ib || i >= ie) continue;
+        if (i < ib || i >= ie || i >= nb_of(t)) continue;
         const int row = min(i * 32 + m, t.rows - 1);
         uint16_t* hrow = hout + (int64_t)(t.row0 + row) * N + t.nt * 128 + wave * 32 + 4 * kg;
 #pragma unroll
@@ -300,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       const int last = piece ? BM - 1 : t.rows - 1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if (i < ib || i >= ie) continue;
+        if (i < ib || i >= ie || i >= nb_of(t)) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float* orow = base + (int64_t)min(i * 32 + 8 * (r / 4) + 4 * kg + (r % 4), last) * ld + wave * 64 + m;
@@ -330,10 +349,8 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   // Super-stage 0 of a tile has landed once at most W_FIRST of the loads issued
   // after it are outstanding, plus whatever was issued after those loads (all
   // vector memory operations of a wave complete in issue order): after a
-  // previous tile, the stores of its last four row blocks.
-  constexpr int S_LATE = (MODE == 1) ? 4 * 4 : 4 * 32;
-  constexpr int W_FIRST_LATE = (W_FIRST + S_LATE < 63) ? W_FIRST + S_LATE : 63;
-  bool late_stores = false;
+  // previous tile, the stores of its row blocks 4 .. 7 that hold rows.
+  int late_blocks = 0;
   for (;;) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -341,61 +358,84 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    if (late_stores)
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST_LATE, 15));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_FIRST, 15));
+    switch (late_blocks) {
+      case 0: __builtin_amdgcn_s_waitcnt(waitcnt_imm(packed_w_late(MODE, 0), 15)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(waitcnt_imm(packed_w_late(MODE, 1), 15)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(waitcnt_imm(packed_w_late(MODE, 2), 15)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(waitcnt_imm(packed_w_late(MODE, 3), 15)); break;
+      default: __builtin_amdgcn_s_waitcnt(waitcnt_imm(packed_w_late(MODE, 4), 15)); break;
+    }
     fence();
     __builtin_amdgcn_s_barrier();
     fence();
-    bf16x8_t a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
-      fence();  // in block order, as in the loop: the loop's first wait then covers one read, not eight
-    }
 
-    // Step kk: 16 MFMAs on the fragments read during step kk-1; after each row
-    // block's two MFMAs, that block's fragment of step kk+1 is read.  After the
-    // first block come this step's activation loads (a quarter of a super-stage,
-    // into the slot the last barrier released), after the fourth the weight loads
-    // of step kk + PD.  The last step of each super-stage starts with the barrier
-    // that publishes the next super-stage and releases the slot of the previous one.
-    for (int base = 0; base < nk16; base += PR) {
+    // Step kk: 2 NB MFMAs on the fragments read during step kk-1, NB = the tile's
+    // live 32-row blocks (rows past the tile's end are neither multiplied nor
+    // stored); after each row block's two MFMAs, that block's fragment of step
+    // kk+1 is read.  After the first block's turn come this step's activation
+    // loads (a quarter of a super-stage, into the slot the last barrier released),
+    // after the fourth's the weight loads of step kk + PD: every wave issues the
+    // same loads whatever NB is.  The last step of each super-stage starts with the
+    // barrier that publishes the next super-stage and releases the slot of the
+    // previous one.
+    auto kloop = [&](auto nb_c) {
+      constexpr int NB = decltype(nb_c)::value;
+      bf16x8_t a[8];
 #pragma unroll
-      for (int u = 0; u < PR; ++u) {
-        const int kk = base + u;
-        if ((u & 3) == 3) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 15));  // own loads of super-stage kk/4 + 1 landed
-          fence();
-          __builtin_amdgcn_s_barrier();
-          fence();
-        }
-        const int stn = (kk + 1) >> 2;  // super-stage of step kk+1
-        const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (MODE == 1) {
-            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][0], a[i], acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][1], a[i], acc[i][1], 0, 0, 0);
-          } else {
-            acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][0], acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][1], acc[i][1], 0, 0, 0);
-          }
-          a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
-          if (i == 0) {
-            fence();
-            issue_a(stn + PSA - LAG, ((u + 1) & 3) * (kDS / 4), kDS / 4);
-            fence();
-          }
-          if (i == 3) {
-            fence();
-            load_b(kk + PD, br[(u + PD) % PR]);
-            fence();
-          }
-        }
-        fence();  // the next step's fragment reads stay in this step
+      for (int i = 0; i < NB; ++i) {
+        a[i] = *reinterpret_cast<const bf16x8_t*>(smem + i * 4096 + a_off[0]);
+        fence();  // in block order, as in the loop: the loop's first wait then covers one read
       }
+      for (int base = 0; base < nk16; base += PR) {
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+          const int kk = base + u;
+          if ((u & 3) == 3) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm(W_STAGE, 15));  // own loads of super-stage kk/4 + 1 landed
+            fence();
+            __builtin_amdgcn_s_barrier();
+            fence();
+          }
+          const int stn = (kk + 1) >> 2;  // super-stage of step kk+1
+          const char* an = smem + (stn % PSA) * A_SUPER + a_off[(u + 1) & 3];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (i < NB) {
+              if (MODE == 1) {
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][0], a[i], acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(br[u][1], a[i], acc[i][1], 0, 0, 0);
+              } else {
+                acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][0], acc[i][0], 0, 0, 0);
+                acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], br[u][1], acc[i][1], 0, 0, 0);
+              }
+              a[i] = *reinterpret_cast<const bf16x8_t*>(an + i * 4096);
+            }
+            if (i == 0) {
+              fence();
+              issue_a(stn + PSA - LAG, ((u + 1) & 3) * (kDS / 4), kDS / 4);
+              fence();
+            }
+            if (i == 3) {
+              fence();
+              load_b(kk + PD, br[(u + PD) % PR]);
+              fence();
+            }
+          }
+          fence();  // the next step's fragment reads stay in this step
+        }
+      }
+    };
+    // (a loop of fewer than three blocks got its weight ring in other registers than the
+    // prologue's, and with it a wait for every load at its head: such tiles take three)
+    switch (nb_of(tc)) {
+      case 1:
+      case 2:
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 5: kloop(std::integral_constant<int, 5>{}); break;
+      case 6: kloop(std::integral_constant<int, 6>{}); break;
+      case 7: kloop(std::integral_constant<int, 7>{}); break;
+      default: kloop(std::integral_constant<int, 8>{}); break;
     }
     // Every wave's loads have landed (the last, redundant ones included) and its
     // LDS reads are done: after the barrier the ring may take the next tile.
@@ -431,7 +471,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     }
     fence();
     epilogue(told, 4, 8);
-    late_stores = true;
+    late_blocks = max(0, nb_of(told) - 4);
     if (!more) break;
     fence();
   }
@@ -616,6 +656,7 @@ hipError_t launch_packed_stream_down(const uint16_t* h, const uint16_t* W2p, con
                      W2p, offsets, n, f, d, (int)TK, (int)TK, splits, (uint16_t*)nullptr, o);
   return hipGetLastError();
 }
+
 
 hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, int R, int C, uint16_t* out,
                        hipStream_t s) {

@@ -75,6 +75,7 @@ def _run_both(inp):
     (300, 256, 128, 256, 8),  # weight streaming, maximum n and K
     (1, 256, 128, 8, 2),      # single token
     (300, 256, 256, 4, 4),    # K = n: dense softmax mixture
+    (2400, 256, 14336, 8, 2), # tiled, 8+ up tiles per compute unit: padded row blocks skipped (2-5 live)
 ])
 def test_forward_packed_shapes(T, d, f, n, K):
     log(f"forward_packed: T={T} d={d} f={f} n={n} K={K}")
