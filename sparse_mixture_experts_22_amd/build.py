@@ -49,10 +49,16 @@ SAN_BUILD = os.path.join(BUILD, "sanitized")
 SAN_LIB = os.path.join(SAN_BUILD, "libmoe_sanitized.so")
 
 
-def _compile(src: str, sanitize: bool = False) -> str:
-    out_dir = SAN_BUILD if sanitize else BUILD
+# Tile-trace build: the same library with per-tile timestamps in the packed
+# grouped GEMMs (include/moe_tile_trace.h), read by tile_trace.py.
+TRACE_BUILD = os.path.join(BUILD, "tiletrace")
+TRACE_LIB = os.path.join(PKG, "libmoe_tiletrace.so")
+
+
+def _compile(src: str, sanitize: bool = False, trace: bool = False) -> str:
+    out_dir = SAN_BUILD if sanitize else (TRACE_BUILD if trace else BUILD)
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-    flags = compile_flags() + (SANITIZE_FLAGS if sanitize else [])
+    flags = compile_flags() + (SANITIZE_FLAGS if sanitize else []) + (["-DMOE_TILE_TRACE"] if trace else [])
     cmd = [hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -74,6 +80,24 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_tile_trace(verbose: bool = True) -> str:
+    """libmoe_tiletrace.so next to libmoe.so: every source compiled with
+    MOE_TILE_TRACE (only the packed grouped GEMMs and the C ABI change)."""
+    os.makedirs(TRACE_BUILD, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda src: _compile(src, trace=True), SOURCES))
+    tmp = TRACE_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, TRACE_LIB)
+    if verbose:
+        print(f"built {TRACE_LIB}")
+    return TRACE_LIB
 
 
 def sanitizer_runtime() -> str:

@@ -511,6 +511,21 @@ int64_t capacity_of(int64_t T, int32_t n, int32_t K, double cf) {
 
 }  // namespace
 
+#ifdef MOE_TILE_TRACE
+#include "moe_tile_trace.h"
+namespace moe {
+hipError_t tile_trace_read(long long* host);
+hipError_t tile_trace_clear();
+}
+static_assert(MOE_TILE_TRACE_WGS == moe::kTileTraceWgs && MOE_TILE_TRACE_TILES == moe::kTileTraceTiles &&
+                  MOE_TILE_TRACE_FIELDS == moe::kTileTraceFields,
+              "trace layout");
+extern "C" int moe_tile_trace_read(long long* host) {
+  return host ? (int)moe::tile_trace_read(host) : (int)hipErrorInvalidValue;
+}
+extern "C" int moe_tile_trace_clear(void) { return (int)moe::tile_trace_clear(); }
+#endif
+
 extern "C" {
 
 moe_status_t moe_forward(const void* x, const void* Wg, const void* W1, const void* W3, const void* W2,

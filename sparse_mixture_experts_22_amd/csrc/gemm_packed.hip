@@ -121,6 +121,16 @@ __device__ __forceinline__ float agpr(float v) {
   return r;
 }
 
+#ifdef MOE_TILE_TRACE
+// Per-tile timeline (tile-trace build only): for each projection, workgroup and
+// tile in the order the workgroup ran them, five moments read from the constant
+// 100 MHz counter (s_memrealtime) and from the shader clock counter (s_memtime):
+// k-loop start (after the tile's first barrier), k-loop end, after the closing
+// barrier, after the next tile's loads are issued, after the epilogue; then the
+// tile's live row blocks and k-steps, and the row blocks its k-loop multiplies.
+__device__ long long g_tile_trace[2][kTileTraceWgs][kTileTraceTiles][kTileTraceFields];
+#endif
+
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ perm_token,
@@ -351,6 +361,25 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   // vector memory operations of a wave complete in issue order): after a
   // previous tile, the stores of its row blocks 4 .. 7 that hold rows.
   int late_blocks = 0;
+#ifdef MOE_TILE_TRACE
+  int traced = 0;
+  auto stamp = [&](int k) {
+    const long long rt = __builtin_amdgcn_s_memrealtime();
+    const long long ct = __builtin_amdgcn_s_memtime();
+    if (threadIdx.x == 0 && traced < kTileTraceTiles && blockIdx.x < kTileTraceWgs) {
+      long long* rec = g_tile_trace[MODE - 1][blockIdx.x][traced];
+      rec[k] = rt;
+      rec[5 + k] = ct;
+      if (k == 0) {
+        rec[10] = nb_of(tc) + 16LL * (tc.k1 - tc.k0);
+        rec[11] = max(3, nb_of(tc));  // row blocks the k-loop multiplies (see the switch below)
+      }
+    }
+  };
+#define MOE_STAMP(k) stamp(k)
+#else
+#define MOE_STAMP(k)
+#endif
   for (;;) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -368,6 +397,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     fence();
     __builtin_amdgcn_s_barrier();
     fence();
+    MOE_STAMP(0);
 
     // Step kk: 2 NB MFMAs on the fragments read during step kk-1, NB = the tile's
     // live 32-row blocks (rows past the tile's end are neither multiplied nor
@@ -437,12 +467,14 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       case 7: kloop(std::integral_constant<int, 7>{}); break;
       default: kloop(std::integral_constant<int, 8>{}); break;
     }
+    MOE_STAMP(1);
     // Every wave's loads have landed (the last, redundant ones included) and its
     // LDS reads are done: after the barrier the ring may take the next tile.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     fence();
     __builtin_amdgcn_s_barrier();
     fence();
+    MOE_STAMP(2);
     // The transition to the next tile is interleaved with this tile's epilogue:
     // row blocks 0-1 are written while the hand-over word comes in, 2-3 while
     // the next tile's gathered row indices come in, 4-7 while its first
@@ -470,11 +502,17 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       }
     }
     fence();
+    MOE_STAMP(3);
     epilogue(told, 4, 8);
+    MOE_STAMP(4);
+#ifdef MOE_TILE_TRACE
+    ++traced;
+#endif
     late_blocks = max(0, nb_of(told) - 4);
     if (!more) break;
     fence();
   }
+#undef MOE_STAMP
 }
 
 // Weight streaming on packed weights, for decode-sized batches (a few rows per
@@ -657,6 +695,20 @@ hipError_t launch_packed_stream_down(const uint16_t* h, const uint16_t* W2p, con
   return hipGetLastError();
 }
 
+
+#ifdef MOE_TILE_TRACE
+hipError_t tile_trace_read(long long* host) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tile_trace), sizeof(g_tile_trace), 0, hipMemcpyDeviceToHost);
+}
+hipError_t tile_trace_clear() {
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_tile_trace));
+  if (e != hipSuccess) return e;
+  e = hipMemset(p, 0, sizeof(g_tile_trace));
+  if (e != hipSuccess) return e;
+  return hipDeviceSynchronize();
+}
+#endif
 
 hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, int R, int C, uint16_t* out,
                        hipStream_t s) {

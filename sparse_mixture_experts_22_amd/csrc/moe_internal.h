@@ -111,6 +111,8 @@ hipError_t launch_pack(int mode, const uint16_t* W, const uint16_t* W3, int n, i
 // kPackedSchedWords int32 of device memory whose first kPackedCounterWords
 // words are zero at the up projection's launch (the router clears them).
 constexpr int kPackedCounterWords = 16;
+// Tile-trace build: records per projection, workgroup and tile (see gemm_packed.hip).
+constexpr int kTileTraceWgs = 512, kTileTraceTiles = 64, kTileTraceFields = 12;
 constexpr int kPackedSchedWords = kPackedCounterWords + 2 * 2 * 8 * 64;
 hipError_t launch_packed_up(const uint16_t* x, int64_t T, const int* perm_token, const uint16_t* W13p,
                             const int* offsets, int64_t TK, int n, int d, int f, int cus_per_xcd, int* sched,
