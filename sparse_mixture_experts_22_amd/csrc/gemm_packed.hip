@@ -163,9 +163,12 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
   // none).  Workgroup (x, i) starts at position i of its XCD's share; later
   // positions are handed out in order by an atomic counter per XCD, and a
   // workgroup whose own share is used up takes positions of the other XCDs.
-  // Wave 0 asks for the position after next while a tile runs and hands the
-  // answer to the other waves through a word in global memory (the LDS is all
-  // taken by the activation ring), read after the next end-of-tile barrier.
+  // Wave 0 asks for the next position when a tile starts (the atomic's answer
+  // comes in while the tile runs) and hands it to the other waves through a
+  // word in global memory (the LDS is all taken by the activation ring),
+  // written before the tile's closing barrier and read after it.  Holding one
+  // position ahead, not two, keeps the workgroups' end times within about one
+  // tile of each other.
   const int len_l = lane < kXcds ? queue_len(xcd_plan(total, lane, cus, nk, may_split, PR / 2)) : 0;
   auto share_len = [&](int xq) { return __builtin_amdgcn_readlane(len_l, xq); };
   auto tile_of = [&](int c, Tile& t) -> bool {
@@ -346,15 +349,10 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     setup(tc, src);
   }
   prologue();
-  // wave 0: the position after cur (waited for here, once), handed over now;
-  // the request for the one after that stays in flight during the tile
-  int next = -1, pending = INT32_MAX;
-  int par = 1;
-  if (wave == 0) {
-    next = settle(request());
-    if (lane == 0) __hip_atomic_store(&handoff[par], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (next >= 0) pending = request();
-  }
+  // wave 0: the request for the position after cur stays in flight during the
+  // tile and is settled just before the tile's closing barrier
+  int pending = INT32_MAX;
+  if (wave == 0) pending = request();
 
   // Super-stage 0 of a tile has landed once at most W_FIRST of the loads issued
   // after it are outstanding, plus whatever was issued after those loads (all
@@ -468,8 +466,16 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       default: kloop(std::integral_constant<int, 8>{}); break;
     }
     MOE_STAMP(1);
-    // Every wave's loads have landed (the last, redundant ones included) and its
-    // LDS reads are done: after the barrier the ring may take the next tile.
+    // wave 0: the next position, handed to the other waves through handoff[1]
+    // (read after the barrier; the word is written again only after the next
+    // tile's first barrier, when every wave has read it)
+    if (wave == 0) {
+      const int nx = settle(pending);
+      if (lane == 0) __hip_atomic_store(&handoff[1], nx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Every wave's loads have landed (the last, redundant ones included), its
+    // LDS reads are done and wave 0's hand-over word is written: after the
+    // barrier the ring may take the next tile.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     fence();
     __builtin_amdgcn_s_barrier();
@@ -479,8 +485,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     // row blocks 0-1 are written while the hand-over word comes in, 2-3 while
     // the next tile's gathered row indices come in, 4-7 while its first
     // super-stages and weight steps load.
-    // (wave 0 reads back its own word: its store completed before the barrier)
-    int c = __hip_atomic_load(&handoff[par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int c = __hip_atomic_load(&handoff[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const Tile told = tc;
     epilogue(told, 0, 2);
     fence();
@@ -494,12 +499,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
     if (more) {
       setup(tc, src);
       prologue();
-      par ^= 1;
-      if (wave == 0) {
-        next = settle(pending);
-        if (lane == 0) __hip_atomic_store(&handoff[par], next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pending = next >= 0 ? request() : INT32_MAX;
-      }
+      if (wave == 0) pending = request();
     }
     fence();
     MOE_STAMP(3);
