@@ -160,3 +160,47 @@ def test_forward_packed_full_configs(name):
         lambda e: inp.expert_f64("W2", e), sub)
     rel = assert_rows_close(y, ref, BF16_MAX_REL, BF16_MEAN_REL)
     log(f"  {name}: rows={inp.T} max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
+
+
+@pytest.mark.parametrize("T,d,f,n,K", [
+    (2000, 256, 384, 4, 2),    # tiled, ragged last tiles (all 8 blocks multiplied)
+    (2400, 256, 14336, 8, 2),  # tiled, padded row blocks skipped
+])
+def test_tile_trace_build_matches_and_records(T, d, f, n, K):
+    """The tile-trace build (libmoe_tiletrace.so) gives libmoe.so's output bit for bit,
+    and records one complete timeline entry per tile of each projection."""
+    import ctypes
+    import os
+
+    import torch
+    from sparse_mixture_experts_22_amd import build, tile_trace
+    if not os.path.exists(build.TRACE_LIB):
+        pytest.skip("libmoe_tiletrace.so not built")
+    moe = _moe()
+    log(f"tile trace build: T={T} d={d} f={f} n={n} K={K}")
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=7300 + T + f)
+    dev = upload(inp)
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    ref = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, f, K).clone()
+    L = tile_trace._lib()
+    assert L.moe_tile_trace_clear() == 0
+    y = torch.empty_like(ref)
+    s = torch.cuda.current_stream()
+    assert L.moe_forward_packed(dev["x"].data_ptr(), dev["Wg"].data_ptr(), p13.data_ptr(), p2.data_ptr(),
+                                T, d, f, n, K, y.data_ptr(), s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+    buf = np.zeros(tile_trace.PROJS * tile_trace.WGS * tile_trace.TILES * tile_trace.FIELDS, dtype=np.int64)
+    assert L.moe_tile_trace_read(buf.ctypes.data_as(ctypes.POINTER(ctypes.c_longlong))) == 0
+    tr = buf.reshape(tile_trace.PROJS, tile_trace.WGS, tile_trace.TILES, tile_trace.FIELDS)
+    counts = np.bincount(oracle.route(inp.f64("x"), inp.f64("Wg"), K)["sel"].ravel(), minlength=n)
+    row_tiles = int(sum((c + 255) // 256 for c in counts))
+    for proj, cols in ((0, f // 128), (1, d // 256)):
+        rec = tr[proj][tr[proj][:, :, 4] != 0]
+        assert len(rec) >= row_tiles * cols  # every tile once (split down-projection tiles: once per piece)
+        assert np.all(np.diff(rec[:, 0:5], axis=1) >= 0) and np.all(np.diff(rec[:, 5:10], axis=1) >= 0)
+        live = rec[:, 10] % 16
+        assert np.all((live >= 1) & (live <= 8)) and np.all(rec[:, 11] >= np.maximum(live, 3))
+    if f == 14336:  # 8+ up tiles per compute unit: some tiles multiply fewer than 8 blocks
+        assert (tr[0][tr[0][:, :, 4] != 0][:, 11] < 8).any()
