@@ -204,3 +204,29 @@ def test_tile_trace_build_matches_and_records(T, d, f, n, K):
         assert np.all((live >= 1) & (live <= 8)) and np.all(rec[:, 11] >= np.maximum(live, 3))
     if f == 14336:  # 8+ up tiles per compute unit: some tiles multiply fewer than 8 blocks
         assert (tr[0][tr[0][:, :, 4] != 0][:, 11] < 8).any()
+
+
+def test_forward_packed_interleaved_shapes_match_isolated_calls():
+    """Calls of different shapes in a row on one stream (prefill-size tiled path with
+    skipped padded blocks, decode-size streaming path, many experts, a grown and a
+    shrunk workspace) each give, bit for bit, what the same call gives after a
+    synchronise on its own: the work-list counters, hand-over words and split
+    partial sums of one call leave nothing behind for the next."""
+    import torch
+    moe = _moe()
+    shapes = [(2400, 256, 14336, 8, 2), (32, 256, 384, 8, 2), (4096, 256, 128, 64, 2),
+              (700, 512, 256, 8, 2), (1, 256, 128, 8, 2)]
+    cases = []
+    for i, (T, d, f, n, K) in enumerate(shapes):
+        inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=7500 + i)
+        dev = upload(inp)
+        p13, p2 = moe.pack_up(dev["W1"], dev["W3"]), moe.pack_down(dev["W2"])
+        ref = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, f, K).clone()
+        torch.cuda.synchronize()
+        cases.append((dev["x"], dev["Wg"], p13, p2, f, K, ref))
+    log(f"interleaved packed calls over {len(cases)} shapes")
+    order = [0, 1, 2, 0, 3, 4, 2, 1, 0, 4, 3, 2]
+    outs = [moe.forward_packed(*cases[j][:6]).clone() for j in order]  # no synchronisation in between
+    torch.cuda.synchronize()
+    for j, y in zip(order, outs):
+        assert torch.equal(y, cases[j][6]), f"shape {shapes[j]} differs when interleaved"
