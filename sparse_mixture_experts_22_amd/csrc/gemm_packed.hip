@@ -105,7 +105,9 @@ constexpr int packed_w_late(int mode, int blocks) {
 
 // Work-list words (int32) of one launch: taken[kXcds] counts the positions
 // handed out beyond the first `cus` of each XCD's share (zero at launch), and
-// kHandoffWords hold two words per workgroup (at most 8 x 64 workgroups).
+// kHandoffWords hold two hand-over words per workgroup (at most 8 x 64
+// workgroups): word 0 for a workgroup without a first position of its own,
+// word 1 for the position after each tile.
 constexpr int kHandoffWords = 2 * kXcds * 64;
 static_assert(kPackedCounterWords == 2 * kXcds && kPackedSchedWords == kPackedCounterWords + 2 * kHandoffWords,
               "work-list words of the two projections");
