@@ -230,3 +230,27 @@ def test_forward_packed_interleaved_shapes_match_isolated_calls():
     torch.cuda.synchronize()
     for j, y in zip(order, outs):
         assert torch.equal(y, cases[j][6]), f"shape {shapes[j]} differs when interleaved"
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["mixtral_prefill", "many_experts"])
+def test_packed_equals_caller_layout_bitwise_at_full_size(name):
+    """At full size the packed kernels (padded row blocks skipped, one position ahead on
+    the work list) and the caller-layout kernels (every row block multiplied, one tile
+    per workgroup) multiply the same products in the same k order and split the same
+    leftover down-projection tiles into the same k-pieces, so y is equal bit for bit."""
+    import torch
+    moe = _moe()
+    inp = config_inputs(name)
+    log(f"packed vs caller layout, bitwise: {name}")
+    dev = upload(inp)
+    yc = moe.forward(dev["x"], dev["Wg"], dev["W1"], dev["W3"], dev["W2"], inp.K).clone()
+    p13 = moe.pack_up(dev["W1"], dev["W3"])
+    p2 = moe.pack_down(dev["W2"])
+    del dev["W1"], dev["W3"], dev["W2"]
+    yp = moe.forward_packed(dev["x"], dev["Wg"], p13, p2, inp.f, inp.K)
+    torch.cuda.synchronize()
+    diff = int((yp != yc).sum().item())
+    log(f"  {name}: {diff} of {yp.numel()} elements differ")
+    assert diff == 0
