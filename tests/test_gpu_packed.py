@@ -254,3 +254,37 @@ def test_packed_equals_caller_layout_bitwise_at_full_size(name):
     diff = int((yp != yc).sum().item())
     log(f"  {name}: {diff} of {yp.numel()} elements differ")
     assert diff == 0
+
+
+def test_forward_packed_chosen_expert_sizes_with_skipped_blocks():
+    """Expert row counts chosen to hit every case of the padded-block skipping (8+ up
+    tiles per compute unit, f = 14336): a multiple of 256 (no partial tile), last tiles of
+    1, 2, 32, 33 and 255 rows, and an expert with no rows.  Routing is forced exactly: W_g's
+    first n rows are the identity and token t's x holds 2 at its first expert and 1 at its
+    second, so every logit gap is 1.  Every row against the oracle."""
+    from synth import bf16_bits_from_f32
+    moe = _moe()
+    counts = [1024, 1025, 1056, 1279, 1281, 801, 258, 0]
+    n, d, f, K = len(counts), 256, 14336, 2
+    labels = np.repeat(np.arange(n), counts)
+    half = len(labels) // 2
+    assert len(labels) == 2 * half and max(counts) < half
+    T = half
+    inp = make_inputs(T, d, f, n, K, dtype="bf16", seed=7600)
+    xv = np.zeros((T, d), dtype=np.float32)
+    xv[np.arange(T), labels[:T]] = 2.0      # the first expert of token t
+    xv[np.arange(T), labels[T:]] = 1.0      # and its second (a different one: no expert spans half)
+    inp.x[...] = bf16_bits_from_f32(xv)
+    wg = np.zeros((d, n), dtype=np.float32)
+    wg[np.arange(n), np.arange(n)] = 1.0
+    inp.Wg[...] = bf16_bits_from_f32(wg)
+    log(f"forward_packed, chosen expert sizes {counts}: T={T} d={d} f={f}")
+    yp, y, rt = _run_both(inp)
+    assert np.array_equal(np.bincount(rt["topk_idx"].ravel(), minlength=n), counts)
+    assert_rows_close(yp, y, F32_MAX_REL, F32_MEAN_REL, what="packed vs caller layout")
+    r = oracle.route(inp.f64("x"), inp.f64("Wg"), K)
+    sub = check_routing(r, rt, K)
+    ref = oracle.forward_with_selection(inp.f64("x"), inp.f64("Wg"), inp.f64("W1"), inp.f64("W3"), inp.f64("W2"),
+                                        sub)
+    rel = assert_rows_close(yp, ref, BF16_MAX_REL, BF16_MEAN_REL)
+    log(f"  max_rel={rel.max():.3e} mean_rel={rel.mean():.3e}")
