@@ -54,7 +54,7 @@ namespace moe {
 namespace {
 
 constexpr int A_SUPER = BM * 64 * 2;  // 32 KiB: 256 rows x 64 k
-constexpr int PSA = 5;                // activation super-stages in LDS (160 KiB)
+constexpr int PSA = 4;                // activation super-stages in LDS (128 KiB; a power of two keeps the slot a mask)
 constexpr int PR = 8;                 // register ring of weight k16-steps
 constexpr int PD = 7;                 // weight look-ahead in k16-steps
 static_assert(PD < PR, "a weight load must not target the slot in use");

@@ -10,58 +10,19 @@ gave a loop copy its weight ring in other registers than the prologue's, or when
 the fragment reads ahead of the loop were emitted out of order.  These tests
 fail if any k-loop block of either projection holds such a wait.
 """
-import os
 import re
-import shutil
-import subprocess
 
 import pytest
 
-from sparse_mixture_experts_22_amd import build
+from asm_util import basic_blocks
 
 KERNELS = {1: "packed_gemm_kernelILi1E", 2: "packed_gemm_kernelILi2E"}
 
 
-def _asm(tmp_path) -> str:
-    try:
-        cc = build.hipcc()
-    except RuntimeError:
-        pytest.skip("hipcc not available")
-    out = os.path.join(str(tmp_path), "gemm_packed.s")
-    cmd = [cc, *build.compile_flags(), "--cuda-device-only", "-S",
-           os.path.join(build.CSRC, "gemm_packed.hip"), "-o", out]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-4000:]
-    with open(out) as fh:
-        return fh.read()
-
-
-def _kernel_blocks(asm: str, mangled: str):
-    """Basic blocks (label -> instruction lines) of one kernel's body."""
-    start = re.search(r"^_Z\S*" + mangled + r"\S*:", asm, flags=re.M)
-    assert start, f"kernel {mangled} not found in the assembly"
-    body = asm[start.end():]
-    body = body[:body.index("s_endpgm")]
-    blocks, label, cur = [], "entry", []
-    for line in body.splitlines():
-        if re.match(r"^\.LBB\S*:", line):
-            blocks.append((label, cur))
-            label, cur = line.split(":")[0], []
-        elif line.strip() and not line.lstrip().startswith(";"):
-            cur.append(line.strip())
-    blocks.append((label, cur))
-    return blocks
-
-
-@pytest.fixture(scope="module")
-def packed_asm(tmp_path_factory):
-    return _asm(tmp_path_factory.mktemp("asm"))
-
-
 @pytest.mark.parametrize("mode", [1, 2])
 def test_packed_kloops_wait_only_for_the_oldest_loads(packed_asm, mode):
-    blocks = _kernel_blocks(packed_asm, KERNELS[mode])
-    loops = [(lbl, ins) for lbl, ins in blocks if sum(i.startswith("v_mfma") for i in ins) >= 32]
+    blocks = basic_blocks(packed_asm, KERNELS[mode])
+    loops = [(lbl, ins) for lbl, ins, _ in blocks if sum(i.startswith("v_mfma") for i in ins) >= 32]
     # one k-loop copy per count of live row blocks: 3 (also taking 1 and 2) .. 8
     mfmas = sorted(sum(i.startswith("v_mfma") for i in ins) for _, ins in loops)
     assert mfmas == [48, 64, 80, 96, 112, 128], mfmas

@@ -1,0 +1,246 @@
+"""The packed grouped GEMM's waits for its own direct-to-LDS loads, checked on
+the CPU against a replay of the loads one wave issues.
+
+A wave of packed_gemm_kernel brings its tile's activation rows into an LDS ring
+of PSA super-stages (64 k each) with direct-to-LDS loads, which the compiler
+does not track: the kernel waits for them itself with `s_waitcnt vmcnt(N)`, N
+taken from a closed-form count of the vector memory operations issued after the
+last load it needs (a wave's vector memory operations, stores included, complete
+in issue order).  These tests derive the same bounds another way, by replaying
+the wave's issue sequence one operation at a time, and hold the compiled kernel
+to them:
+
+- the per-step issue order the replay assumes is the one in every compiled
+  k-loop copy: kDS/4 activation loads, then 2 weight loads, per k16-step, with
+  the barriers at the start of steps 3 and 7 of each 8-step iteration;
+- each barrier publishes a super-stage whose kDS loads were all issued before
+  it, and the compiled wait guarantees they have landed;
+- no load refills a ring slot before the barrier after which every wave has
+  consumed the super-stage the slot held (the slot-release lag);
+- the waits ahead of a tile's first barrier, one for each count of the
+  previous tile's row blocks stored after the new tile's loads (0 .. 4), cover
+  super-stage 0 with those stores counted.
+
+Planting a wait one operation too loose in the kernel's count, or a wrong store
+count per row block, fails the last two tests.
+"""
+import os
+import re
+
+import pytest
+
+from asm_util import basic_blocks, vmcnt
+from sparse_mixture_experts_22_amd import build
+
+KERNELS = {1: "packed_gemm_kernelILi1E", 2: "packed_gemm_kernelILi2E"}
+# Stores per 32-row block of a finished tile, from the tile geometry: each wave
+# owns one column pair of 32 rows x (MODE 1) 32 bf16 h columns = 2 KiB, written
+# 8 bytes per lane (512 B per store instruction), or (MODE 2) 64 fp32 output
+# columns = 8 KiB, written 4 bytes per lane (256 B per store instruction).
+STORES_PER_BLOCK = {1: 32 * 32 * 2 // 512, 2: 32 * 64 * 4 // 256}
+LATE_BLOCKS = range(0, 5)  # row blocks 4 .. 7 of the previous tile are stored after the next tile's loads
+
+
+def _constants():
+    with open(os.path.join(build.CSRC, "gemm_packed.hip")) as fh:
+        text = fh.read()
+    out = {}
+    for name in ("PSA", "LAG", "kDS", "PD", "PR"):
+        m = re.search(r"^constexpr int %s = (\d+);" % name, text, flags=re.M)
+        assert m, f"constant {name} not found"
+        out[name] = int(m.group(1))
+    return out
+
+
+C = _constants()
+
+
+def _replay(nss: int):
+    """One wave's vector memory operations for a tile of `nss` super-stages.
+
+    Returns (ops, barriers, fills): ops in issue order, ('A', stage) for a
+    direct-to-LDS activation load and ('B', step) for a weight load; barriers as
+    (super-stage published, operations issued when its wait runs, step it
+    starts; -1 for the tile's first); fills as (super-stage, step issuing it).
+    """
+    psa, lag, kds, pd = C["PSA"], C["LAG"], C["kDS"], C["PD"]
+    ops = []
+    # prologue: super-stages 0 .. PSA-LAG-1 whole, the first quarter of the next,
+    # then the weights of steps 0 .. PD-1
+    for st in range(psa - lag):
+        ops += [("A", st)] * kds
+    ops += [("A", psa - lag)] * (kds // 4)
+    for t in range(pd):
+        ops += [("B", t)] * 2
+    barriers = [(0, len(ops), -1)]
+    fills = []
+    for kk in range(4 * nss):
+        if kk % 4 == 3:
+            # publishes the super-stage whose fragments are read from this step on
+            barriers.append(((kk + 1) // 4, len(ops), kk))
+        st = (kk + 1) // 4 + psa - lag  # the next quarter of the super-stage being filled
+        ops += [("A", st)] * (kds // 4)
+        fills.append((st, kk))
+        ops += [("B", kk + pd)] * 2
+    return ops, barriers, fills
+
+
+def _bounds(nss: int):
+    """(super-stage, largest vmcnt that still guarantees its loads landed) per barrier."""
+    ops, barriers, _ = _replay(nss)
+    out = []
+    for stage, issued, _ in barriers:
+        mine = [i for i in range(issued) if ops[i] == ("A", stage)]
+        assert len(mine) == C["kDS"], f"super-stage {stage} published with {len(mine)} of {C['kDS']} loads issued"
+        out.append((stage, issued - mine[-1] - 1))
+    return out
+
+
+TILE_SIZES = (2, 4, 6, 64, 224)  # super-stages per tile: short k-pieces .. the 14336-long reduction
+
+
+def _loop_bound():
+    return min(b for nss in TILE_SIZES for stage, b in _bounds(nss) if stage >= 1)
+
+
+def _first_bound():
+    return _bounds(2)[0][1]
+
+
+def test_replay_every_super_stage_is_whole_and_in_order():
+    for nss in TILE_SIZES:
+        ops, barriers, _ = _replay(nss)
+        stages = [s for kind, s in ops if kind == "A"]
+        assert stages == sorted(stages), "activation loads fill the super-stages in order"
+        for s in set(stages):
+            assert stages.count(s) == C["kDS"] or s == max(stages), s
+        assert [b[0] for b in barriers] == list(range(nss + 1))
+
+
+def test_replay_slots_are_refilled_only_after_release():
+    """A fill of super-stage st overwrites the slot of st - PSA, whose fragments
+    are read during steps 4(st-PSA)-1 .. 4(st-PSA)+2 and consumed by the MFMAs of
+    steps up to 4(st-PSA)+3; the barrier before the fill (at the start of its
+    step, or the last one before) must come after that step, so that every wave
+    has consumed them (their reads are complete: each MFMA waited for its read)."""
+    for nss in TILE_SIZES:
+        _, _, fills = _replay(nss)
+        for st, kk in fills:
+            prev = st - C["PSA"]
+            if prev < 0:
+                continue  # a slot this tile has not used (the previous tile ended at a full barrier)
+            last_use = 4 * prev + 3
+            barrier = max(4 * s + 3 for s in range(nss) if 4 * s + 3 <= kk)
+            assert last_use < barrier, f"super-stage {st} refills slot {st % C['PSA']} at step {kk}"
+
+
+def test_replay_bounds_by_hand():
+    """The bound by counting, for the ring as built: the prologue issues
+    (PSA-LAG) whole super-stages, a quarter and PD weight steps; a steady-state
+    barrier publishes a super-stage whose last quarter went out
+    4 (PSA-LAG) - 3 steps earlier, 4 operations per step, minus that step's
+    2 activation loads of its own."""
+    psa, lag, kds, pd = C["PSA"], C["LAG"], C["kDS"], C["PD"]
+    per_step = kds // 4 + 2
+    assert _first_bound() == (psa - lag - 1) * kds + kds // 4 + 2 * pd
+    assert _loop_bound() == (4 * (psa - lag) - 3) * per_step - kds // 4
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_compiled_kloops_issue_in_replay_order(packed_asm, mode):
+    expect = "".join(("|" if u % 4 == 3 else "") + "a" * (C["kDS"] // 4) + "bb" for u in range(C["PR"]))
+    loops = 0
+    for name, ins, _ in basic_blocks(packed_asm, KERNELS[mode]):
+        if sum(i.startswith("v_mfma") for i in ins) < 32:
+            continue
+        loops += 1
+        seq = "".join("a" if i.startswith("global_load_lds") else "b" if i.startswith("global_load") else
+                      "|" if i.startswith("s_barrier") else "" for i in ins)
+        assert seq == expect, f"MODE {mode} {name}: {seq}"
+    assert loops == 6
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_compiled_kloop_barriers_wait_for_the_published_super_stage(packed_asm, mode):
+    bound = _loop_bound()
+    for name, ins, _ in basic_blocks(packed_asm, KERNELS[mode]):
+        if sum(i.startswith("v_mfma") for i in ins) < 32:
+            continue
+        for j, i in enumerate(ins):
+            if not i.startswith("s_barrier"):
+                continue
+            waits = [vmcnt(x) for x in ins[:j] if vmcnt(x) is not None]
+            assert waits, f"{name}: barrier without a vmcnt wait before it"
+            # the closed form in the kernel matches the replay exactly: not looser
+            # (a super-stage published before it landed), not tighter (a wait for
+            # loads the barrier does not need)
+            assert waits[-1] == bound, f"MODE {mode} {name}: vmcnt({waits[-1]}), replay bound {bound}"
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_compiled_tile_start_waits_cover_super_stage_zero(packed_asm, mode):
+    blocks = basic_blocks(packed_asm, KERNELS[mode])
+    by_name = {name: (ins, succ) for name, ins, succ in blocks}
+    preds = {name: [] for name, _, _ in blocks}
+    for name, _, succ in blocks:
+        for s in succ:
+            preds[s].append(name)
+
+    # stores per row block as compiled: MODE 1 writes h in 8-byte stores, MODE 2
+    # its accumulators straight from AGPRs
+    if mode == 1:
+        stores = sum(i.startswith("global_store_dwordx2") for _, ins, _ in blocks for i in ins)
+    else:
+        stores = sum(bool(re.match(r"global_store_dword\s+\S+,\s*a\d+", i)) for _, ins, _ in blocks for i in ins)
+    assert stores == 8 * STORES_PER_BLOCK[mode]
+
+    # the tile's first barrier: outside the k-loops, and not a full drain (the
+    # closing barrier and the work list's barrier wait for everything)
+    starts = []
+    for name, ins, _ in blocks:
+        if sum(i.startswith("v_mfma") for i in ins) >= 32:
+            continue
+        for j, i in enumerate(ins):
+            if i.startswith("s_barrier"):
+                before = [vmcnt(x) for x in ins[:j] if vmcnt(x) is not None]
+                if not (before and before[-1] == 0):
+                    starts.append((name, j))
+    assert len(starts) == 1, starts
+    name, j = starts[0]
+
+    # Every wait between the tile's loads (the last direct-to-LDS loads on a path
+    # back from the barrier) and the barrier.  The wait is chosen by a switch on
+    # the previous tile's late row blocks, which the compiler lowers to a chain of
+    # flag tests with one wait per case, so the graph also holds paths that skip
+    # every case, and paths back to the last tile's closing barrier with no loads
+    # (taken only when no tile follows); none of them can run.  So the waits on
+    # the paths that do reach the loads are compared as a set: one per count of
+    # late blocks, and no other.
+    memo = {}
+
+    def waits_back(block, upto):
+        """Waits on the paths from the loads to this point, or None if no path back
+        reaches loads before a barrier."""
+        key = (block, upto)
+        if key in memo:
+            return memo[key]
+        memo[key] = None  # a cycle back to here adds nothing
+        ins = by_name[block][0][:upto]
+        loads = [k for k, x in enumerate(ins) if x.startswith("global_load_lds")]
+        bars = [k for k, x in enumerate(ins) if x.startswith("s_barrier")]
+        if loads and (not bars or loads[-1] > bars[-1]):
+            out = {vmcnt(x) for x in ins[loads[-1] + 1:] if vmcnt(x) is not None}
+        elif bars:
+            out = None
+        else:
+            here = {vmcnt(x) for x in ins if vmcnt(x) is not None}
+            back = [waits_back(p, None) for p in preds[block]]
+            back = [b for b in back if b is not None]
+            out = set().union(here, *back) if back else None
+        memo[key] = out
+        return out
+
+    found = waits_back(name, j)
+    assert found is not None, f"no path from the loads to {name}"
+    expect = {min(63, _first_bound() + b * STORES_PER_BLOCK[mode]) for b in LATE_BLOCKS}
+    assert found == expect, f"MODE {mode}: waits {sorted(found)}, replay {sorted(expect)}"
