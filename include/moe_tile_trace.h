@@ -20,7 +20,7 @@
  *   10     live 32-row blocks (8 where padded blocks are not skipped)
  *          + 16 * k-steps (of 32) of the tile;
  *   11     32-row blocks the tile's k-loop multiplies (the live ones, at least
- *          3; 8 where padded blocks are not skipped).
+ *          2; 8 where padded blocks are not skipped).
  * A record whose field 4 is 0 was not written.
  */
 #ifndef MOE_TILE_TRACE_H

@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
       rec[5 + k] = ct;
       if (k == 0) {
         rec[10] = nb_of(tc) + 16LL * (tc.k1 - tc.k0);
-        rec[11] = max(3, nb_of(tc));  // row blocks the k-loop multiplies (see the switch below)
+        rec[11] = max(2, nb_of(tc));  // row blocks the k-loop multiplies (see the switch below)
       }
     }
   };
@@ -455,11 +455,11 @@ __global__ __launch_bounds__(256, 1) void packed_gemm_kernel(
         }
       }
     };
-    // (a loop of fewer than three blocks got its weight ring in other registers than the
-    // prologue's, and with it a wait for every load at its head: such tiles take three)
+    // (a one-block loop would wait for its single fragment read at the head of every
+    // step, a wait for every LDS read: such tiles take the two-block loop)
     switch (nb_of(tc)) {
       case 1:
-      case 2:
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
       case 3: kloop(std::integral_constant<int, 3>{}); break;
       case 4: kloop(std::integral_constant<int, 4>{}); break;
       case 5: kloop(std::integral_constant<int, 5>{}); break;

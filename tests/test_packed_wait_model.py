@@ -151,20 +151,20 @@ def test_compiled_kloops_issue_in_replay_order(packed_asm, mode):
     expect = "".join(("|" if u % 4 == 3 else "") + "a" * (C["kDS"] // 4) + "bb" for u in range(C["PR"]))
     loops = 0
     for name, ins, _ in basic_blocks(packed_asm, KERNELS[mode]):
-        if sum(i.startswith("v_mfma") for i in ins) < 32:
+        if sum(i.startswith("v_mfma") for i in ins) < 32 or not any(i.startswith("s_barrier") for i in ins):
             continue
         loops += 1
         seq = "".join("a" if i.startswith("global_load_lds") else "b" if i.startswith("global_load") else
                       "|" if i.startswith("s_barrier") else "" for i in ins)
         assert seq == expect, f"MODE {mode} {name}: {seq}"
-    assert loops == 6
+    assert loops == 7
 
 
 @pytest.mark.parametrize("mode", [1, 2])
 def test_compiled_kloop_barriers_wait_for_the_published_super_stage(packed_asm, mode):
     bound = _loop_bound()
     for name, ins, _ in basic_blocks(packed_asm, KERNELS[mode]):
-        if sum(i.startswith("v_mfma") for i in ins) < 32:
+        if sum(i.startswith("v_mfma") for i in ins) < 32 or not any(i.startswith("s_barrier") for i in ins):
             continue
         for j, i in enumerate(ins):
             if not i.startswith("s_barrier"):
@@ -198,7 +198,7 @@ def test_compiled_tile_start_waits_cover_super_stage_zero(packed_asm, mode):
     # closing barrier and the work list's barrier wait for everything)
     starts = []
     for name, ins, _ in blocks:
-        if sum(i.startswith("v_mfma") for i in ins) >= 32:
+        if sum(i.startswith("v_mfma") for i in ins) >= 32 and any(i.startswith("s_barrier") for i in ins):
             continue
         for j, i in enumerate(ins):
             if i.startswith("s_barrier"):
