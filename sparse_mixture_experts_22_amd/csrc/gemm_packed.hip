@@ -581,8 +581,8 @@ __global__ __launch_bounds__(64) void packed_stream_kernel(
       const bf16x8_t* src = reinterpret_cast<const bf16x8_t*>(bptr + (int64_t)k * 4096);
 #pragma unroll
       for (int q = 0; q < SQ; ++q) {
-        rb[slot][q][0] = src[q * 128];
-        rb[slot][q][1] = src[q * 128 + 64];
+        rb[slot][q][0] = ld_stream(src + q * 128);
+        rb[slot][q][1] = ld_stream(src + q * 128 + 64);
       }
     };
 #pragma unroll

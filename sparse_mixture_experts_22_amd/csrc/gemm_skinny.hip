@@ -54,7 +54,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4_t (&in)[8], bf16x8_t (&
 __device__ __forceinline__ void load_block(u32x4_t (&q)[8], const uint16_t* src, int64_t row_stride) {
 #pragma unroll
   for (int r = 0; r < 8; ++r)
-    q[r] = *reinterpret_cast<const u32x4_t*>(src + (int64_t)r * row_stride);
+    q[r] = ld_stream(reinterpret_cast<const u32x4_t*>(src + (int64_t)r * row_stride));
 }
 
 __device__ __forceinline__ void mma_block(const u32x4_t (&q)[8], const bf16x8_t& a, f32x4_t (&acc)[8]) {

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void skinny_q4_kernel(
     auto load = [&](int blk, u32x4_t (&w)[TPW], bf16x8_t (&a)[4], float (&s)[TPW]) {
 #pragma unroll
       for (int ct = 0; ct < TPW; ++ct) {
-        w[ct] = *reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * N * 64);
+        w[ct] = ld_stream(reinterpret_cast<const u32x4_t*>(qsrc + ct * qtile + (int64_t)blk * N * 64));
         s[ct] = __uint_as_float((uint32_t)ssrc[(int64_t)blk * N + ct * 16] << 16);
       }
 #pragma unroll
