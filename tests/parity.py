@@ -84,7 +84,9 @@ def assert_rows_close(got, ref, max_rel, mean_rel, what="y", elem_rel=None):
         assert e.max() <= elem_rel, (
             f"{what}: element {tuple(int(i) for i in worst)} off by {e.max():.3e} x rms(row) "
             f"(<= {elem_rel}); {int((e > elem_rel).sum())} elements over")
-        print(f"  {what}: elementwise max {e.max():.3e} x rms(row)", flush=True)
+        print(f"  {what}: rows {r.size}, normwise max {r.max():.3e} mean {r.mean():.3e} "
+              f"(bounds {max_rel:g}, {mean_rel:g}); elementwise max {e.max():.3e} x rms(row) "
+              f"(bound {elem_rel:g})", flush=True)
     return r
 
 
